@@ -1,0 +1,316 @@
+"""CPU oracle of the SageAttention-style quantized attention forward pass.
+
+TEST INFRASTRUCTURE ONLY: this is the checker the HIP path is compared with.
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import it; the product never calls it and it shares no code with the
+HIP path.  Plain NumPy in float64 (float32 only where the method's own
+arithmetic is float32: the K mean cast, the smoothing subtraction, the scales
+and the x/scale divisions that decide integer codes).
+
+Two results are computed:
+
+(i)  ``attn_exact`` -- the plain definition O = softmax(sm_scale Q K^T + mask) V
+     in float64 on the unquantized fp16/bf16 inputs.
+(ii) ``quantize_qk`` / ``quantize_v`` / ``attn_quant`` -- the quantized
+     method step by step, in the order of Algorithm 1 on the SageAttention2
+     detail page (with INT8 codes for Q and K, and without smoothing Q).
+
+Where the pages leave a step open the reading taken is stated at the step.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import fp8_e4m3
+
+BLKQ = 128        # Q tokens per INT8 scale (Algorithm 1's b_q, detail page sec. 3)
+BLKK = 64         # K tokens per INT8 scale (Algorithm 1's b_kv)
+INT8_MAX = 127.0
+P_SCALE = 448.0   # static scale of P before the FP8 cast (Algorithm 1)
+KV_TILE = 128     # keys per online-softmax step of the GPU kernel
+
+
+# ---------------------------------------------------------------------------
+# Step 1: Smooth K  (SageAttention synthesis page, the Smooth K paragraph;
+# SageAttention2 detail page, Algorithm 1 "Preprocessing": K = K - mean(K)).
+
+def k_sum_exact(k: np.ndarray) -> np.ndarray:
+    """Per-channel sum of K over tokens, float64, [..., N, d] -> [..., d].
+
+    Reading: the mean is the exact sum over all N tokens, divided by N and
+    rounded to float32.  ``np.sum`` in float64 is exact -- hence equal to the
+    correctly rounded sum ``math.fsum`` -- whenever every partial sum is a
+    multiple of the smallest quantum present with fewer than 2^53 quanta;
+    ``exactness_margin_bits`` checks that condition.
+    """
+    return np.sum(np.asarray(k, dtype=np.float64), axis=-2)
+
+
+def exactness_margin_bits(k: np.ndarray) -> float:
+    """53 - log2(sum|x| / min quantum) over all columns; > 0 means exact."""
+    x = np.abs(np.asarray(k, dtype=np.float64))
+    nz = x[x > 0]
+    if nz.size == 0:
+        return 53.0
+    # quantum of a value with 8 (bf16) or 11 (fp16) significant bits is at most
+    # 2^(e-10); use the fp16 bound, which is the finer of the two for equal e.
+    _, e = np.frexp(nz.min())
+    q = 2.0 ** (e - 1 - 10)
+    tot = np.sum(x, axis=-2).max()
+    return 53.0 - math.log2(max(tot / q, 1.0))
+
+
+def k_mean(k: np.ndarray) -> np.ndarray:
+    """mean32 = float32(sum64 / N), [B, H_kv, N, d] -> [B, H_kv, d]."""
+    n = k.shape[-2]
+    return (k_sum_exact(k) / n).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Steps 2-3: per-block INT8 quantization of Q and K (deployment-guide page,
+# quantization formula: code = round(x / S); source-analysis page, the
+# quantization module: Q/K enter the kernel as INT8 with FP32 scales).
+# Reading: scale = float32(amax / 127) by IEEE division, code =
+# RNE(float32(x / scale)) clamped to [-127, 127]; an all-zero block has
+# scale 0 and codes 0; tail blocks take amax over their valid tokens only.
+
+def quantize_int8_blocks(x32: np.ndarray, block: int):
+    """x32: float32 [..., N, d] -> (int8 codes [..., N, d], float32 scales [..., nblk])."""
+    assert x32.dtype == np.float32
+    *lead, n, d = x32.shape
+    nblk = -(-n // block)
+    codes = np.zeros(x32.shape, dtype=np.int8)
+    scales = np.zeros((*lead, nblk), dtype=np.float32)
+    for i in range(nblk):
+        xb = x32[..., i * block:(i + 1) * block, :]
+        amax = np.max(np.abs(xb), axis=(-2, -1))
+        s = (amax / np.float32(INT8_MAX)).astype(np.float32)
+        scales[..., i] = s
+        safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+        y = (xb / safe[..., None, None]).astype(np.float32)       # float32 IEEE division
+        c = np.clip(np.rint(y), -INT8_MAX, INT8_MAX)
+        c = np.where((s > 0)[..., None, None], c, 0.0)
+        codes[..., i * block:(i + 1) * block, :] = c.astype(np.int8)
+    return codes, scales
+
+
+def quantize_qk(q, k, smooth_k: bool = True):
+    """Quantize Q per 128 tokens and smoothed K per 64 tokens.
+
+    q: [B, H, N, d], k: [B, H_kv, N, d] (fp16/bf16 values as torch or numpy).
+    Returns dict(q_i8, q_scale, k_i8, k_scale, k_mean).
+    """
+    q32 = _f32(q)
+    k32 = _f32(k)
+    if smooth_k:
+        mean = k_mean(k32)
+        ks = (k32 - mean[..., None, :]).astype(np.float32)         # float32 RN subtraction
+    else:
+        mean = np.zeros(k32.shape[:-2] + k32.shape[-1:], dtype=np.float32)
+        ks = k32
+    qc, qs = quantize_int8_blocks(q32, BLKQ)
+    kc, ksc = quantize_int8_blocks(ks, BLKK)
+    return dict(q_i8=qc, q_scale=qs, k_i8=kc, k_scale=ksc, k_mean=mean)
+
+
+# ---------------------------------------------------------------------------
+# Step 4: per-channel FP8 E4M3 quantization of V (SageAttention2 detail page,
+# Algorithm 1 "(delta_V, V^) = psi_V(V)"; source-analysis page, "V 的 FP16/FP8
+# 准备": per-channel scale).  Reading: the channel's scale covers all N
+# tokens of a (b, kv-head); scale = float32(amax / 448), code =
+# E4M3(clamp(float32(v / scale), +-448)) with RNE.
+
+def quantize_v(v):
+    """v: [B, H_kv, N, d] -> dict(v_f8 uint8 [B,H_kv,N,d] natural layout, v_scale f32 [B,H_kv,d])."""
+    v32 = _f32(v)
+    amax = np.max(np.abs(v32), axis=-2)                              # [B, H_kv, d]
+    s = (amax / np.float32(fp8_e4m3.E4M3_MAX)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    y = (v32 / safe[..., None, :]).astype(np.float32)
+    y = np.clip(y, -fp8_e4m3.E4M3_MAX, fp8_e4m3.E4M3_MAX)
+    codes = fp8_e4m3.encode(y.astype(np.float64))
+    codes = np.where((s > 0)[..., None, :], codes, np.uint8(0)).astype(np.uint8)
+    return dict(v_f8=codes, v_scale=s)
+
+
+# ---------------------------------------------------------------------------
+# (i) Exact attention: the plain definition, float64.
+
+def attn_exact(q, k, v, *, causal: bool, sm_scale: float, rows=None, heads=None):
+    """O = softmax(sm_scale Q K^T + mask) V in float64.
+
+    q [B,H,N,d]; k, v [B,H_kv,N,d]; query head h reads kv head h // (H/H_kv)
+    (source-analysis page: num_qo_heads divisible by num_kv_heads).  Causal:
+    key j is visible to query i iff j <= i.  ``rows``: optional index array
+    of query rows to compute; ``heads``: optional list of (b, h).
+    Returns float64 [B,H,len(rows),d] (unselected heads are zero).
+    """
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q64.shape
+    grp = H // k64.shape[1]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    out = np.zeros((B, H, len(rows), d))
+    for b, h in (heads or [(b, h) for b in range(B) for h in range(H)]):
+        hk = h // grp
+        s = (q64[b, h, rows] @ k64[b, hk].T) * sm_scale
+        if causal:
+            s = np.where(np.arange(N)[None, :] > rows[:, None], -np.inf, s)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        out[b, h] = p @ v64[b, hk]
+    return out
+
+
+def softmax_rows(q, k, *, causal: bool, sm_scale: float, b=0, h=0, hk=None):
+    """Full probability matrix P of one head (float64), for the row-sum check."""
+    q64, k64 = _f64(q), _f64(k)
+    hk = h if hk is None else hk
+    s = (q64[b, h] @ k64[b, hk].T) * sm_scale
+    n = s.shape[0]
+    if causal:
+        s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# (ii) The quantized attention of Algorithm 1 (SageAttention2 detail page),
+# INT8 QK^T and FP8 PV, written as the sums the online recursion produces.
+#
+# Per query row i and key tile t (tiles of ``kv_tile`` keys, ascending):
+#   S_ij   = (sum_c qcode_ic kcode_jc) * dQ(i) * dK(j) * sm_scale, masked to -inf
+#   m_t    = max(m_{t-1}, rowmax_t S)                      (running max)
+#   Pt_ij  = exp(S_ij - m_t)                               (P tilde)
+#   Pq_ij  = E4M3(448 * Pt_ij)                             (static P scale)
+#   l      = sum_t exp(m_t - m_T) rowsum(Pt_t)             (unquantized P tilde)
+#   O_i    = [sum_t exp(m_t - m_T) sum_{j in t} Pq_ij Vdq_j] / (448 l)
+# which is what "l = exp(m_old - m_new) l + rowsum(Pt)" and
+# "O = diag(exp(m_old - m_new)) O + Pq V" (Algorithm 1 and the online-softmax
+# update of the source-analysis page) accumulate to, followed by the final
+# rescale O = diag(l)^-1 O / 448 * delta_V.
+
+def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
+               kv_tile: int = KV_TILE, rows=None, heads=None,
+               quantize_p: bool = True, blkq: int = BLKQ, blkk: int = BLKK):
+    """Quantized attention, float64 result [B,H,len(rows),d].
+
+    qc int8 [B,H,N,d], qs f32 [B,H,nq]; kc int8 [B,H_kv,N,d], ks f32
+    [B,H_kv,nk]; vc uint8 E4M3 codes [B,H_kv,N,d] (natural layout), vs f32
+    [B,H_kv,d].  ``quantize_p=False`` skips the FP8 rounding of 448*Pt (the
+    result is then exact attention on the dequantized inputs).
+    """
+    B, H, N, d = qc.shape
+    grp = H // kc.shape[1]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    nt = -(-N // kv_tile)
+    npad = nt * kv_tile
+    key_blk = np.arange(N) // blkk
+    out = np.zeros((B, H, len(rows), d))
+    chunk = max(1, (1 << 24) // npad)               # bound the [rows, keys] temporaries
+    for b, h in (heads or [(b, h) for b in range(B) for h in range(H)]):
+        hk = h // grp
+        vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
+        kf = kc[b, hk].astype(np.float64).T
+        ksc = ks[b, hk, key_blk].astype(np.float64)[None, :]
+        for r0 in range(0, len(rows), chunk):
+            rr = rows[r0:r0 + chunk]
+            # exact integer dot products (|partial sums| <= 127^2 d < 2^53)
+            s = qc[b, h, rr].astype(np.float64) @ kf
+            s = s * qs[b, h, rr // blkq].astype(np.float64)[:, None]
+            s = s * ksc * sm_scale
+            if causal:
+                s = np.where(np.arange(N)[None, :] > rr[:, None], -np.inf, s)
+            sp = np.full((len(rr), npad), -np.inf)
+            sp[:, :N] = s
+            st = sp.reshape(len(rr), nt, kv_tile)
+            m_run = np.maximum.accumulate(st.max(axis=2), axis=1)        # [R, nt]
+            m_fin = m_run[:, -1:]
+            pt = np.exp(st - m_run[:, :, None])                          # P tilde in [0, 1]
+            pq = fp8_e4m3.round_to_e4m3(P_SCALE * pt) if quantize_p else P_SCALE * pt
+            carry = np.exp(m_run - m_fin)                                # exp(m_t - m_T)
+            l = np.sum(pt.sum(axis=2) * carry, axis=1)
+            w = (pq * carry[:, :, None]).reshape(len(rr), npad)[:, :N]
+            out[b, h, r0:r0 + chunk] = (w @ vdq) / (P_SCALE * l)[:, None]
+    return out
+
+
+def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
+                         b=0, h=0, hk=None, blkq=BLKQ, blkk=BLKK):
+    """Literal online recursion of Algorithm 1 in pure Python loops (tiny sizes).
+
+    Used to pin ``attn_quant``'s closed form: the same steps, one key tile at
+    a time, with m, l and O updated in place.
+    """
+    n, d = qc.shape[2], qc.shape[3]
+    hk = h if hk is None else hk
+    vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
+    out = np.zeros((n, d))
+    for i in range(n):
+        m, l = -math.inf, 0.0
+        o = [0.0] * d
+        for t0 in range(0, n, kv_tile):
+            keys = range(t0, min(t0 + kv_tile, n))
+            srow = {}
+            for j in keys:
+                if causal and j > i:
+                    continue
+                acc = sum(int(qc[b, h, i, c]) * int(kc[b, hk, j, c]) for c in range(d))
+                srow[j] = acc * float(qs[b, h, i // blkq]) * float(ks[b, hk, j // blkk]) * sm_scale
+            if not srow:
+                continue
+            m_new = max(m, max(srow.values()))
+            alpha = math.exp(m - m_new) if m != -math.inf else 0.0
+            l = alpha * l
+            o = [alpha * x for x in o]
+            for j, sv in srow.items():
+                pt = math.exp(sv - m_new)
+                l += pt
+                pq = float(fp8_e4m3.round_to_e4m3(P_SCALE * pt))
+                for c in range(d):
+                    o[c] += pq * vdq[j, c]
+            m = m_new
+        out[i] = [x / (P_SCALE * l) for x in o]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Metrics (SageAttention2 detail page, Tables 4 and 6 name CosSim, Relative L1
+# and RMSE; the definitions are the usual ones, on flattened tensors).
+
+def metrics(a, ref) -> dict:
+    a = np.asarray(a, dtype=np.float64).ravel()
+    r = np.asarray(ref, dtype=np.float64).ravel()
+    return dict(
+        cos=float(np.dot(a, r) / math.sqrt(np.dot(a, a) * np.dot(r, r))),
+        rel_l1=float(np.abs(a - r).sum() / np.abs(r).sum()),
+        rmse=float(math.sqrt(np.mean((a - r) ** 2))),
+        max_abs=float(np.abs(a - r).max()),
+    )
+
+
+def round_output(o64, dtype: str):
+    """Round the float64 result to the output dtype (RNE), returned as float64.
+
+    torch's CPU cast goes float64 -> float32 -> bf16, so a bf16 tie can be
+    double-rounded (one bf16 ulp, rare); the output comparison is toleranced.
+    """
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(o64, dtype=np.float64))
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    return t.to(tdt).to(torch.float64).numpy()
+
+
+def _f32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        return x.detach().cpu().float().numpy()
+    return np.asarray(x, dtype=np.float32)
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        return x.detach().cpu().double().numpy()
+    return np.asarray(x, dtype=np.float64)

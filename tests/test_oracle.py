@@ -1,0 +1,368 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's formula: each checks a worked value, a
+closed form, an invariant, a library routine or a brute-force loop.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import fp8_e4m3 as F8
+from oracle import sage_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------- FP8 codec
+
+def test_fp8_golden_points():
+    for line in open(os.path.join(GOLD, "fp8_e4m3_points.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        val, code = line.split()
+        assert int(F8.encode(float(val))) == int(code, 16), line
+        if abs(float(val)) <= 448 and "e" not in val:
+            # points that are grid values decode back exactly
+            r = F8.decode(np.uint8(int(code, 16)))
+            assert r == F8.round_to_e4m3(float(val))
+
+
+def test_fp8_exhaustive_roundtrip():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = F8.decode(codes)
+    ok = ~np.isnan(vals)
+    assert ok.sum() == 254                       # only S.1111.111 is NaN
+    assert np.nanmax(vals) == 448.0 and np.nanmin(vals) == -448.0
+    assert (F8.encode(vals[ok]) == codes[ok]).all()
+
+
+def test_fp8_midpoints_round_to_even():
+    vals = np.unique(F8.decode(np.arange(0, 0x7F, dtype=np.uint8)))   # 0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2
+    got = F8.encode(mids)
+    lo = F8.encode(vals[:-1])
+    hi = F8.encode(vals[1:])
+    even = np.where(lo % 2 == 0, lo, hi)
+    assert (got == even).all()
+    # just off the midpoint goes to the nearer neighbour
+    assert (F8.encode(mids * (1 - 1e-9)) == lo).all()
+    assert (F8.encode(mids * (1 + 1e-9)) == hi).all()
+
+
+def test_fp8_matches_torch_in_range():
+    g = np.random.default_rng(0)
+    x = np.concatenate([g.standard_normal(20000) * 10 ** g.uniform(-4, 2.6, 20000),
+                        g.uniform(-448, 448, 20000)]).astype(np.float32)
+    x = x[np.abs(x) <= 448]            # torch's cast does not saturate; compare in range
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = F8.encode(x.astype(np.float64))
+    same = (F8.decode(got) == F8.decode(ref))
+    assert same.all(), x[~same][:10]
+
+
+def test_fp8_saturates():
+    assert (F8.encode([449.0, 464.0, 479.0, 1e30]) == 0x7E).all()
+    assert (F8.encode([-449.0, -1e30]) == 0xFE).all()
+
+
+# --------------------------------------------------------------------- INT8 quant
+
+def _read_sections(path):
+    sec, out = None, {}
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("# section:"):
+            sec = line.split(":", 1)[1].strip()
+            out[sec] = []
+        elif line and not line.startswith("#"):
+            out[sec].append([float(t) for t in line.split()])
+    return out
+
+
+def test_int8_worked_example():
+    s = _read_sections(os.path.join(GOLD, "int8_block_example.txt"))
+    x = np.array(s["input"], dtype=np.float32)[None]
+    codes, scales = O.quantize_int8_blocks(x, 128)
+    assert scales[0, 0] == np.float32(s["scale"][0][0])
+    assert (codes[0] == np.array(s["codes"])).all()
+
+
+def test_int8_invariants_random_blocks():
+    g = np.random.default_rng(1)
+    x = (g.standard_normal((3, 300, 64)) * np.exp(g.uniform(-20, 20, (3, 1, 1)))).astype(np.float32)
+    codes, scales = O.quantize_int8_blocks(x, 64)
+    assert codes.dtype == np.int8 and np.abs(codes.astype(int)).max() <= 127
+    for h in range(3):
+        for i in range(scales.shape[1]):
+            xb = x[h, i * 64:(i + 1) * 64].astype(np.float64)
+            cb = codes[h, i * 64:(i + 1) * 64].astype(np.float64)
+            s = float(scales[h, i])
+            assert np.abs(cb).max() == 127                     # the block's amax hits 127
+            assert abs(np.abs(xb).max() / s - 127) < 127 * 2 ** -22
+            err = np.abs(xb - cb * s)
+            assert (err <= s / 2 * (1 + 2 ** -20)).all()      # nearest code
+
+
+def test_int8_zero_block_and_tail():
+    x = np.zeros((1, 150, 8), dtype=np.float32)
+    x[0, 130:] = 3.0
+    codes, scales = O.quantize_int8_blocks(x, 128)
+    assert scales[0, 0] == 0 and (codes[0, :128] == 0).all()
+    assert scales.shape == (1, 2)
+    assert (codes[0, 130:] == 127).all() and (codes[0, 128:130] == 0).all()
+
+
+def test_int8_ties_go_to_even():
+    # amax 127 -> scale exactly 1.0; x = k + 0.5 hits ties
+    x = np.array([[127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5]], dtype=np.float32)[None]
+    codes, scales = O.quantize_int8_blocks(x, 128)
+    assert scales[0, 0] == 1.0
+    assert codes[0, 0].tolist() == [127, 0, 2, 2, 0, -2, -2, 4]
+
+
+# --------------------------------------------------------------------- Smooth K
+
+def test_k_mean_equals_fsum():
+    t = W.generate(W.get("tiny"))
+    k = t["k"].float().numpy()
+    assert O.exactness_margin_bits(k) > 0
+    got = O.k_sum_exact(k)
+    for h in range(k.shape[1]):
+        for c in range(k.shape[3]):
+            assert got[0, h, c] == math.fsum(k[0, h, :, c].astype(np.float64).tolist())
+    mean = O.k_mean(k)
+    assert mean.dtype == np.float32
+
+
+def test_smoothing_invariance_exact_attention():
+    """Softmax is shift invariant along a row: K and K - mean give the same O."""
+    w = W.get("tiny")
+    t = W.generate(w)
+    k64 = t["k"].double()
+    ks = k64 - k64.mean(dim=2, keepdim=True)
+    for causal in (False, True):
+        a = O.attn_exact(t["q"], k64, t["v"], causal=causal, sm_scale=w.sm_scale)
+        b = O.attn_exact(t["q"], ks, t["v"], causal=causal, sm_scale=w.sm_scale)
+        assert np.abs(a - b).max() <= 1e-6
+
+
+def test_smoothing_removes_a_shared_bias_exactly():
+    """K + c (c exact per channel) smooths to the same K - mean, so same codes."""
+    g = np.random.default_rng(2)
+    # k on a 1/16 grid, c on an 8 grid, N a power of two: k + c is exact in
+    # fp16, and the sums, the mean and k - mean are all exact in float32/64
+    k = (g.integers(-64, 64, (1, 2, 256, 16)) / 16.0).astype(np.float32)
+    c = (g.integers(-4, 5, (1, 2, 1, 16)) * 8.0).astype(np.float32)
+    q = g.standard_normal((1, 2, 256, 16)).astype(np.float32)
+    a = O.quantize_qk(q, torch.from_numpy(k).half())
+    b = O.quantize_qk(q, torch.from_numpy(k + c).half())
+    assert (a["k_i8"] == b["k_i8"]).all() and (a["k_scale"] == b["k_scale"]).all()
+    assert np.allclose(b["k_mean"] - a["k_mean"], c[:, :, 0], atol=0)
+    # without smoothing the bias leaks into the codes
+    n = O.quantize_qk(q, torch.from_numpy(k + c).half(), smooth_k=False)
+    assert not (n["k_i8"] == a["k_i8"]).all()
+
+
+# --------------------------------------------------------------------- exact attention
+
+def _brute_attention(q, k, v, causal, sm_scale, grp):
+    B, H, N, d = q.shape
+    out = np.zeros(q.shape)
+    for b in range(B):
+        for h in range(H):
+            hk = h // grp
+            for i in range(N):
+                sc = []
+                for j in range(N):
+                    if causal and j > i:
+                        continue
+                    sc.append((j, sm_scale * sum(float(q[b, h, i, c]) * float(k[b, hk, j, c]) for c in range(d))))
+                mx = max(s for _, s in sc)
+                den = sum(math.exp(s - mx) for _, s in sc)
+                for c in range(d):
+                    out[b, h, i, c] = sum(math.exp(s - mx) * float(v[b, hk, j, c]) for j, s in sc) / den
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (4, 2)])
+def test_exact_attention_brute_force(causal, H, H_kv):
+    g = np.random.default_rng(3)
+    q = g.standard_normal((1, H, 12, 8))
+    k = g.standard_normal((1, H_kv, 12, 8)) + 2
+    v = g.standard_normal((1, H_kv, 12, 8))
+    ref = _brute_attention(q, k, v, causal, 0.4, H // H_kv)
+    got = O.attn_exact(q, k, v, causal=causal, sm_scale=0.4)
+    assert np.abs(got - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_attention_matches_sdpa(causal):
+    w = W.get("tiny")
+    t = W.generate(w)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        t["q"].double(), t["k"].double(), t["v"].double(), is_causal=causal,
+        scale=w.sm_scale).numpy()
+    got = O.attn_exact(t["q"], t["k"], t["v"], causal=causal, sm_scale=w.sm_scale)
+    assert np.abs(got - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    w = W.get("tiny")
+    t = W.generate(w)
+    p = O.softmax_rows(t["q"], t["k"], causal=causal, sm_scale=w.sm_scale, h=1)
+    assert np.abs(p.sum(axis=1) - 1).max() <= 1e-12
+    if causal:
+        assert (np.triu(p, 1) == 0).all()
+
+
+# --------------------------------------------------------------------- quantized attention
+
+def _quant_all(t, smooth=True):
+    qz = O.quantize_qk(t["q"], t["k"], smooth_k=smooth)
+    vz = O.quantize_v(t["v"])
+    return qz, vz
+
+
+def _aq(qz, vz, **kw):
+    return O.attn_quant(qz["q_i8"], qz["q_scale"], qz["k_i8"], qz["k_scale"],
+                        vz["v_f8"], vz["v_scale"], **kw)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("grp", [1, 2])
+def test_closed_form_matches_literal_recursion(causal, grp):
+    g = np.random.default_rng(4)
+    n, d, H = 45, 8, 2 * grp
+    q = torch.from_numpy(g.standard_normal((1, H, n, d)).astype(np.float32) * 2).half()
+    k = torch.from_numpy(g.standard_normal((1, 2, n, d)).astype(np.float32) + 3).half()
+    v = torch.from_numpy(g.standard_normal((1, 2, n, d)).astype(np.float32)).half()
+    qz = O.quantize_qk(q, k)
+    vz = O.quantize_v(v)
+    kw = dict(causal=causal, sm_scale=0.35, kv_tile=16, blkq=16, blkk=8)
+    qz16 = dict(q_i8=qz["q_i8"], k_i8=qz["k_i8"])
+    # per-16 / per-8 scales so several scale blocks fall in one run
+    _, qs = O.quantize_int8_blocks(q.float().numpy(), 16)
+    qc, _ = O.quantize_int8_blocks(q.float().numpy(), 16)
+    ks32 = (k.float().numpy() - qz["k_mean"][:, :, None, :]).astype(np.float32)
+    kc, kss = O.quantize_int8_blocks(ks32, 8)
+    a = O.attn_quant(qc, qs, kc, kss, vz["v_f8"], vz["v_scale"], **kw)
+    for h in range(H):
+        r = O.attn_quant_recursive(qc, qs, kc, kss, vz["v_f8"], vz["v_scale"],
+                                   causal=causal, sm_scale=0.35, kv_tile=16, h=h,
+                                   hk=h // grp, blkq=16, blkk=8)
+        assert np.abs(a[0, h] - r).max() < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_q_gives_mean_of_dequantized_v(causal):
+    w = W.get("tiny")
+    t = W.generate(w)
+    t["q"] = torch.zeros_like(t["q"])
+    qz, vz = _quant_all(t)
+    assert (qz["q_scale"] == 0).all()
+    o = _aq(qz, vz, causal=causal, sm_scale=w.sm_scale)
+    vdq = F8.decode(vz["v_f8"]) * vz["v_scale"][:, :, None, :].astype(np.float64)
+    if causal:
+        ref = np.cumsum(vdq, axis=2) / np.arange(1, w.N + 1)[None, None, :, None]
+    else:
+        ref = np.broadcast_to(vdq.mean(axis=2, keepdims=True), vdq.shape)
+    assert np.abs(o - ref).max() < 1e-12
+
+
+def test_constant_v_returns_it():
+    w = W.get("tiny")
+    t = W.generate(w)
+    row = torch.linspace(-3, 3, w.d).half()
+    t["v"] = row.expand_as(t["v"]).contiguous()
+    qz, vz = _quant_all(t)
+    o = _aq(qz, vz, causal=True, sm_scale=w.sm_scale)
+    vdq = F8.decode(vz["v_f8"][0, 0, 0]) * vz["v_scale"][0, 0].astype(np.float64)
+    # weights sum to l * 448 up to the FP8 rounding of P, so O is v times a
+    # factor within the P-rounding error of 1
+    ratio = o / vdq[None, None, None, :]
+    fin = np.isfinite(ratio) & (np.abs(vdq) > 0)[None, None, None, :]
+    assert np.abs(ratio[fin] - 1).max() < 2 ** -4
+
+
+def test_one_dominant_key():
+    g = np.random.default_rng(5)
+    n, d = 64, 16
+    k = g.standard_normal((1, 1, n, d)).astype(np.float32)
+    q = np.zeros((1, 1, n, d), dtype=np.float32)
+    q[..., :] = 40 * k[0, 0, 17]                        # every query aligns with key 17
+    v = g.standard_normal((1, 1, n, d)).astype(np.float32)
+    qz = O.quantize_qk(torch.from_numpy(q).half(), torch.from_numpy(k).half(), smooth_k=False)
+    vz = O.quantize_v(torch.from_numpy(v).half())
+    o = _aq(qz, vz, causal=False, sm_scale=1.0)
+    vdq = F8.decode(vz["v_f8"][0, 0, 17]) * vz["v_scale"][0, 0]
+    assert np.abs(o[0, 0] - vdq[None, :]).max() < 1e-6
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_unrounded_p_equals_exact_attention_on_dequantized_inputs(causal):
+    w = W.get("tiny")
+    t = W.generate(w)
+    qz, vz = _quant_all(t)
+    got = _aq(qz, vz, causal=causal, sm_scale=w.sm_scale, quantize_p=False)
+    qd = qz["q_i8"].astype(np.float64) * np.repeat(qz["q_scale"], 128, axis=-1)[..., :w.N, None]
+    kd = qz["k_i8"].astype(np.float64) * np.repeat(qz["k_scale"], 64, axis=-1)[..., :w.N, None]
+    vd = F8.decode(vz["v_f8"]) * vz["v_scale"][:, :, None, :].astype(np.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qd), torch.from_numpy(kd), torch.from_numpy(vd),
+        is_causal=causal, scale=w.sm_scale).numpy()
+    assert np.abs(got - ref).max() < 1e-12
+
+
+def test_tile_choice_changes_little():
+    w = W.get("tiny")
+    t = W.generate(w)
+    qz, vz = _quant_all(t)
+    a = _aq(qz, vz, causal=False, sm_scale=w.sm_scale, kv_tile=128)
+    b = _aq(qz, vz, causal=False, sm_scale=w.sm_scale, kv_tile=w.N)
+    m = O.metrics(a, b)
+    assert m["max_abs"] < 2e-2 and m["cos"] > 0.9995
+
+
+# --------------------------------------------------------------------- accuracy self-check
+
+def _sample_check(name, heads, nrows, seed):
+    w = W.get(name)
+    t = W.generate(w, heads=heads)
+    qz, vz = _quant_all(t)
+    g = np.random.default_rng(seed)
+    rows = np.sort(g.choice(w.N, size=min(nrows, w.N), replace=False))
+    if w.causal:
+        rows = np.unique(np.concatenate([rows, [0, 1, w.N - 1]]))
+    oq = _aq(qz, vz, causal=w.causal, sm_scale=w.sm_scale, rows=rows, heads=heads)
+    oe = O.attn_exact(t["q"], t["k"], t["v"], causal=w.causal, sm_scale=w.sm_scale,
+                      rows=rows, heads=heads)
+    sel = np.array([[b, h] for b, h in heads])
+    m = O.metrics(oq[sel[:, 0], sel[:, 1]], oe[sel[:, 0], sel[:, 1]])
+    assert m["cos"] >= 0.998, m
+    return m
+
+
+def test_quantized_vs_exact_tiny_full():
+    w = W.get("tiny")
+    t = W.generate(w)
+    qz, vz = _quant_all(t)
+    m = O.metrics(_aq(qz, vz, causal=False, sm_scale=w.sm_scale),
+                  O.attn_exact(t["q"], t["k"], t["v"], causal=False, sm_scale=w.sm_scale))
+    assert m["cos"] >= 0.998
+
+
+@pytest.mark.parametrize("name,heads", [
+    ("llm_prefill", [(0, 0), (0, 31)]),
+    ("video_dit", [(0, 7)]),
+    ("sweep@N1024", [(3, 5)]),
+    ("gqa_long", [(0, 13)]),
+])
+def test_quantized_vs_exact_sampled(name, heads):
+    _sample_check(name, heads, 96, 7)
