@@ -1,0 +1,173 @@
+/*
+ * sage.h -- C ABI of the MI355X (gfx950) quantized attention forward pass.
+ *
+ * The method (SageAttention2 detail page, Algorithm 1, with INT8 Q/K as the
+ * source-analysis page's "Q/K 统一走 INT8" and without smoothing Q):
+ *   1. Smooth K: subtract the per-channel mean of K over tokens
+ *      (SageAttention synthesis page, Smooth K; Algorithm 1 preprocessing).
+ *   2. Quantize Q per block of 128 tokens and smoothed K per block of 64
+ *      tokens to INT8 with one FP32 scale per block: scale = amax / 127,
+ *      code = round-half-even(x / scale) (deployment-guide page, quantization
+ *      formula; block sizes b_q = 128, b_kv = 64 from the detail page's
+ *      "Optimization Techniques" table).
+ *   3. Quantize V per channel to FP8 E4M3 with one FP32 scale per channel:
+ *      scale = amax / 448 (Algorithm 1's psi_V; source-analysis page: V is
+ *      transposed, padded and permuted before the per-channel FP8 cast).
+ *   4. Tiled online-softmax attention: S = (Q^ K^T) dQ dK sm_scale on INT8
+ *      matrix cores, P~ = exp(S - m_running) scaled by 448 and cast to FP8
+ *      E4M3, O accumulated in FP32 from FP8 P~ V products, final
+ *      O = O / l / 448 * dV (Algorithm 1, the inner loop and the final
+ *      rescale; online-softmax update on the source-analysis page).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors), caller-owned, contiguous, and must not alias each other.
+ *     The library allocates nothing and keeps no state between calls; the
+ *     entry points are re-entrant and thread-safe.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and returns without synchronizing.  Read outputs only after
+ *     synchronizing the stream.
+ *   - Arguments are validated on the host before anything is launched; the
+ *     first violated rule is returned and nothing is enqueued.  Launch
+ *     failures return SAGE_ERR_HIP.  Nothing throws across the ABI.
+ *   - Layouts: Q, O are [B][H][N][d]; K, V are [B][H_kv][N][d] (the HND
+ *     layout, source-analysis page, input checks); query head h reads kv
+ *     head h / (H / H_kv) (GQA: H must be a multiple of H_kv).
+ *   - d must be 64 or 128 (the pages' kernels cover head dims 64 and 128 and
+ *     reject d > 128).  Inputs are fp16 or bf16 (the pages accept only these).
+ *   - Non-finite inputs are outside the method's domain (the pages do not
+ *     treat NaN/Inf); results for them are unspecified.
+ */
+#ifndef SAGE_H_
+#define SAGE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_ABI_VERSION 1
+
+/* Q tokens per INT8 scale, K tokens per INT8 scale. */
+#define SAGE_BLKQ 128
+#define SAGE_BLKK 64
+/* Keys per online-softmax step; also the padding unit of the FP8 V layout. */
+#define SAGE_KV_TILE 128
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  SAGE_ERR_SHAPE = 2,     /* B, H, H_kv or N <= 0, or sizes overflow           */
+  SAGE_ERR_HEADDIM = 3,   /* d not in {64, 128}                                */
+  SAGE_ERR_GQA = 4,       /* H % H_kv != 0                                     */
+  SAGE_ERR_DTYPE = 5,     /* dtype not SAGE_FP16 / SAGE_BF16                   */
+  SAGE_ERR_ARG = 6,       /* sm_scale not finite or <= 0; bad flag or index    */
+  SAGE_ERR_WORKSPACE = 7, /* workspace NULL or smaller than required           */
+  SAGE_ERR_HIP = 8,       /* a HIP launch or runtime call failed               */
+  SAGE_ERR_ALIGN = 9      /* a pointer is not 16-byte aligned                  */
+} sage_status;
+
+typedef enum { SAGE_FP16 = 0, SAGE_BF16 = 1 } sage_dtype;
+
+/* Byte sizes of every buffer the entry points take, for given shapes. */
+typedef struct {
+  size_t q_i8;      /* int8  [B][H][N][d]                                       */
+  size_t q_scale;   /* float [B][H][ceil(N/128)]                                */
+  size_t k_i8;      /* int8  [B][H_kv][N][d]                                    */
+  size_t k_scale;   /* float [B][H_kv][ceil(N/64)]                              */
+  size_t k_mean;    /* float [B][H_kv][d]                                       */
+  size_t v_f8;      /* uint8 [B][H_kv][ceil(N/128)*128*d], layout below         */
+  size_t v_scale;   /* float [B][H_kv][d]                                       */
+  size_t o;         /* fp16/bf16 [B][H][N][d]                                   */
+  size_t ws_quant_qk; /* workspace bytes sage_quant_qk needs                    */
+  size_t ws_quant_v;  /* workspace bytes sage_quant_v needs                     */
+} sage_sizes;
+
+/*
+ * Layout of v_f8 (private to sage_quant_v / sage_attn_fwd, published so
+ * callers and tests can decode it).  Per (b, kv head), V is cut into tiles
+ * of 128 keys (keys >= N are zero codes).  A tile holds 128*d bytes as
+ * 2 key halves (kb = 0, 1: keys kb*64 .. kb*64+63) x d/32 channel blocks
+ * (cb) x 2 parts (p) x 64 lanes (L) x 16 bytes (i):
+ *     offset = tile*128*d + ((kb*(d/32) + cb)*2 + p)*1024 + L*16 + i
+ * holds the code of V[key][chan] with
+ *     chan = cb*32 + (L % 32),    s = p*16 + i,    g = L / 32,
+ *     key  = tile*128 + kb*64 + (s / 16)*32 + ((s % 16) / 4)*8 + g*4 + (s % 4).
+ * (This is the transpose + pad + fixed permutation of the source-analysis
+ * page's FP8 V preparation, chosen so one 32-byte row fragment per lane
+ * feeds the FP8 matrix core with keys in the order the INT8 matrix core
+ * leaves P in registers.)
+ */
+
+/* Fill *out with buffer sizes.  Host only; touches no device. */
+sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, sage_sizes* out);
+
+/*
+ * Steps 1-2: smooth K and quantize Q and K to INT8.
+ *   q [B][H][N][d], k [B][H_kv][N][d] in `dtype` (read only).
+ *   smooth_k: 1 = subtract the per-channel token mean of K before
+ *     quantizing (the mean is the exact sum over all N tokens, divided by N
+ *     and rounded to float32); 0 = no smoothing (k_mean is written as 0).
+ *   Outputs: q_i8, q_scale, k_i8, k_scale, k_mean (shapes in sage_sizes).
+ *     scale = float32(amax / 127) with IEEE division over the block's valid
+ *     tokens; code = RNE(float32(x / scale)) clamped to [-127, 127]; an
+ *     all-zero block has scale 0 and codes 0.  Deterministic, bit-exact.
+ *   workspace: >= sizes.ws_quant_qk bytes of device memory (scratch; its
+ *     contents on entry do not matter).
+ */
+sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype,
+                          int B, int H, int H_kv, int N, int d, int smooth_k,
+                          int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                          float* k_mean, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Step 3: per-channel FP8 E4M3 quantization of V.
+ *   v [B][H_kv][N][d] in `dtype`.
+ *   Outputs: v_f8 (layout above) and v_scale [B][H_kv][d]:
+ *     scale = float32(amax / 448) over all N tokens of the channel;
+ *     code = E4M3_RNE(clamp(float32(v / scale), -448, 448)) (OCP E4M3,
+ *     no infinities); zero channel -> scale 0, codes 0.
+ *   workspace: >= sizes.ws_quant_v bytes.
+ */
+sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N, int d,
+                         uint8_t* v_f8, float* v_scale, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * Step 4: the attention kernel.
+ *   Inputs are the outputs of sage_quant_qk / sage_quant_v for the same
+ *   shapes.  o [B][H][N][d] is written in `out_dtype` (round to nearest even).
+ *   causal: 1 = key j visible to query i iff j <= i; fully masked key tiles
+ *     are skipped.  sm_scale: the softmax scale (> 0, finite), commonly
+ *     1/sqrt(d).
+ *   P~ is quantized against the running max of the keys seen so far, one
+ *   128-key tile at a time; l sums the unquantized P~.
+ */
+sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                          const float* k_scale, const uint8_t* v_f8, const float* v_scale,
+                          void* o, sage_dtype out_dtype, int B, int H, int H_kv, int N, int d,
+                          int causal, float sm_scale, void* stream);
+
+/*
+ * Diagnostic: the exact int32 dot products sum_c q_i8[b][h][i][c] *
+ * k_i8[b][h/(H/H_kv)][j][c] of one query head, computed by the same INT8
+ * matrix-core tile routine and K loader the attention kernel uses.
+ *   s_out: int32 [N][N] (row = query i, column = key j), caller-owned.
+ *   b in [0, B), h in [0, H), else SAGE_ERR_ARG.
+ */
+sage_status sage_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int H_kv,
+                          int N, int d, int b, int h, int32_t* s_out, void* stream);
+
+/* Static description of a status code. */
+const char* sage_status_str(sage_status s);
+
+/* SAGE_ABI_VERSION of the built library. */
+int sage_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H_ */

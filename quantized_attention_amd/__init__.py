@@ -1,0 +1,245 @@
+"""MI355X (gfx950) quantized attention forward pass: Python binding.
+
+A thin ctypes layer over ``libsage_amd.so`` (the C ABI in ``include/sage.h``).
+It only marshals arguments: every step of the method runs in the HIP
+kernels; PyTorch provides device memory and the current stream.  There is no
+CPU fallback -- if the library is not built or no GPU is visible, calls fail.
+
+The method (SageAttention2 detail page, Algorithm 1, with INT8 Q/K):
+smooth K by its token mean, quantize Q (per 128 tokens) and K (per 64 tokens)
+to INT8 with FP32 scales, quantize V per channel to FP8 E4M3, then run a tiled
+online-softmax attention with INT8 QK^T and FP8 PV (P scaled by 448).
+
+Entry points (same names as the C ABI):
+    sage_buffer_sizes(B, H, H_kv, N, d) -> dict of byte sizes
+    sage_quant_qk(q, k, smooth_k=True) -> dict(q_i8, q_scale, k_i8, k_scale, k_mean)
+    sage_quant_v(v) -> dict(v_f8, v_scale)
+    sage_attn_fwd(qk, vq, causal=..., sm_scale=..., out_dtype=...) -> o
+    sage_qk_int32(q_i8, k_i8, b, h) -> int32 [N, N] (diagnostic)
+and the composition ``sageattn(q, k, v, is_causal=False, sm_scale=None)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["SageError", "library_path", "load_library", "sage_buffer_sizes", "sage_quant_qk",
+           "sage_quant_v", "sage_attn_fwd", "sage_qk_int32", "sageattn", "SagePlan",
+           "BLKQ", "BLKK", "KV_TILE"]
+
+BLKQ, BLKK, KV_TILE = 128, 64, 128
+_FP16, _BF16 = 0, 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, msg: str, where: str):
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+class _Sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_f8", "v_scale", "o",
+        "ws_quant_qk", "ws_quant_v")]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libsage_amd.so")
+
+
+def load_library():
+    """Load libsage_amd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m quantized_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.sage_abi_version.restype = i
+    lib.sage_status_str.argtypes = [i]
+    lib.sage_status_str.restype = ctypes.c_char_p
+    lib.sage_buffer_sizes.argtypes = [i, i, i, i, i, ctypes.POINTER(_Sizes)]
+    lib.sage_quant_qk.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sage_quant_v.argtypes = [vp, i, i, i, i, i, vp, vp, vp, sz, vp]
+    lib.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                  ctypes.c_float, vp]
+    lib.sage_qk_int32.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp]
+    for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_quant_v", "sage_attn_fwd",
+              "sage_qk_int32"):
+        getattr(lib, f).restype = i
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        msg = load_library().sage_status_str(status).decode()
+        raise SageError(status, msg, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dt(dtype) -> int:
+    if dtype == torch.float16:
+        return _FP16
+    if dtype == torch.bfloat16:
+        return _BF16
+    raise TypeError(f"q/k/v must be float16 or bfloat16, got {dtype}")
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if not (isinstance(t, torch.Tensor) and t.is_cuda):
+            raise ValueError("all tensors must be CUDA (HIP) device tensors")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def sage_buffer_sizes(B: int, H: int, H_kv: int, N: int, d: int) -> dict:
+    s = _Sizes()
+    _check(load_library().sage_buffer_sizes(B, H, H_kv, N, d, ctypes.byref(s)), "sage_buffer_sizes")
+    return {n: getattr(s, n) for n, _ in _Sizes._fields_}
+
+
+def _alloc_qk(B, H, H_kv, N, d, device):
+    nq, nk = -(-N // BLKQ), -(-N // BLKK)
+    return dict(
+        q_i8=torch.empty((B, H, N, d), dtype=torch.int8, device=device),
+        q_scale=torch.empty((B, H, nq), dtype=torch.float32, device=device),
+        k_i8=torch.empty((B, H_kv, N, d), dtype=torch.int8, device=device),
+        k_scale=torch.empty((B, H_kv, nk), dtype=torch.float32, device=device),
+        k_mean=torch.empty((B, H_kv, d), dtype=torch.float32, device=device),
+    )
+
+
+def _alloc_v(B, H_kv, N, d, device):
+    npad = -(-N // KV_TILE) * KV_TILE
+    return dict(
+        v_f8=torch.empty((B, H_kv, npad * d), dtype=torch.uint8, device=device),
+        v_scale=torch.empty((B, H_kv, d), dtype=torch.float32, device=device),
+    )
+
+
+def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *, out=None,
+                  workspace=None, stream=None) -> dict:
+    """Smooth K and quantize Q, K to INT8 (see sage.h for exact semantics)."""
+    _need_gpu(q, k)
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share a dtype")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (B, H_kv, N, d):
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    out = out or _alloc_qk(B, H, H_kv, N, d, q.device)
+    if workspace is None and smooth_k:
+        ws = sage_buffer_sizes(B, H, H_kv, N, d)["ws_quant_qk"]
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    st = load_library().sage_quant_qk(
+        q.data_ptr(), k.data_ptr(), _dt(q.dtype), B, H, H_kv, N, d, int(bool(smooth_k)),
+        out["q_i8"].data_ptr(), out["q_scale"].data_ptr(), out["k_i8"].data_ptr(),
+        out["k_scale"].data_ptr(), out["k_mean"].data_ptr(), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream, q.device))
+    _check(st, "sage_quant_qk")
+    return out
+
+
+def sage_quant_v(v: torch.Tensor, *, out=None, workspace=None, stream=None) -> dict:
+    """Per-channel FP8 E4M3 quantization of V into the fragment layout of sage.h."""
+    _need_gpu(v)
+    B, H_kv, N, d = v.shape
+    out = out or _alloc_v(B, H_kv, N, d, v.device)
+    if workspace is None:
+        ws = sage_buffer_sizes(B, H_kv, H_kv, N, d)["ws_quant_v"]
+        workspace = torch.empty(ws, dtype=torch.uint8, device=v.device)
+    st = load_library().sage_quant_v(
+        v.data_ptr(), _dt(v.dtype), B, H_kv, N, d, out["v_f8"].data_ptr(),
+        out["v_scale"].data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream, v.device))
+    _check(st, "sage_quant_v")
+    return out
+
+
+def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
+                  out_dtype=torch.float16, out=None, stream=None) -> torch.Tensor:
+    """Attention on quantized inputs; returns O [B, H, N, d] in out_dtype."""
+    q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
+    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"])
+    B, H, N, d = q_i8.shape
+    H_kv = k_i8.shape[1]
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
+    _need_gpu(out)
+    st = load_library().sage_attn_fwd(
+        q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
+        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
+        B, H, H_kv, N, d, int(bool(causal)), float(sm_scale), _stream(stream, q_i8.device))
+    _check(st, "sage_attn_fwd")
+    return out
+
+
+def sage_qk_int32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, *,
+                  stream=None) -> torch.Tensor:
+    """Exact int32 Q^ K^T of query head (b, h) through the attention kernel's tile routine."""
+    _need_gpu(q_i8, k_i8)
+    B, H, N, d = q_i8.shape
+    H_kv = k_i8.shape[1]
+    s = torch.empty((N, N), dtype=torch.int32, device=q_i8.device)
+    st = load_library().sage_qk_int32(q_i8.data_ptr(), k_i8.data_ptr(), B, H, H_kv, N, d, b, h,
+                                      s.data_ptr(), _stream(stream, q_i8.device))
+    _check(st, "sage_qk_int32")
+    return s
+
+
+def sageattn(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
+             smooth_k: bool = True) -> torch.Tensor:
+    """The whole forward pass: quantize Q/K/V, then the attention kernel."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    qk = sage_quant_qk(q, k, smooth_k)
+    vq = sage_quant_v(v)
+    return sage_attn_fwd(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype)
+
+
+class SagePlan:
+    """Preallocated buffers for repeated calls on fixed shapes (no allocation per call)."""
+
+    def __init__(self, B, H, H_kv, N, d, dtype, causal, sm_scale=None, device="cuda"):
+        self.shape = (B, H, H_kv, N, d)
+        self.dtype, self.causal = dtype, causal
+        self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+        sz = sage_buffer_sizes(B, H, H_kv, N, d)
+        self.qk = _alloc_qk(B, H, H_kv, N, d, device)
+        self.vq = _alloc_v(B, H_kv, N, d, device)
+        self.ws_qk = torch.empty(max(sz["ws_quant_qk"], 16), dtype=torch.uint8, device=device)
+        self.ws_v = torch.empty(max(sz["ws_quant_v"], 16), dtype=torch.uint8, device=device)
+        self.o = torch.empty((B, H, N, d), dtype=dtype, device=device)
+
+    def quant(self, q, k, v, stream=None):
+        sage_quant_qk(q, k, True, out=self.qk, workspace=self.ws_qk, stream=stream)
+        sage_quant_v(v, out=self.vq, workspace=self.ws_v, stream=stream)
+
+    def attn(self, stream=None):
+        return sage_attn_fwd(self.qk, self.vq, causal=self.causal, sm_scale=self.sm_scale,
+                             out_dtype=self.dtype, out=self.o, stream=stream)
+
+    def __call__(self, q, k, v, stream=None):
+        self.quant(q, k, v, stream)
+        return self.attn(stream)

@@ -1,0 +1,316 @@
+// attn_fwd.hip -- INT8 QK^T / FP8 PV online-softmax attention for gfx950.
+//
+// Algorithm 1 of the SageAttention2 detail page (inner loop and final
+// rescale), with INT8 Q/K codes and per-block FP32 scales, FP8 E4M3 V with
+// per-channel scales, and P~ * 448 cast to FP8 before the P V product.
+//
+// Work decomposition: one workgroup = 4 waves = 128 queries of one head (one
+// Q scale block).  Each wave owns 32 queries and computes S^T = K Q^T for a
+// 128-key tile as four 32x32 INT8 MFMA blocks, so every lane holds the
+// scores of ONE query (column L % 32) for 64 of the tile's keys; the other
+// 64 keys sit in lane L ^ 32.  Row max and row sum are therefore in-lane
+// plus one cross-half exchange.  P~ is converted to FP8 in registers and fed
+// as the B operand of the 32x32x64 FP8 MFMA (O^T = V^T P^T); V^T arrives
+// from HBM already permuted (sage.h, v_f8 layout) so that its keys line up
+// with the register order of P.  K and V^T tiles are double-buffered in LDS.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <hip/hip_bf16.h>
+#include <limits.h>
+#include <math.h>
+
+#include <type_traits>
+
+#include "sage_device.hpp"
+
+namespace sage {
+
+template <int D, bool CAUSAL, bool BF16>
+__global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
+    const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
+    const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
+    const uint8_t* __restrict__ v_f8, const float* __restrict__ v_scale,
+    void* __restrict__ out, int H, int H_kv, int N, float sm_log2, int nqt, int total) {
+  constexpr int NKC = D / 32;                 // 32-wide channel chunks
+  constexpr int KBYTES = kKvTile * D;         // K tile bytes (== V tile bytes)
+  __shared__ __attribute__((aligned(16))) char lds[2][2 * KBYTES];
+
+  // ---- which (b, kv head, q tile, group member) this workgroup computes.
+  // Logical order: the `group` query heads that share a kv head are
+  // adjacent and walk the q tiles together (they read the same K/V tiles);
+  // causal runs the heaviest q tiles first.
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int group = H / H_kv;
+  int rest = lid;
+  const int gm = rest % group; rest /= group;
+  int qt = rest % nqt; rest /= nqt;
+  const int hk = rest % H_kv;
+  const int b = rest / H_kv;
+  if (CAUSAL) qt = nqt - 1 - qt;
+  const int h = hk * group + gm;
+
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int col = lane & 31, half = lane >> 5;
+  const int q0 = qt * kBlockQ + wave * kWaveQ;
+  const int qi = q0 + col;                    // this lane's query row
+
+  const int8_t* qh = q_i8 + (size_t)(b * H + h) * N * D;
+  const int8_t* kh = k_i8 + (size_t)(b * H_kv + hk) * N * D;
+  const int ntk = (N + kKvTile - 1) / kKvTile;
+  const uint8_t* vh = v_f8 + (size_t)(b * H_kv + hk) * ntk * KBYTES;
+  const int nkb = (N + kBlkK - 1) / kBlkK;
+  const float* ksc = k_scale + (size_t)(b * H_kv + hk) * nkb;
+  const int ntiles = CAUSAL ? qt + 1 : ntk;
+
+  // Q fragments for the whole loop (B operand of S^T = K Q^T).
+  i32x4 qf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc)
+    qf[kc] = (qi < N) ? *reinterpret_cast<const i32x4*>(qh + (size_t)qi * D + kc * 32 + half * 16)
+                      : i32x4{0, 0, 0, 0};
+  const float cq = q_scale[(size_t)(b * H + h) * nqt + qt] * sm_log2;
+
+  f32x16 acc_o[NKC];
+#pragma unroll
+  for (int c = 0; c < NKC; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[c][r] = 0.f;
+  float m_run = -INFINITY;   // running max of the log2-domain scores
+  float l_part = 0.f;        // this lane's share of sum 448*P~
+
+  load_k_tile<D>(kh, 0, N, lds[0], wave, lane);
+  load_v_tile<D>(vh, lds[0] + KBYTES, wave, lane);
+
+  // One 128-key step of the online softmax.  MASK: the tile holds keys past
+  // the diagonal (causal) or past N; only the last tile can.
+  auto step = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // Tile t has landed in buffer t&1 for every wave; buffer (t+1)&1 was
+    // last read in iteration t-1, which every wave has finished.
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      load_k_tile<D>(kh, (t + 1) * kKvTile, N, lds[(t + 1) & 1], wave, lane);
+      load_v_tile<D>(vh + (size_t)(t + 1) * KBYTES, lds[(t + 1) & 1] + KBYTES, wave, lane);
+    }
+    const char* kt = lds[t & 1];
+    const char* vt = lds[t & 1] + KBYTES;
+
+    // ---- S^T = K Q^T on the INT8 matrix cores (exact int32 sums).
+    i32x16 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) s[kb] = qk_block<NKC>(kt + kb * NKC * 1024, qf, lane);
+
+    // Per 32-key block: combined dequant factor (log2 domain).
+    float ck[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int kidx = (t * kKvTile + kb * 32) / kBlkK;
+      // in a tail tile a 32-key block may lie wholly past N: clamp the read
+      // (its scores are masked anyway)
+      ck[kb] = cq * ksc[MASK ? min(kidx, nkb - 1) : kidx];
+    }
+
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = t * kKvTile + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+          if ((CAUSAL && key > qi) || key >= N) s[kb][r] = INT_MIN;
+        }
+    }
+
+    // ---- tile row max (in-lane on the int bits, then across the lane halves).
+    float xm = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      int fm = s[kb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) fm = max(fm, s[kb][r]);
+      const float x = (as_float(fm) - kMagic) * ck[kb];
+      xm = MASK ? (fm != INT_MIN ? fmaxf(xm, x) : xm) : fmaxf(xm, x);
+    }
+    xm = fmaxf(xm, __shfl_xor(xm, 32));
+    const float m_new = fmaxf(m_run, xm);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_part *= alpha;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int c = 0; c < NKC; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[c][r] *= alpha;
+    }
+
+    // ---- P~ * 448 = exp2(score - m + log2 448), summed unquantized, cast to FP8.
+    // The score is (f - kMagic) * ck with f the biased float of the int32
+    // sum.  When ck is small, f*ck - (kMagic*ck + m') in one FMA is exact up
+    // to ulp(kMagic*ck)/2 <= 2^-11 (log2 units); otherwise subtract kMagic
+    // first (exact) and then apply ck.  ck is uniform over the wave.
+    const float mq = m_new - kLog2_448;
+    const bool fast = fmaxf(fmaxf(ck[0], ck[1]), fmaxf(ck[2], ck[3])) <= kFastCk;
+    i32x8 pf[2];
+    auto exp_block = [&](auto fast_tag) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float off = fmaf(kMagic, ck[kb], mq);
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float a = decltype(fast_tag)::value
+                              ? fmaf(as_float(s[kb][r]), ck[kb], -off)
+                              : fmaf(as_float(s[kb][r]) - kMagic, ck[kb], -mq);
+          e[r] = __builtin_amdgcn_exp2f(a);
+          if constexpr (MASK) e[r] = (s[kb][r] == INT_MIN) ? 0.f : e[r];
+          l_part += e[r];
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], pk, true);
+          pf[kb / 2][(kb % 2) * 4 + w] = pk;
+        }
+      }
+    };
+    if (fast) exp_block(std::true_type{});
+    else exp_block(std::false_type{});
+
+    // ---- O^T += V^T P^T on the FP8 matrix cores (FP32 accumulation).
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+        const char* vp = vt + ((kb * NKC + c) * 2) * 1024 + lane * 16;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(vp);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(vp + 1024);
+        const i32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf[kb], acc_o[c], 0, 0,
+                                                                     0, 127, 0, 127);
+      }
+  };
+
+  const bool last_masked = CAUSAL || (N % kKvTile) != 0;
+  const int nfull = last_masked ? ntiles - 1 : ntiles;
+  for (int t = 0; t < nfull; ++t) step(t, std::false_type{});
+  if (last_masked) step(ntiles - 1, std::true_type{});
+
+  // ---- O = O / l * dV (l already carries the factor 448).
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) pin(acc_o[c]);
+  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float inv = 1.0f / l_tot;
+  if (qi < N) {
+    char* orow = reinterpret_cast<char*>(out) + ((size_t)(b * H + h) * N + qi) * D * 2;
+    const float* vs = v_scale + (size_t)(b * H_kv + hk) * D;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ch = c * 32 + 8 * r4 + 4 * half;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = acc_o[c][r4 * 4 + j] * inv * vs[ch + j];
+        uint2 pk;
+        if (BF16) {
+          __hip_bfloat16 x0 = __float2bfloat16(v[0]), x1 = __float2bfloat16(v[1]);
+          __hip_bfloat16 x2 = __float2bfloat16(v[2]), x3 = __float2bfloat16(v[3]);
+          pk.x = (uint32_t)__builtin_bit_cast(uint16_t, x0) | ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+          pk.y = (uint32_t)__builtin_bit_cast(uint16_t, x2) | ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16);
+        } else {
+          __half x0 = __float2half(v[0]), x1 = __float2half(v[1]);
+          __half x2 = __float2half(v[2]), x3 = __float2half(v[3]);
+          pk.x = (uint32_t)__builtin_bit_cast(uint16_t, x0) | ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+          pk.y = (uint32_t)__builtin_bit_cast(uint16_t, x2) | ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16);
+        }
+        *reinterpret_cast<uint2*>(orow + ch * 2) = pk;
+      }
+  }
+}
+
+// Diagnostic: exact int32 S = Q^ K^T of one head, through the same K tile
+// loader, LDS fragment layout and qk_block routine as attn_fwd_kernel.
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
+    const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8, int32_t* __restrict__ s_out,
+    int N, size_t qoff, size_t koff) {
+  constexpr int NKC = D / 32;
+  __shared__ __attribute__((aligned(16))) char lds[kKvTile * D];
+  const int qt = blockIdx.x, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int half = lane >> 5;
+  const int qi = qt * kBlockQ + wave * kWaveQ + (lane & 31);
+  const int8_t* qh = q_i8 + qoff;
+  const int8_t* kh = k_i8 + koff;
+
+  load_k_tile<D>(kh, t * kKvTile, N, lds, wave, lane);
+  wait_vmem();
+  __syncthreads();
+  i32x4 qf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc)
+    qf[kc] = (qi < N) ? *reinterpret_cast<const i32x4*>(qh + (size_t)qi * D + kc * 32 + half * 16)
+                      : i32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    i32x16 s = qk_block<NKC>(lds + kb * NKC * 1024, qf, lane);
+    pin(s);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = t * kKvTile + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+      if (qi < N && key < N)
+        s_out[(size_t)qi * N + key] = s[r] - kMagicBits;
+    }
+  }
+}
+
+}  // namespace sage
+
+// ---------------------------------------------------------------------------
+// Host launchers (called by the C ABI after validation).
+
+hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                const float* k_scale, const uint8_t* v_f8, const float* v_scale,
+                                void* o, int bf16_out, int B, int H, int H_kv, int N, int d,
+                                int causal, float sm_scale, hipStream_t stream) {
+  using namespace sage;
+  const int nqt = (N + kBlockQ - 1) / kBlockQ;
+  const long long total = (long long)B * H * nqt;
+  if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
+  const float sm_log2 = sm_scale * kLog2e;
+  dim3 grid((unsigned)total), block(kWaves * 64);
+#define SAGE_ATTN_CASE(DD, CC, BB)                                                               \
+  if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB) {                                 \
+    hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB>), grid, block, 0, stream, q_i8, q_scale,     \
+                       k_i8, k_scale, v_f8, v_scale, o, H, H_kv, N, sm_log2, nqt, (int)total);  \
+    return hipGetLastError();                                                                    \
+  }
+  SAGE_ATTN_CASE(64, false, false)
+  SAGE_ATTN_CASE(64, false, true)
+  SAGE_ATTN_CASE(64, true, false)
+  SAGE_ATTN_CASE(64, true, true)
+  SAGE_ATTN_CASE(128, false, false)
+  SAGE_ATTN_CASE(128, false, true)
+  SAGE_ATTN_CASE(128, true, false)
+  SAGE_ATTN_CASE(128, true, true)
+#undef SAGE_ATTN_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t sage_launch_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int H_kv,
+                                int N, int d, int b, int h, int32_t* s_out, hipStream_t stream) {
+  using namespace sage;
+  const int nt = (N + kKvTile - 1) / kKvTile;
+  const size_t qoff = (size_t)(b * H + h) * N * d;
+  const size_t koff = (size_t)(b * H_kv + h / (H / H_kv)) * N * d;
+  dim3 grid(nt, nt), block(kWaves * 64);
+  if (d == 64)
+    hipLaunchKernelGGL(qk_int32_kernel<64>, grid, block, 0, stream, q_i8, k_i8, s_out, N, qoff, koff);
+  else if (d == 128)
+    hipLaunchKernelGGL(qk_int32_kernel<128>, grid, block, 0, stream, q_i8, k_i8, s_out, N, qoff, koff);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}

@@ -1,0 +1,317 @@
+// quant.hip -- smoothing and quantization kernels for gfx950 (HBM-bound).
+//
+//   colstats_partial / colstats_final : per-channel token statistics of a
+//       [N][d] slice: the exact FP64 sum of K (its mean smooths K: the
+//       SageAttention synthesis page's Smooth K, Algorithm 1 preprocessing
+//       on the SageAttention2 detail page) or the absolute max of V (the
+//       per-channel FP8 scale of Algorithm 1's psi_V).
+//   quant_int8        : per-block INT8 quantization of Q (128 tokens) and of
+//       smoothed K (64 tokens): scale = amax/127, code = RNE(x/scale)
+//       (deployment-guide page, quantization formula).
+//   quant_v_fp8       : per-channel FP8 E4M3 quantization of V, written
+//       transposed and key-permuted in the fragment layout of sage.h.
+//
+// Every read of the fp16/bf16 inputs is a 16-byte vector load of 8 channels
+// of one token; consecutive threads read consecutive 16-byte chunks.
+// Results are deterministic: FP64 partial sums are combined in a fixed
+// order (and are exact when every partial sum fits 53 bits), maxima are
+// order-free, and every rounding is an explicit IEEE fp32 operation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sage_device.hpp"
+
+namespace sage {
+
+constexpr int kQuantThreads = 256;
+constexpr int kStatChunk = 256;   // tokens per colstats_partial workgroup
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const uint4 u, float* x) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (BF16) {
+      x[2 * i] = as_float((int)(w[i] << 16));
+      x[2 * i + 1] = as_float((int)(w[i] & 0xFFFF0000u));
+    } else {
+      x[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+      x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-channel statistics over a chunk of kStatChunk tokens.
+// MODE 0: FP64 sum (K).  MODE 1: abs max (V), stored as float.
+// grid (nchunk, B*Hkv); ws layout [B*Hkv][nchunk][D] (double or float).
+template <int D, bool BF16, int MODE>
+__global__ __launch_bounds__(kQuantThreads) void colstats_partial(const void* __restrict__ x,
+                                                                  void* __restrict__ ws, int N,
+                                                                  int nchunk) {
+  constexpr int TPR = D / 8;                    // threads per token row
+  constexpr int RPP = kQuantThreads / TPR;      // rows per pass
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, cg = tid % TPR, rsub = tid / TPR;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
+  const int n0 = chunk * kStatChunk, n1 = min(N, n0 + kStatChunk);
+
+  double acc[8];
+  float mx[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { acc[i] = 0.0; mx[i] = 0.f; }
+  for (int n = n0 + rsub; n < n1; n += RPP) {
+    const uint4 u = *reinterpret_cast<const uint4*>(xs + (size_t)n * D + cg * 8);
+    float v[8];
+    unpack8<BF16>(u, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (MODE == 0) acc[i] += (double)v[i];
+      else mx[i] = fmaxf(mx[i], fabsf(v[i]));
+    }
+  }
+  // combine the RPP row groups in a fixed order
+  __shared__ double red[RPP][D];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rsub][cg * 8 + i] = MODE == 0 ? acc[i] : (double)mx[i];
+  __syncthreads();
+  if (tid < D) {
+    if (MODE == 0) {
+      double s = 0.0;
+      for (int r = 0; r < RPP; ++r) s += red[r][tid];
+      reinterpret_cast<double*>(ws)[((size_t)bh * nchunk + chunk) * D + tid] = s;
+    } else {
+      float m = 0.f;
+      for (int r = 0; r < RPP; ++r) m = fmaxf(m, (float)red[r][tid]);
+      reinterpret_cast<float*>(ws)[((size_t)bh * nchunk + chunk) * D + tid] = m;
+    }
+  }
+}
+
+// MODE 0: out[bh][c] = float32(sum / N) (the K mean), or 0 when !enable.
+// MODE 1: out[bh][c] = float32(amax / 448) (the V scale).
+template <int D, int MODE>
+__global__ __launch_bounds__(D) void colstats_final(const void* __restrict__ ws,
+                                                    float* __restrict__ out, int N, int nchunk,
+                                                    int enable) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  if (MODE == 0) {
+    double s = 0.0;
+    if (enable)
+      for (int k = 0; k < nchunk; ++k)
+        s += reinterpret_cast<const double*>(ws)[((size_t)bh * nchunk + k) * D + c];
+    out[(size_t)bh * D + c] = enable ? (float)(s / (double)N) : 0.f;
+  } else {
+    float m = 0.f;
+    for (int k = 0; k < nchunk; ++k)
+      m = fmaxf(m, reinterpret_cast<const float*>(ws)[((size_t)bh * nchunk + k) * D + c]);
+    out[(size_t)bh * D + c] = m / 448.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block max over the workgroup (all threads get the result).
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int wave = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < kQuantThreads / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+// Per-block INT8 quantization of one block of BLK tokens x D channels.
+// SMOOTH: subtract mean[c] (float32) first.  grid (nblk, B*heads).
+template <int D, int BLK, bool BF16, bool SMOOTH>
+__global__ __launch_bounds__(kQuantThreads) void quant_int8(const void* __restrict__ x,
+                                                            const float* __restrict__ mean,
+                                                            int8_t* __restrict__ codes,
+                                                            float* __restrict__ scales, int N,
+                                                            int nblk) {
+  constexpr int TPR = D / 8;
+  constexpr int PER = BLK * TPR / kQuantThreads;   // 16-byte chunks per thread
+  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int cg = tid % TPR;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
+  int8_t* cs = codes + (size_t)bh * N * D;
+
+  float mu[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mu[i] = SMOOTH ? mean[(size_t)bh * D + cg * 8 + i] : 0.f;
+
+  float v[PER][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int row = blk * BLK + (p * kQuantThreads + tid) / TPR;
+    if (row < N) {
+      const uint4 u = *reinterpret_cast<const uint4*>(xs + (size_t)row * D + cg * 8);
+      unpack8<BF16>(u, v[p]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (SMOOTH) v[p][i] = v[p][i] - mu[i];
+        amax = fmaxf(amax, fabsf(v[p][i]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[p][i] = 0.f;
+    }
+  }
+  __shared__ float red[kQuantThreads / 64];
+  amax = block_max(amax, red);
+  const float sc = amax / 127.0f;            // IEEE division
+  if (tid == 0) scales[(size_t)bh * nblk + blk] = sc;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int row = blk * BLK + (p * kQuantThreads + tid) / TPR;
+    if (row >= N) continue;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q = 0.f;
+      if (sc > 0.f) q = fminf(fmaxf(__builtin_rintf(v[p][i] / sc), -127.f), 127.f);
+      w[i / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (i % 4));
+    }
+    *reinterpret_cast<uint2*>(cs + (size_t)row * D + cg * 8) = uint2{w[0], w[1]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 V: one workgroup per 128-key tile of one (b, kv head).
+template <int D, bool BF16>
+__global__ __launch_bounds__(kQuantThreads) void quant_v_fp8(const void* __restrict__ x,
+                                                             const float* __restrict__ vscale,
+                                                             uint8_t* __restrict__ out, int N,
+                                                             int ntile) {
+  constexpr int TPR = D / 8;
+  constexpr int PER = kKvTile * TPR / kQuantThreads;
+  const int tile = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int cg = tid % TPR;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
+  __shared__ __attribute__((aligned(16))) uint8_t st[D][kKvTile];   // [channel][key]
+
+  float sv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sv[i] = vscale[(size_t)bh * D + cg * 8 + i];
+
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int key = (p * kQuantThreads + tid) / TPR;
+    const int n = tile * kKvTile + key;
+    float v[8];
+    if (n < N) {
+      const uint4 u = *reinterpret_cast<const uint4*>(xs + (size_t)n * D + cg * 8);
+      unpack8<BF16>(u, v);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      float y0 = 0.f, y1 = 0.f;
+      if (n < N) {
+        if (sv[i] > 0.f) y0 = fminf(fmaxf(v[i] / sv[i], -448.f), 448.f);
+        if (sv[i + 1] > 0.f) y1 = fminf(fmaxf(v[i + 1] / sv[i + 1], -448.f), 448.f);
+      }
+      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      st[cg * 8 + i][key] = (uint8_t)(pk & 0xFF);
+      st[cg * 8 + i + 1][key] = (uint8_t)((pk >> 8) & 0xFF);
+    }
+  }
+  __syncthreads();
+  // Emit 16-byte chunks in the fragment layout: chunk c = ((kb*(D/32)+cb)*2+p)*64 + L.
+  constexpr int NCH = kKvTile * D / 16;
+  uint8_t* ot = out + ((size_t)bh * ntile + tile) * kKvTile * D;
+#pragma unroll
+  for (int it = 0; it < NCH / kQuantThreads; ++it) {
+    const int c = it * kQuantThreads + tid;
+    const int L = c % 64, p = (c / 64) % 2, cb = (c / 128) % (D / 32), kb = c / (128 * (D / 32));
+    const int chan = cb * 32 + (L % 32), g = L / 32;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // bytes 4q..4q+3 of the chunk: slot s = p*16 + 4q + j, keys are 4 consecutive
+      const int key = kb * 64 + fp8_slot_key(g, p * 16 + 4 * q);
+      w[q] = *reinterpret_cast<const uint32_t*>(&st[chan][key]);
+    }
+    *reinterpret_cast<uint4*>(ot + (size_t)c * 16) = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+}  // namespace sage
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+
+namespace {
+inline int nchunks(int N) { return (N + sage::kStatChunk - 1) / sage::kStatChunk; }
+}  // namespace
+
+size_t sage_ws_quant_qk_bytes(int B, int H_kv, int N, int d) {
+  return (size_t)B * H_kv * nchunks(N) * d * sizeof(double);
+}
+size_t sage_ws_quant_v_bytes(int B, int H_kv, int N, int d) {
+  return (size_t)B * H_kv * nchunks(N) * d * sizeof(float);
+}
+
+template <int D, bool BF16>
+static hipError_t quant_qk_impl(const void* q, const void* k, int B, int H, int H_kv, int N,
+                                int smooth_k, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                                float* k_scale, float* k_mean, void* ws, hipStream_t st) {
+  using namespace sage;
+  const int nc = nchunks(N);
+  const int nbq = (N + kBlkQ - 1) / kBlkQ, nbk = (N + kBlkK - 1) / kBlkK;
+  if (smooth_k) {
+    hipLaunchKernelGGL((colstats_partial<D, BF16, 0>), dim3(nc, B * H_kv), dim3(kQuantThreads), 0,
+                       st, k, ws, N, nc);
+  }
+  hipLaunchKernelGGL((colstats_final<D, 0>), dim3(B * H_kv), dim3(D), 0, st, ws, k_mean, N, nc,
+                     smooth_k);
+  hipLaunchKernelGGL((quant_int8<D, kBlkQ, BF16, false>), dim3(nbq, B * H), dim3(kQuantThreads), 0,
+                     st, q, nullptr, q_i8, q_scale, N, nbq);
+  if (smooth_k)
+    hipLaunchKernelGGL((quant_int8<D, kBlkK, BF16, true>), dim3(nbk, B * H_kv),
+                       dim3(kQuantThreads), 0, st, k, k_mean, k_i8, k_scale, N, nbk);
+  else
+    hipLaunchKernelGGL((quant_int8<D, kBlkK, BF16, false>), dim3(nbk, B * H_kv),
+                       dim3(kQuantThreads), 0, st, k, nullptr, k_i8, k_scale, N, nbk);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+static hipError_t quant_v_impl(const void* v, int B, int H_kv, int N, uint8_t* v_f8,
+                               float* v_scale, void* ws, hipStream_t st) {
+  using namespace sage;
+  const int nc = nchunks(N);
+  const int nt = (N + kKvTile - 1) / kKvTile;
+  hipLaunchKernelGGL((colstats_partial<D, BF16, 1>), dim3(nc, B * H_kv), dim3(kQuantThreads), 0, st,
+                     v, ws, N, nc);
+  hipLaunchKernelGGL((colstats_final<D, 1>), dim3(B * H_kv), dim3(D), 0, st, ws, v_scale, N, nc, 1);
+  hipLaunchKernelGGL((quant_v_fp8<D, BF16>), dim3(nt, B * H_kv), dim3(kQuantThreads), 0, st, v,
+                     v_scale, v_f8, N, nt);
+  return hipGetLastError();
+}
+
+hipError_t sage_launch_quant_qk(const void* q, const void* k, int bf16, int B, int H, int H_kv,
+                                int N, int d, int smooth_k, int8_t* q_i8, float* q_scale,
+                                int8_t* k_i8, float* k_scale, float* k_mean, void* ws,
+                                hipStream_t st) {
+  if (d == 64)
+    return bf16 ? quant_qk_impl<64, true>(q, k, B, H, H_kv, N, smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st)
+                : quant_qk_impl<64, false>(q, k, B, H, H_kv, N, smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
+  if (d == 128)
+    return bf16 ? quant_qk_impl<128, true>(q, k, B, H, H_kv, N, smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st)
+                : quant_qk_impl<128, false>(q, k, B, H, H_kv, N, smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, int d,
+                               uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st) {
+  if (d == 64)
+    return bf16 ? quant_v_impl<64, true>(v, B, H_kv, N, v_f8, v_scale, ws, st)
+                : quant_v_impl<64, false>(v, B, H_kv, N, v_f8, v_scale, ws, st);
+  if (d == 128)
+    return bf16 ? quant_v_impl<128, true>(v, B, H_kv, N, v_f8, v_scale, ws, st)
+                : quant_v_impl<128, false>(v, B, H_kv, N, v_f8, v_scale, ws, st);
+  return hipErrorInvalidValue;
+}

@@ -1,0 +1,149 @@
+// sage_abi.hip -- the C ABI declared in include/sage.h: host-side argument
+// validation, buffer-size arithmetic and kernel launches.  No entry point
+// makes a HIP call before every argument has been checked, so argument
+// errors are reported identically on machines without a GPU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sage.h"
+
+hipError_t sage_launch_quant_qk(const void* q, const void* k, int bf16, int B, int H, int H_kv,
+                                int N, int d, int smooth_k, int8_t* q_i8, float* q_scale,
+                                int8_t* k_i8, float* k_scale, float* k_mean, void* ws,
+                                hipStream_t st);
+hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, int d,
+                               uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st);
+hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                const float* k_scale, const uint8_t* v_f8, const float* v_scale,
+                                void* o, int bf16_out, int B, int H, int H_kv, int N, int d,
+                                int causal, float sm_scale, hipStream_t stream);
+hipError_t sage_launch_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int H_kv,
+                                int N, int d, int b, int h, int32_t* s_out, hipStream_t stream);
+size_t sage_ws_quant_qk_bytes(int B, int H_kv, int N, int d);
+size_t sage_ws_quant_v_bytes(int B, int H_kv, int N, int d);
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // sanity bound on any tensor
+
+sage_status check_shape(int B, int H, int H_kv, int N, int d) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || N <= 0) return SAGE_ERR_SHAPE;
+  if (d != 64 && d != 128) return SAGE_ERR_HEADDIM;
+  if (H % H_kv != 0) return SAGE_ERR_GQA;
+  // every tensor must be indexable: B*H*N*d (and the padded V) below 2^40;
+  // B*H is a grid y-dimension (at most 65535)
+  const int64_t npad = ((int64_t)N + SAGE_KV_TILE - 1) / SAGE_KV_TILE * SAGE_KV_TILE;
+  if ((int64_t)B * H > 65535 || (int64_t)B * H * npad * d > kMaxElems) return SAGE_ERR_SHAPE;
+  return SAGE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+sage_status from_hip(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int sage_abi_version(void) { return SAGE_ABI_VERSION; }
+
+const char* sage_status_str(sage_status s) {
+  switch (s) {
+    case SAGE_OK: return "ok";
+    case SAGE_ERR_NULL: return "null pointer argument";
+    case SAGE_ERR_SHAPE: return "invalid shape (B, H, H_kv, N must be positive and sizes bounded)";
+    case SAGE_ERR_HEADDIM: return "head dim must be 64 or 128";
+    case SAGE_ERR_GQA: return "H must be a multiple of H_kv";
+    case SAGE_ERR_DTYPE: return "dtype must be SAGE_FP16 or SAGE_BF16";
+    case SAGE_ERR_ARG: return "invalid argument (sm_scale, flag or index)";
+    case SAGE_ERR_WORKSPACE: return "workspace missing or too small";
+    case SAGE_ERR_HIP: return "HIP launch or runtime error";
+    case SAGE_ERR_ALIGN: return "pointer not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, sage_sizes* out) {
+  if (!out) return SAGE_ERR_NULL;
+  const sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  const size_t b = B, h = H, hk = H_kv, n = N, dd = d;
+  const size_t nq = (n + SAGE_BLKQ - 1) / SAGE_BLKQ, nk = (n + SAGE_BLKK - 1) / SAGE_BLKK;
+  const size_t npad = (n + SAGE_KV_TILE - 1) / SAGE_KV_TILE * SAGE_KV_TILE;
+  out->q_i8 = b * h * n * dd;
+  out->q_scale = b * h * nq * sizeof(float);
+  out->k_i8 = b * hk * n * dd;
+  out->k_scale = b * hk * nk * sizeof(float);
+  out->k_mean = b * hk * dd * sizeof(float);
+  out->v_f8 = b * hk * npad * dd;
+  out->v_scale = b * hk * dd * sizeof(float);
+  out->o = b * h * n * dd * 2;
+  out->ws_quant_qk = sage_ws_quant_qk_bytes(B, H_kv, N, d);
+  out->ws_quant_v = sage_ws_quant_v_bytes(B, H_kv, N, d);
+  return SAGE_OK;
+}
+
+sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype, int B, int H, int H_kv,
+                          int N, int d, int smooth_k, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                          float* k_scale, float* k_mean, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean) return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (smooth_k != 0 && smooth_k != 1) return SAGE_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8)) return SAGE_ERR_ALIGN;
+  if (smooth_k) {
+    if (!workspace) return SAGE_ERR_WORKSPACE;
+    if (ws_bytes < sage_ws_quant_qk_bytes(B, H_kv, N, d)) return SAGE_ERR_WORKSPACE;
+  }
+  return from_hip(sage_launch_quant_qk(q, k, dtype == SAGE_BF16, B, H, H_kv, N, d, smooth_k, q_i8,
+                                       q_scale, k_i8, k_scale, k_mean, workspace,
+                                       (hipStream_t)stream));
+}
+
+sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N, int d,
+                         uint8_t* v_f8, float* v_scale, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  if (!v || !v_f8 || !v_scale) return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H_kv, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!aligned16(v) || !aligned16(v_f8)) return SAGE_ERR_ALIGN;
+  if (!workspace) return SAGE_ERR_WORKSPACE;
+  if (ws_bytes < sage_ws_quant_v_bytes(B, H_kv, N, d)) return SAGE_ERR_WORKSPACE;
+  return from_hip(sage_launch_quant_v(v, dtype == SAGE_BF16, B, H_kv, N, d, v_f8, v_scale,
+                                      workspace, (hipStream_t)stream));
+}
+
+sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                          const float* k_scale, const uint8_t* v_f8, const float* v_scale,
+                          void* o, sage_dtype out_dtype, int B, int H, int H_kv, int N, int d,
+                          int causal, float sm_scale, void* stream) {
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8 || !v_scale || !o) return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return SAGE_ERR_ARG;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
+  if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
+    return SAGE_ERR_ALIGN;
+  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, o,
+                                       out_dtype == SAGE_BF16, B, H, H_kv, N, d, causal,
+                                       sm_scale, (hipStream_t)stream));
+}
+
+sage_status sage_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int H_kv, int N,
+                          int d, int b, int h, int32_t* s_out, void* stream) {
+  if (!q_i8 || !k_i8 || !s_out) return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (b < 0 || b >= B || h < 0 || h >= H) return SAGE_ERR_ARG;
+  if ((int64_t)N * N > ((int64_t)1 << 34)) return SAGE_ERR_SHAPE;
+  if (!aligned16(q_i8) || !aligned16(k_i8)) return SAGE_ERR_ALIGN;
+  return from_hip(sage_launch_qk_int32(q_i8, k_i8, B, H, H_kv, N, d, b, h, s_out,
+                                       (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// sage_device.hpp -- device-side building blocks shared by the gfx950 kernels.
+//
+// Matrix-core conventions used throughout (CDNA 32x32 MFMA family):
+//   A operand: lane L supplies row (L % 32) and the K-slice chosen by L / 32;
+//   B operand: lane L supplies column (L % 32) and the same K-slice;
+//   C/D (32x32, 16 values per lane): register r of lane L holds
+//     row = 8*(r/4) + 4*(L/32) + (r%4), column = L % 32.
+// A and B share the K-slice mapping, so a contraction over K is correct for
+// any order of K inside the slices, as long as both operands use one order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBlkQ = 128;     // Q tokens per INT8 scale
+constexpr int kBlkK = 64;      // K tokens per INT8 scale
+constexpr int kKvTile = 128;   // keys per online-softmax step / V tile
+constexpr int kWaveQ = 32;     // queries per wave (one 32-wide MFMA column block)
+constexpr int kWaves = 4;      // waves per workgroup
+constexpr int kBlockQ = kWaveQ * kWaves;   // queries per workgroup (== kBlkQ)
+static_assert(kBlockQ == kBlkQ, "one Q scale per workgroup");
+
+// 1.5 * 2^23: for |n| < 2^22 the float with bits (0x4B400000 + n) equals
+// 12582912 + n exactly.  Seeding the INT8 accumulator with these bits makes
+// the MFMA's int32 sum directly readable as a float offset by kMagic.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
+constexpr float kLog2_448 = 8.8073549220576041f;   // log2(448)
+constexpr float kLog2e = 1.4426950408889634f;
+// Largest per-element score scale (log2 units per unit of the int32 sum) for
+// which the one-FMA exponent argument is used; its error is at most
+// ulp(kMagic * kFastCk) / 2 = 2^-11.
+constexpr float kFastCk = 1.0f / 1024.0f;
+
+// Bit casts through a by-value parameter.  (Applying __builtin_bit_cast
+// directly to an ext_vector element, e.g. bit_cast<float>(v[r]), makes this
+// compiler read element 0 for every r; going through a scalar is correct.)
+__device__ __forceinline__ float as_float(int x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ int as_int(float x) { return __builtin_bit_cast(int, x); }
+
+// Force a matrix-core accumulator to be fully computed at this point.  The
+// MFMA reads its operands from all 64 lanes regardless of the exec mask, so
+// it must never be moved (with the loads feeding it) into a lane-divergent
+// branch; an empty asm that "modifies" the value pins its computation here.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+
+// Key (0..63 inside a 64-key half tile) held by byte s (0..31) of a lane in
+// half g (0/1) of the 32x32x64 FP8 operand: bytes 0..15 come from the C/D
+// registers r = 0..15 of the first 32-key S block, bytes 16..31 from the
+// second block (see the C/D row formula above).
+__host__ __device__ constexpr int fp8_slot_key(int g, int s) {
+  return (s / 16) * 32 + ((s % 16) / 4) * 8 + g * 4 + (s % 4);
+}
+
+// Map a linear workgroup id to a logical work id so that each XCD (ids are
+// dealt round-robin to the 8 XCDs) receives one contiguous range of logical
+// ids.  A bijection on [0, total).
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int q = total / 8, rem = total % 8;
+  const int x = id % 8, j = id / 8;
+  return x * q + min(x, rem) + j;
+}
+
+// ---------------------------------------------------------------------------
+// INT8 S^T tile: 32 keys x 32 queries.  `kfrag` points at the LDS fragment
+// block of this key block (NKC x 1 KB, lane-major 16 bytes per lane);
+// `qf` holds the lane's Q fragments (B operand).  Returns the 16 C/D values
+// as the bit patterns of the floats kMagic + sum_c q*k (exact); as signed
+// ints they order like the sums.
+template <int NKC>
+__device__ __forceinline__ i32x16 qk_block(const char* kfrag, const i32x4* qf, int lane) {
+  i32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = kMagicBits;
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    const i32x4 a = *reinterpret_cast<const i32x4*>(kfrag + kc * 1024 + lane * 16);
+    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[kc], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until this wave's outstanding vector-memory operations (including
+// global->LDS loads) have completed: s_waitcnt vmcnt(0), other counters
+// left alone.  Must precede the barrier that publishes LDS-load data.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// K tile (kKvTile keys x D int8) -> LDS in fragment-major order with
+// direct global->LDS loads (16 bytes per lane; lane L of an instruction
+// lands at byte 16*L of the instruction's 1 KB LDS block).  Block
+// (kb32, kc) holds, for lane L, key kb32*32 + L%32 and channel bytes
+// kc*32 + 16*(L/32) .. +16: exactly the A-operand fragment of the INT8
+// MFMA.  Keys >= N read row N-1 (those scores are masked).
+template <int D>
+__device__ __forceinline__ void load_k_tile(const int8_t* kh, int key0, int N, char* lds_k,
+                                            int wave, int lane) {
+  constexpr int NKC = D / 32;
+  constexpr int NB = (kKvTile / 32) * NKC;
+  static_assert(NB % kWaves == 0, "whole blocks per wave");
+#pragma unroll
+  for (int i = 0; i < NB / kWaves; ++i) {
+    const int blk = i * kWaves + wave;
+    const int kb32 = blk / NKC, kc = blk % NKC;
+    const int key = min(key0 + kb32 * 32 + (lane % 32), N - 1);
+    const int8_t* g = kh + (size_t)key * D + kc * 32 + 16 * (lane / 32);
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_k + blk * 1024), 16, 0, 0);
+  }
+}
+
+// V tile (already fragment-ordered in HBM, kKvTile*D bytes) -> LDS, a
+// straight copy with direct global->LDS loads.
+template <int D>
+__device__ __forceinline__ void load_v_tile(const uint8_t* vtile, char* lds_v, int wave, int lane) {
+  constexpr int NB = kKvTile * D / 1024;
+  static_assert(NB % kWaves == 0, "whole blocks per wave");
+#pragma unroll
+  for (int i = 0; i < NB / kWaves; ++i) {
+    const int blk = i * kWaves + wave;
+    __builtin_amdgcn_global_load_lds(vtile + blk * 1024 + lane * 16,
+                                     (lds_void*)(lds_v + blk * 1024), 16, 0, 0);
+  }
+}
+
+}  // namespace sage

@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, computes buffer sizes, and rejects bad arguments before
+touching the device."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import quantized_attention_amd as qa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+FAKE = 0x10000          # an aligned, never-dereferenced pointer value
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qa.load_library()
+    names = _declared()
+    assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_buffer_sizes",
+            "sage_qk_int32", "sage_status_str", "sage_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.sage_abi_version() == 1
+
+
+def test_status_strings():
+    lib = qa.load_library()
+    for s in range(10):
+        assert lib.sage_status_str(s)
+    assert lib.sage_status_str(0) == b"ok"
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 256, 64), (4, 32, 8, 17550, 128),
+                                          (1, 1, 1, 1, 64), (2, 6, 3, 129, 128)])
+def test_buffer_sizes(B, H, H_kv, N, d):
+    s = qa.sage_buffer_sizes(B, H, H_kv, N, d)
+    assert s["q_i8"] == B * H * N * d
+    assert s["q_scale"] == 4 * B * H * math.ceil(N / 128)
+    assert s["k_i8"] == B * H_kv * N * d
+    assert s["k_scale"] == 4 * B * H_kv * math.ceil(N / 64)
+    assert s["k_mean"] == s["v_scale"] == 4 * B * H_kv * d
+    assert s["v_f8"] == B * H_kv * math.ceil(N / 128) * 128 * d
+    assert s["o"] == 2 * B * H * N * d
+    assert s["ws_quant_qk"] == 8 * B * H_kv * math.ceil(N / 256) * d
+    assert s["ws_quant_v"] == 4 * B * H_kv * math.ceil(N / 256) * d
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 2, 2, 256, 64), 2), ((1, 2, 2, 0, 64), 2), ((1, 0, 1, 256, 64), 2),
+    ((1, 2, 2, 256, 96), 3), ((1, 2, 2, 256, 256), 3), ((1, 6, 4, 256, 64), 4),
+    ((1, 70000, 1, 16, 64), 2), ((64, 512, 512, 1 << 30, 128), 2),
+])
+def test_buffer_sizes_rejects(args, code):
+    with pytest.raises(qa.SageError) as e:
+        qa.sage_buffer_sizes(*args)
+    assert e.value.status == code
+
+
+def _qk(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, dt=0, B=1, H=2, H_kv=2, N=256, d=64, smooth=1, q_i8=FAKE,
+             q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, ws=FAKE, ws_bytes=1 << 20,
+             stream=None)
+    a.update(kw)
+    return lib.sage_quant_qk(*a.values())
+
+
+def _v(lib, **kw):
+    a = dict(v=FAKE, dt=0, B=1, H_kv=2, N=256, d=64, v_f8=FAKE, v_scale=FAKE, ws=FAKE,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.sage_quant_v(*a.values())
+
+
+def _attn(lib, **kw):
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, o=FAKE,
+             dt=0, B=1, H=2, H_kv=2, N=256, d=64, causal=0, sm_scale=0.125, stream=None)
+    a.update(kw)
+    return lib.sage_attn_fwd(*a.values())
+
+
+def _qk32(lib, **kw):
+    a = dict(q_i8=FAKE, k_i8=FAKE, B=1, H=2, H_kv=2, N=256, d=64, b=0, h=0, s=FAKE, stream=None)
+    a.update(kw)
+    return lib.sage_qk_int32(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k_mean=None), 1), (dict(B=0), 2), (dict(N=-5), 2),
+    (dict(d=32), 3), (dict(H=3), 4), (dict(dt=2), 5), (dict(smooth=2), 6),
+    (dict(q=FAKE + 8), 9), (dict(k_i8=FAKE + 4), 9), (dict(ws=None), 7), (dict(ws_bytes=1023), 7),
+])
+def test_quant_qk_rejects(kw, code):
+    assert _qk(qa.load_library(), **kw) == code
+
+
+def test_quant_qk_no_workspace_needed_without_smoothing_is_validated_first():
+    # smooth_k = 0 needs no workspace, but a bad shape still fails first
+    assert _qk(qa.load_library(), smooth=0, ws=None, ws_bytes=0, d=80) == 3
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), 1), (dict(v_scale=None), 1), (dict(N=0), 2), (dict(d=100), 3),
+    (dict(dt=-1), 5), (dict(v_f8=FAKE + 1), 9), (dict(ws=None), 7), (dict(ws_bytes=511), 7),
+])
+def test_quant_v_rejects(kw, code):
+    assert _v(qa.load_library(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), 1), (dict(v_scale=None), 1), (dict(H_kv=0), 2), (dict(d=16), 3),
+    (dict(H=4, H_kv=3), 4), (dict(dt=7), 5), (dict(causal=3), 6), (dict(sm_scale=0.0), 6),
+    (dict(sm_scale=-1.0), 6), (dict(sm_scale=float("inf")), 6), (dict(sm_scale=float("nan")), 6),
+    (dict(o=FAKE + 2), 9),
+])
+def test_attn_fwd_rejects(kw, code):
+    assert _attn(qa.load_library(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(s=None), 1), (dict(b=1), 6), (dict(h=2), 6), (dict(h=-1), 6), (dict(d=48), 3),
+    (dict(N=200000), 2),
+])
+def test_qk_int32_rejects(kw, code):
+    assert _qk32(qa.load_library(), **kw) == code
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        qa.sage_quant_qk(q, q)
+    with pytest.raises(ValueError):
+        qa.sage_quant_v(q)

@@ -1,0 +1,198 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: K mean, INT8 codes and scales of Q and K, V scales and V codes
+(compared by decoded value), int32 QK^T dot products.  Output: max-abs error
+<= 2e-2 and cosine >= 0.9995 against the oracle's quantized attention.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import fp8_e4m3 as F8
+from oracle import sage_oracle as O
+from tests.sage_testlib import compare_output, to_np, v_natural
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _rand_inputs(B, H, H_kv, N, d, dtype, seed, bias=3.0):
+    g = np.random.default_rng(seed)
+    q = torch.from_numpy(g.standard_normal((B, H, N, d), dtype=np.float32)).to(dtype)
+    k = g.standard_normal((B, H_kv, N, d), dtype=np.float32)
+    k += (g.standard_normal((B, H_kv, 1, d), dtype=np.float32) * bias)
+    k = torch.from_numpy(k).to(dtype)
+    v = torch.from_numpy(g.standard_normal((B, H_kv, N, d), dtype=np.float32)).to(dtype)
+    return q, k, v
+
+
+def _check_quant(qa, q, k, v, smooth=True, heads_kv=None):
+    qk = qa.sage_quant_qk(q.to(DEV), k.to(DEV), smooth)
+    vq = qa.sage_quant_v(v.to(DEV))
+    torch.cuda.synchronize()
+    ref = O.quantize_qk(q, k, smooth_k=smooth)
+    refv = O.quantize_v(v)
+    assert np.array_equal(to_np(qk["k_mean"]), ref["k_mean"])
+    assert np.array_equal(to_np(qk["q_scale"]), ref["q_scale"])
+    assert np.array_equal(to_np(qk["k_scale"]), ref["k_scale"])
+    assert np.array_equal(to_np(qk["q_i8"]), ref["q_i8"])
+    assert np.array_equal(to_np(qk["k_i8"]), ref["k_i8"])
+    assert np.array_equal(to_np(vq["v_scale"]), refv["v_scale"])
+    N, d = q.shape[2], q.shape[3]
+    vn, vpad = v_natural(to_np(vq["v_f8"]), N, d)
+    assert (vpad == 0).all(), "V padding must be zero codes"
+    dec_g, dec_r = F8.decode(vn), F8.decode(refv["v_f8"])
+    assert np.array_equal(dec_g, dec_r), np.argwhere(dec_g != dec_r)[:5]
+    return qk, vq, ref, refv
+
+
+def _oracle_o(ref, refv, causal, sm_scale, rows=None, heads=None):
+    return O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
+                        refv["v_f8"], refv["v_scale"], causal=causal, sm_scale=sm_scale,
+                        rows=rows, heads=heads)
+
+
+# ------------------------------------------------------------------ small full parity
+
+SMALL = [
+    # B, H, H_kv, N, d, dtype, causal
+    (1, 2, 2, 256, 64, torch.float16, False),
+    (2, 4, 2, 700, 64, torch.bfloat16, True),
+    (2, 4, 2, 700, 128, torch.float16, False),
+    (1, 4, 1, 385, 128, torch.bfloat16, True),
+    (1, 2, 2, 1, 64, torch.float16, False),
+    (1, 2, 2, 17, 128, torch.float16, True),
+    (1, 2, 1, 130, 64, torch.bfloat16, False),
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", SMALL)
+def test_small_full_parity(gpu_lib, B, H, H_kv, N, d, dtype, causal):
+    print(f"case B{B} H{H}/{H_kv} N{N} d{d} {dtype} causal={causal}", flush=True)
+    q, k, v = _rand_inputs(B, H, H_kv, N, d, dtype, seed=N * 7 + d)
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v)
+    sm = 1 / math.sqrt(d)
+    o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=sm, out_dtype=dtype)
+    torch.cuda.synchronize()
+    compare_output(o, _oracle_o(ref, refv, causal, sm))
+
+
+@pytest.mark.parametrize("N,d", [(256, 64), (300, 128), (129, 64)])
+def test_qk_int32_bit_exact(gpu_lib, N, d):
+    q, k, v = _rand_inputs(1, 4, 2, N, d, torch.float16, seed=N + d)
+    qk = gpu_lib.sage_quant_qk(q.to(DEV), k.to(DEV))
+    ref = O.quantize_qk(q, k)
+    for h in (0, 3):
+        s = to_np(gpu_lib.sage_qk_int32(qk["q_i8"], qk["k_i8"], 0, h))
+        exact = ref["q_i8"][0, h].astype(np.int64) @ ref["k_i8"][0, h // 2].astype(np.int64).T
+        assert np.array_equal(s, exact)
+
+
+def test_smooth_k_off(gpu_lib):
+    q, k, v = _rand_inputs(1, 2, 2, 300, 64, torch.float16, seed=9)
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v, smooth=False)
+    assert (to_np(qk["k_mean"]) == 0).all()
+    o = gpu_lib.sage_attn_fwd(qk, vq, causal=False, sm_scale=0.125, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    compare_output(o, _oracle_o(ref, refv, False, 0.125))
+
+
+def test_degenerate_inputs(gpu_lib):
+    """Zero Q (uniform attention), an all-zero V channel, a zero K block."""
+    q, k, v = _rand_inputs(1, 2, 2, 200, 64, torch.float16, seed=11)
+    q[:, :, :128] = 0                        # first Q block all zero -> scale 0
+    v[:, :, :, 5] = 0                        # zero channel -> V scale 0
+    kbar = k[:, 0].float().mean(dim=1, keepdim=True).to(k.dtype)       # [B, 1, d]
+    k[:, 0, 64:128] = kbar.expand(-1, 64, -1)  # a K block at the mean: tiny after smoothing
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v)
+    for causal in (False, True):
+        o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=0.125, out_dtype=torch.float16)
+        torch.cuda.synchronize()
+        compare_output(o, _oracle_o(ref, refv, causal, 0.125))
+
+
+def test_large_magnitudes(gpu_lib):
+    """Values near the fp16 range still quantize bit-exactly (scales stay finite)."""
+    q, k, v = _rand_inputs(1, 2, 2, 257, 128, torch.float16, seed=12)
+    q = (q.float() * 3000).clamp(-60000, 60000).half()
+    v = (v.float() * 1e-3).half()
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v)
+    o = gpu_lib.sage_attn_fwd(qk, vq, causal=False, sm_scale=1 / 11.3, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    compare_output(o, _oracle_o(ref, refv, False, 1 / 11.3), max_abs=2e-2 * 1e-3 * 4)
+
+
+def test_deterministic(gpu_lib):
+    q, k, v = _rand_inputs(2, 4, 2, 700, 128, torch.bfloat16, seed=13)
+    outs = []
+    for _ in range(3):
+        qk = gpu_lib.sage_quant_qk(q.to(DEV), k.to(DEV))
+        vq = gpu_lib.sage_quant_v(v.to(DEV))
+        outs.append(gpu_lib.sage_attn_fwd(qk, vq, causal=True, sm_scale=0.09,
+                                          out_dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+# ------------------------------------------------------------------ the workloads
+
+def _workload_check(gpu_lib, name, heads, nrows, seed=0):
+    w = W.get(name)
+    print(f"workload {name}: generating", flush=True)
+    t = W.generate(w)
+    plan = gpu_lib.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal)
+    qd, kd, vd = t["q"].to(DEV), t["k"].to(DEV), t["v"].to(DEV)
+    o = plan(qd, kd, vd)
+    torch.cuda.synchronize()
+    print(f"workload {name}: gpu done", flush=True)
+    # bit-exact quantities on the sampled heads (all tokens)
+    hk_set = sorted({(b, h // (w.H // w.H_kv)) for b, h in heads})
+    sub = lambda x, hs: np.stack([x[b, h] for b, h in hs])
+    qsel = torch.stack([t["q"][b, h] for b, h in heads])[None]
+    ksel = torch.stack([t["k"][b, h] for b, h in hk_set])[None]
+    vsel = torch.stack([t["v"][b, h] for b, h in hk_set])[None]
+    ref = O.quantize_qk(qsel, ksel)
+    refv = O.quantize_v(vsel)
+    assert np.array_equal(sub(to_np(plan.qk["k_mean"]), hk_set), ref["k_mean"][0])
+    assert np.array_equal(sub(to_np(plan.qk["q_i8"]), heads), ref["q_i8"][0])
+    assert np.array_equal(sub(to_np(plan.qk["q_scale"]), heads), ref["q_scale"][0])
+    assert np.array_equal(sub(to_np(plan.qk["k_i8"]), hk_set), ref["k_i8"][0])
+    assert np.array_equal(sub(to_np(plan.qk["k_scale"]), hk_set), ref["k_scale"][0])
+    assert np.array_equal(sub(to_np(plan.vq["v_scale"]), hk_set), refv["v_scale"][0])
+    vn, _ = v_natural(sub(to_np(plan.vq["v_f8"]), hk_set)[None], w.N, w.d)
+    assert np.array_equal(F8.decode(vn), F8.decode(refv["v_f8"]))
+    # output on sampled rows (ragged tail and, if causal, the first rows included)
+    g = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([g.choice(w.N, size=min(nrows, w.N), replace=False),
+                                     [0, 1, w.N - 1]]))
+    # re-index the selected heads as a small (1, len(heads)) problem with its own GQA map
+    qsel_i8 = ref["q_i8"]
+    kv_index = [hk_set.index((b, h // (w.H // w.H_kv))) for b, h in heads]
+    o_ref = np.zeros((len(heads), len(rows), w.d))
+    for j, (b, h) in enumerate(heads):
+        kvj = kv_index[j]
+        o1 = O.attn_quant(qsel_i8[:, j:j + 1], ref["q_scale"][:, j:j + 1],
+                          ref["k_i8"][:, kvj:kvj + 1], ref["k_scale"][:, kvj:kvj + 1],
+                          refv["v_f8"][:, kvj:kvj + 1], refv["v_scale"][:, kvj:kvj + 1],
+                          causal=w.causal, sm_scale=w.sm_scale, rows=rows)
+        o_ref[j] = o1[0, 0]
+    o_gpu = torch.stack([o[b, h, torch.from_numpy(rows).to(DEV)] for b, h in heads])
+    m = compare_output(o_gpu, o_ref)
+    print(f"workload {name}: {m}", flush=True)
+
+
+@pytest.mark.parametrize("name,heads,nrows", [
+    ("tiny", [(0, 0), (0, 1)], 256),
+    ("llm_prefill", [(0, 0), (0, 17), (0, 31)], 192),
+    ("video_dit", [(0, 0), (0, 47)], 128),
+    ("sweep@N1024", [(0, 0), (3, 31)], 192),
+    ("sweep@N4096", [(1, 7)], 128),
+    ("sweep@N32768", [(3, 30)], 64),
+    ("gqa_long", [(0, 0), (0, 3), (0, 29)], 48),
+])
+def test_workload_parity(gpu_lib, name, heads, nrows):
+    _workload_check(gpu_lib, name, heads, nrows)
