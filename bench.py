@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized attention forward pass on one MI355X.
+
+One step = the whole hot path on one batch already resident in HBM:
+sage_quant_qk (smooth K + INT8 Q/K), sage_quant_v (FP8 V) and sage_attn_fwd.
+Default workload: the sequence-sweep configuration at N = 32768
+(B=4, H=32, d=128, fp16, non-causal), the one the headline TOPS is quoted on.
+
+Prints ONE JSON line.  ``value`` is whole-step TOPS, 4*B*H*N^2*d / t_step
+(halved when causal); ``attn_tops`` is the attention kernel alone (the pages'
+convention: quantization time excluded).  ``roofline`` is the attention
+kernel's algorithmic TOPS against the dense INT8/FP8 MFMA peak, with the
+kernel time measured by HIP events on the launch stream.  ``cpu_baseline``
+times the float64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TOPS = 5000.0          # MI355X dense INT8 (POPS) / FP8 (PFLOPS) peak, in T/s
+HBM_GBS = 8000.0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_fwd.hip", "sage_device.hpp"):
+        with open(os.path.join(ROOT, "quantized_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per attn_fwd launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_fwd_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"kernel_source_hash:\s*(\w+)", txt)
+    w = re.search(r"workload:\s*(\S+)", txt)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m and t and w) or m.group(1) != kernel_source_hash() or w.group(1) != workload:
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(w, budget_s: float = 15.0) -> dict:
+    """Time the oracle on one (b, head) slice: its quantization plus the
+    quantized attention of a block of query rows against all N keys."""
+    import numpy as np
+    import workloads as W
+    from oracle import sage_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    t = W.generate(w, heads=[(0, 0)])
+    q, k, v = t["q"][:, :1], t["k"][:, :1], t["v"][:, :1]
+    t0 = time.perf_counter()
+    qz = O.quantize_qk(q, k)
+    vz = O.quantize_v(v)
+    t_quant = time.perf_counter() - t0
+    rows_done, t_attn, r0 = 0, 0.0, 0
+    blk = 256
+    while t_attn < budget_s and r0 < w.N:
+        rows = np.arange(r0, min(r0 + blk, w.N))
+        t1 = time.perf_counter()
+        O.attn_quant(qz["q_i8"], qz["q_scale"], qz["k_i8"], qz["k_scale"], vz["v_f8"],
+                     vz["v_scale"], causal=w.causal, sm_scale=w.sm_scale, rows=rows)
+        t_attn += time.perf_counter() - t1
+        rows_done += len(rows)
+        r0 += blk
+    # per-head time: quantization + attention scaled from the sampled rows
+    # (causal rows differ in cost; the sample starts at row 0, so for causal
+    # workloads this under-counts and is marked as such)
+    t_head = t_quant + t_attn * (w.N / rows_done)
+    ops_head = w.ops() / (w.B * w.H)
+    return {"value": ops_head / t_head / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": f"1 of {w.B * w.H} heads: quantize Q/K/V of the head ({t_quant:.2f} s) + "
+                      f"quantized attention of {rows_done} of {w.N} query rows x {w.N} keys "
+                      f"({t_attn:.2f} s), scaled to the head"
+                      + (" (causal: rows from 0, cost under-counted)" if w.causal else "")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="sweep@N32768",
+                    help="workload name: tiny, llm_prefill, video_dit, sweep@N<n>, gqa_long")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
+                    help="only run a plain device-to-device copy of this many MiB (3 times), "
+                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+
+    if args.calib_copy:
+        import torch
+        n = args.calib_copy << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n}))
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_attention_amd as qa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    qa.load_library()
+    w = W.get(args.config)
+    dev = torch.device("cuda:0")
+    t = W.generate(w)
+    q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
+    del t
+    plan = qa.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        plan(q, k, v)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record(stream)
+        qa.sage_quant_qk(q, k, True, out=plan.qk, workspace=plan.ws_qk)
+        e[1].record(stream)
+        qa.sage_quant_v(v, out=plan.vq, workspace=plan.ws_v)
+        e[2].record(stream)
+        plan.attn()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_qk = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    t_v = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    t_attn = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    ops = w.ops()
+    attn_tops = ops / (t_attn * 1e-3) / 1e12
+    # algorithmic bytes of the quantizers: read 2 B + write 1 B per element of Q, K and V
+    quant_bytes = 3 * (w.B * w.H * w.N * w.d + 2 * w.B * w.H_kv * w.N * w.d)
+    traffic = traffic_from_profile(w.name)
+
+    res = {
+        "metric": "quantized attn fwd TOPS at N=32K hd128 (4BHN^2d/t); % of MFMA INT8/FP8 peak",
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8(QK^T)+f8e4m3(PV), f32 accumulate",
+        "data": "synthetic (seeded normals, shared K channel bias)",
+        "config": {"workload": w.description, "name": w.name, "B": w.B, "H": w.H,
+                   "H_kv": w.H_kv, "N": w.N, "d": w.d, "causal": w.causal,
+                   "in_dtype": w.dtype},
+        "attn_tops": round(attn_tops, 2),
+        "attn_ms": round(t_attn, 4),
+        "quant_qk_ms": round(t_qk, 4),
+        "quant_v_ms": round(t_v, 4),
+        "quant_gbs": round(quant_bytes / ((t_qk + t_v) * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel",
+            "achieved": round(attn_tops, 2),
+            "peak": PEAK_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tops / PEAK_TOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
