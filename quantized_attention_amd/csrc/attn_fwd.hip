@@ -98,9 +98,23 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
     const char* vt = lds[t & 1] + KBYTES;
 
     // ---- S^T = K Q^T on the INT8 matrix cores (exact int32 sums).
+    // K fragments are read one 32-key block ahead of the MFMAs that use
+    // them, so the LDS latency hides behind the previous block's MFMAs.
     i32x16 s[4];
+    i32x4 kf[NKC];
+    read_k_frags<NKC>(kt, lane, kf);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb] = qk_block<NKC>(kt + kb * NKC * 1024, qf, lane);
+    for (int kb = 0; kb < 4; ++kb) {
+      i32x4 kn[NKC];
+      if (kb + 1 < 4) read_k_frags<NKC>(kt + (kb + 1) * NKC * 1024, lane, kn);
+      __builtin_amdgcn_sched_barrier(0);
+      s[kb] = qk_frags<NKC>(kf, qf);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + 1 < 4) {
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) kf[kc] = kn[kc];
+      }
+    }
 
     // Per 32-key block: combined dequant factor (log2 domain).
     float ck[4];
@@ -152,6 +166,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
     const float mq = m_new - kLog2_448;
     const bool fast = fmaxf(fmaxf(ck[0], ck[1]), fmaxf(ck[2], ck[3])) <= kFastCk;
     i32x8 pf[2];
+    // The first two V fragments are read before the exponentials, the rest
+    // two MFMAs ahead, so no FP8 MFMA waits on LDS.
+    auto vfrag = [&](int idx) __attribute__((always_inline)) {
+      const char* vp = vt + (idx * 2) * 1024 + lane * 16;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(vp);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(vp + 1024);
+      return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    i32x8 va = vfrag(0), vb = vfrag(1);
+    __builtin_amdgcn_sched_barrier(0);
     auto exp_block = [&](auto fast_tag) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -178,17 +202,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
     else exp_block(std::false_type{});
 
     // ---- O^T += V^T P^T on the FP8 matrix cores (FP32 accumulation).
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < NKC; ++c) {
-        const char* vp = vt + ((kb * NKC + c) * 2) * 1024 + lane * 16;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(vp);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(vp + 1024);
-        const i32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf[kb], acc_o[c], 0, 0,
-                                                                     0, 127, 0, 127);
-      }
+    for (int idx = 0; idx < 2 * NKC; ++idx) {
+      const int kb = idx / NKC, c = idx % NKC;
+      const i32x8 vn = (idx + 2 < 2 * NKC) ? vfrag(idx + 2) : i32x8{};
+      __builtin_amdgcn_sched_barrier(0);
+      acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[kb], acc_o[c], 0, 0, 0,
+                                                                   127, 0, 127);
+      __builtin_amdgcn_sched_barrier(0);
+      va = vb;
+      vb = vn;
+    }
   };
 
   const bool last_masked = CAUSAL || (N % kKvTile) != 0;
@@ -230,7 +255,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
 }
 
 // Diagnostic: exact int32 S = Q^ K^T of one head, through the same K tile
-// loader, LDS fragment layout and qk_block routine as attn_fwd_kernel.
+// loader, LDS fragment layout and qk_frags routine as attn_fwd_kernel.
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
     const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8, int32_t* __restrict__ s_out,
@@ -255,7 +280,9 @@ __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
                       : i32x4{0, 0, 0, 0};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    i32x16 s = qk_block<NKC>(lds + kb * NKC * 1024, qf, lane);
+    i32x4 kf[NKC];
+    read_k_frags<NKC>(lds + kb * NKC * 1024, lane, kf);
+    i32x16 s = qk_frags<NKC>(kf, qf);
     pin(s);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {

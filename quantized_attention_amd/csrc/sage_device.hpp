@@ -70,22 +70,26 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 }
 
 // ---------------------------------------------------------------------------
-// INT8 S^T tile: 32 keys x 32 queries.  `kfrag` points at the LDS fragment
-// block of this key block (NKC x 1 KB, lane-major 16 bytes per lane);
-// `qf` holds the lane's Q fragments (B operand).  Returns the 16 C/D values
-// as the bit patterns of the floats kMagic + sum_c q*k (exact); as signed
-// ints they order like the sums.
+// INT8 S^T tile: 32 keys x 32 queries from the lane's K fragments `kf` (A
+// operand, one per 32-channel chunk) and Q fragments `qf` (B operand).
+// Returns the 16 C/D values as the bit patterns of the floats
+// kMagic + sum_c q*k (exact); as signed ints they order like the sums.
 template <int NKC>
-__device__ __forceinline__ i32x16 qk_block(const char* kfrag, const i32x4* qf, int lane) {
+__device__ __forceinline__ i32x16 qk_frags(const i32x4* kf, const i32x4* qf) {
   i32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = kMagicBits;
 #pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) {
-    const i32x4 a = *reinterpret_cast<const i32x4*>(kfrag + kc * 1024 + lane * 16);
-    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[kc], acc, 0, 0, 0);
-  }
+  for (int kc = 0; kc < NKC; ++kc) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kc], qf[kc], acc, 0, 0, 0);
   return acc;
+}
+
+// The lane's K fragments of one 32-key block: `kfrag` points at the block's
+// LDS fragments (NKC x 1 KB, lane-major 16 bytes per lane).
+template <int NKC>
+__device__ __forceinline__ void read_k_frags(const char* kfrag, int lane, i32x4* kf) {
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) kf[kc] = *reinterpret_cast<const i32x4*>(kfrag + kc * 1024 + lane * 16);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
