@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sage_device.hpp"
 
 namespace sage {
@@ -40,6 +42,19 @@ __device__ __forceinline__ void unpack8(const uint4 u, float* x) {
     }
   }
 }
+
+// The binary32 quotient v / s rounded to nearest, from y = RN(1/s): q0 = RN(v*y)
+// is within one ulp of v/s, so the residual v - s*q0 is exact in one FMA and
+// q0 + r*y (one more FMA) is the correctly rounded quotient (Markstein's
+// theorem; s normal, quotient without overflow).  Three VALU operations
+// instead of the full division sequence, bit-identical to x / s.
+__device__ __forceinline__ float div_rn(float v, float s, float y) {
+  const float q0 = v * y;
+  const float r = fmaf(-s, q0, v);
+  return fmaf(r, y, q0);
+}
+// Scales below this use true division (1/s would overflow or lose range).
+constexpr float kDivRnMinScale = 1e-30f;
 
 // ---------------------------------------------------------------------------
 // Per-channel statistics over a chunk of kStatChunk tokens.
@@ -90,22 +105,44 @@ __global__ __launch_bounds__(kQuantThreads) void colstats_partial(const void* __
 
 // MODE 0: out[bh][c] = float32(sum / N) (the K mean), or 0 when !enable.
 // MODE 1: out[bh][c] = float32(amax / 448) (the V scale).
+// kQuantThreads threads per (b, kv head): thread (r, c) combines chunks
+// r, r + R, ... of channel c in order, then the R partials are combined in
+// order (a fixed order, so the result is deterministic).
 template <int D, int MODE>
-__global__ __launch_bounds__(D) void colstats_final(const void* __restrict__ ws,
-                                                    float* __restrict__ out, int N, int nchunk,
-                                                    int enable) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+__global__ __launch_bounds__(kQuantThreads) void colstats_final(const void* __restrict__ ws,
+                                                                float* __restrict__ out, int N,
+                                                                int nchunk, int enable) {
+  constexpr int R = kQuantThreads / D;
+  const int bh = blockIdx.x, c = threadIdx.x % D, r = threadIdx.x / D;
+  __shared__ double red[R][D];
   if (MODE == 0) {
+    const double* w = reinterpret_cast<const double*>(ws) + (size_t)bh * nchunk * D + c;
     double s = 0.0;
-    if (enable)
-      for (int k = 0; k < nchunk; ++k)
-        s += reinterpret_cast<const double*>(ws)[((size_t)bh * nchunk + k) * D + c];
-    out[(size_t)bh * D + c] = enable ? (float)(s / (double)N) : 0.f;
+    if (enable) {
+#pragma unroll 8
+      for (int k = r; k < nchunk; k += R) s += w[(size_t)k * D];
+    }
+    red[r][c] = s;
   } else {
+    const float* w = reinterpret_cast<const float*>(ws) + (size_t)bh * nchunk * D + c;
     float m = 0.f;
-    for (int k = 0; k < nchunk; ++k)
-      m = fmaxf(m, reinterpret_cast<const float*>(ws)[((size_t)bh * nchunk + k) * D + c]);
-    out[(size_t)bh * D + c] = m / 448.0f;
+#pragma unroll 8
+    for (int k = r; k < nchunk; k += R) m = fmaxf(m, w[(size_t)k * D]);
+    red[r][c] = m;
+  }
+  __syncthreads();
+  if (r == 0) {
+    if (MODE == 0) {
+      double s = red[0][c];
+#pragma unroll
+      for (int i = 1; i < R; ++i) s += red[i][c];
+      out[(size_t)bh * D + c] = enable ? (float)(s / (double)N) : 0.f;
+    } else {
+      float m = (float)red[0][c];
+#pragma unroll
+      for (int i = 1; i < R; ++i) m = fmaxf(m, (float)red[i][c]);
+      out[(size_t)bh * D + c] = m / 448.0f;
+    }
   }
 }
 
@@ -164,77 +201,94 @@ __global__ __launch_bounds__(kQuantThreads) void quant_int8(const void* __restri
   amax = block_max(amax, red);
   const float sc = amax / 127.0f;            // IEEE division
   if (tid == 0) scales[(size_t)bh * nblk + blk] = sc;
+  auto emit = [&](auto fast_tag) __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    const float rs = FAST ? 1.0f / sc : 0.f;
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int row = blk * BLK + (p * kQuantThreads + tid) / TPR;
-    if (row >= N) continue;
-    uint32_t w[2] = {0u, 0u};
+    for (int p = 0; p < PER; ++p) {
+      const int row = blk * BLK + (p * kQuantThreads + tid) / TPR;
+      if (row >= N) continue;
+      uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float q = 0.f;
-      if (sc > 0.f) q = fminf(fmaxf(__builtin_rintf(v[p][i] / sc), -127.f), 127.f);
-      w[i / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (i % 4));
+      for (int i = 0; i < 8; ++i) {
+        float q = 0.f;
+        if (FAST || sc > 0.f) {   // the fast path implies sc > 0
+          const float x = FAST ? div_rn(v[p][i], sc, rs) : v[p][i] / sc;
+          q = fminf(fmaxf(__builtin_rintf(x), -127.f), 127.f);
+        }
+        w[i / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (i % 4));
+      }
+      *reinterpret_cast<uint2*>(cs + (size_t)row * D + cg * 8) = uint2{w[0], w[1]};
     }
-    *reinterpret_cast<uint2*>(cs + (size_t)row * D + cg * 8) = uint2{w[0], w[1]};
-  }
+  };
+  // sc is the same for every thread of the block: branch on the scalar unit.
+  if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc >= kDivRnMinScale ? 1.f : 0.f)))
+    emit(std::true_type{});
+  else
+    emit(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
-// FP8 V: one workgroup per 128-key tile of one (b, kv head).
+// FP8 V.  Each 16-byte chunk of the v_f8 layout (sage.h) holds one channel
+// and 16 keys, so one wave writes the 64 chunks (kb, cb, p, L = lane) of a
+// (128-key tile, 32-channel block) pair for kb, p in {0, 1}: lane L gathers
+// its channel cb*32 + L%32 for the 64 keys of its lane half straight from
+// HBM (for each key, 32 lanes read 64 contiguous bytes) and stores whole
+// 16-byte chunks, consecutive across the wave.  No LDS staging.
+// grid (ceil(ntile * D/32 / 4), B*Hkv), 4 waves per workgroup.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kQuantThreads) void quant_v_fp8(const void* __restrict__ x,
                                                              const float* __restrict__ vscale,
                                                              uint8_t* __restrict__ out, int N,
                                                              int ntile) {
-  constexpr int TPR = D / 8;
-  constexpr int PER = kKvTile * TPR / kQuantThreads;
-  const int tile = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int cg = tid % TPR;
-  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
-  __shared__ __attribute__((aligned(16))) uint8_t st[D][kKvTile];   // [channel][key]
-
-  float sv[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sv[i] = vscale[(size_t)bh * D + cg * 8 + i];
-
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int key = (p * kQuantThreads + tid) / TPR;
-    const int n = tile * kKvTile + key;
-    float v[8];
-    if (n < N) {
-      const uint4 u = *reinterpret_cast<const uint4*>(xs + (size_t)n * D + cg * 8);
-      unpack8<BF16>(u, v);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      float y0 = 0.f, y1 = 0.f;
-      if (n < N) {
-        if (sv[i] > 0.f) y0 = fminf(fmaxf(v[i] / sv[i], -448.f), 448.f);
-        if (sv[i + 1] > 0.f) y1 = fminf(fmaxf(v[i + 1] / sv[i + 1], -448.f), 448.f);
-      }
-      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-      st[cg * 8 + i][key] = (uint8_t)(pk & 0xFF);
-      st[cg * 8 + i + 1][key] = (uint8_t)((pk >> 8) & 0xFF);
-    }
-  }
-  __syncthreads();
-  // Emit 16-byte chunks in the fragment layout: chunk c = ((kb*(D/32)+cb)*2+p)*64 + L.
-  constexpr int NCH = kKvTile * D / 16;
+  constexpr int NCB = D / 32;
+  const int bh = blockIdx.y, lane = threadIdx.x % 64;
+  const int pair = blockIdx.x * (kQuantThreads / 64) + threadIdx.x / 64;
+  if (pair >= ntile * NCB) return;
+  const int tile = pair / NCB, cb = pair % NCB;
+  const int chan = cb * 32 + (lane % 32), g = lane / 32;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D + chan;
+  const float sv = vscale[(size_t)bh * D + chan];
   uint8_t* ot = out + ((size_t)bh * ntile + tile) * kKvTile * D;
+  auto emit = [&](auto fast_tag, auto full_tag) __attribute__((always_inline)) {
+  constexpr bool FAST = decltype(fast_tag)::value;
+  constexpr bool FULL = decltype(full_tag)::value;   // every key of the tile is < N
+  const float rv = FAST ? 1.0f / sv : 0.f;
 #pragma unroll
-  for (int it = 0; it < NCH / kQuantThreads; ++it) {
-    const int c = it * kQuantThreads + tid;
-    const int L = c % 64, p = (c / 64) % 2, cb = (c / 128) % (D / 32), kb = c / (128 * (D / 32));
-    const int chan = cb * 32 + (L % 32), g = L / 32;
-    uint32_t w[4];
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // bytes 4q..4q+3 of the chunk: slot s = p*16 + 4q + j, keys are 4 consecutive
-      const int key = kb * 64 + fp8_slot_key(g, p * 16 + 4 * q);
-      w[q] = *reinterpret_cast<const uint32_t*>(&st[chan][key]);
+    for (int p = 0; p < 2; ++p) {
+      // byte i of the chunk: key = kb*64 + fp8_slot_key(g, p*16 + i)
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int n = tile * kKvTile + kb * 64 + fp8_slot_key(g, p * 16 + i);
+        float v = 0.f;
+        if (FULL || n < N) {
+          const uint16_t h = xs[(size_t)n * D];
+          v = BF16 ? as_float((int)((uint32_t)h << 16)) : (float)__builtin_bit_cast(_Float16, h);
+        }
+        const float x = FAST ? div_rn(v, sv, rv) : v / sv;
+        y[i] = (sv > 0.f) ? fminf(fmaxf(x, -448.f), 448.f) : 0.f;
+      }
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * q], y[4 * q + 1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * q + 2], y[4 * q + 3], pk, true);
+        w[q] = (uint32_t)pk;
+      }
+      const int chunk = ((kb * NCB + cb) * 2 + p) * 64 + lane;
+      *reinterpret_cast<uint4*>(ot + (size_t)chunk * 16) = uint4{w[0], w[1], w[2], w[3]};
     }
-    *reinterpret_cast<uint4*>(ot + (size_t)c * 16) = uint4{w[0], w[1], w[2], w[3]};
+  };
+  const bool fast = sv >= kDivRnMinScale || sv <= 0.f;   // sv <= 0: codes 0 either way
+  if ((tile + 1) * kKvTile <= N) {
+    if (fast) emit(std::true_type{}, std::true_type{});
+    else emit(std::false_type{}, std::true_type{});
+  } else {
+    if (fast) emit(std::true_type{}, std::false_type{});
+    else emit(std::false_type{}, std::false_type{});
   }
 }
 
@@ -265,8 +319,8 @@ static hipError_t quant_qk_impl(const void* q, const void* k, int B, int H, int 
     hipLaunchKernelGGL((colstats_partial<D, BF16, 0>), dim3(nc, B * H_kv), dim3(kQuantThreads), 0,
                        st, k, ws, N, nc);
   }
-  hipLaunchKernelGGL((colstats_final<D, 0>), dim3(B * H_kv), dim3(D), 0, st, ws, k_mean, N, nc,
-                     smooth_k);
+  hipLaunchKernelGGL((colstats_final<D, 0>), dim3(B * H_kv), dim3(kQuantThreads), 0, st, ws, k_mean,
+                     N, nc, smooth_k);
   hipLaunchKernelGGL((quant_int8<D, kBlkQ, BF16, false>), dim3(nbq, B * H), dim3(kQuantThreads), 0,
                      st, q, nullptr, q_i8, q_scale, N, nbq);
   if (smooth_k)
@@ -286,9 +340,11 @@ static hipError_t quant_v_impl(const void* v, int B, int H_kv, int N, uint8_t* v
   const int nt = (N + kKvTile - 1) / kKvTile;
   hipLaunchKernelGGL((colstats_partial<D, BF16, 1>), dim3(nc, B * H_kv), dim3(kQuantThreads), 0, st,
                      v, ws, N, nc);
-  hipLaunchKernelGGL((colstats_final<D, 1>), dim3(B * H_kv), dim3(D), 0, st, ws, v_scale, N, nc, 1);
-  hipLaunchKernelGGL((quant_v_fp8<D, BF16>), dim3(nt, B * H_kv), dim3(kQuantThreads), 0, st, v,
-                     v_scale, v_f8, N, nt);
+  hipLaunchKernelGGL((colstats_final<D, 1>), dim3(B * H_kv), dim3(kQuantThreads), 0, st, ws, v_scale,
+                     N, nc, 1);
+  const int pairs = nt * (D / 32), wpg = kQuantThreads / 64;
+  hipLaunchKernelGGL((quant_v_fp8<D, BF16>), dim3((pairs + wpg - 1) / wpg, B * H_kv),
+                     dim3(kQuantThreads), 0, st, v, v_scale, v_f8, N, nt);
   return hipGetLastError();
 }
 
