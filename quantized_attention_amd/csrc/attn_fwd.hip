@@ -79,6 +79,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
   float m_run = -INFINITY;   // running max of the log2-domain scores
   float l_part = 0.f;        // this lane's share of sum 448*P~
 
+  // this lane's byte offset inside a 32-key K fragment block (full tiles)
+  const uint32_t koff = (uint32_t)((lane % 32) * D + 16 * (lane / 32));
   load_k_tile<D>(kh, 0, N, lds[0], wave, lane);
   load_v_tile<D>(vh, lds[0] + KBYTES, wave, lane);
 
@@ -91,7 +93,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
     wait_vmem();
     __syncthreads();
     if (t + 1 < ntiles) {
-      load_k_tile<D>(kh, (t + 1) * kKvTile, N, lds[(t + 1) & 1], wave, lane);
+      if ((t + 2) * kKvTile <= N) load_k_tile_full<D>(kh, (t + 1) * kKvTile, koff, lds[(t + 1) & 1], wave);
+      else load_k_tile<D>(kh, (t + 1) * kKvTile, N, lds[(t + 1) & 1], wave, lane);
       load_v_tile<D>(vh + (size_t)(t + 1) * KBYTES, lds[(t + 1) & 1] + KBYTES, wave, lane);
     }
     const char* kt = lds[t & 1];
@@ -192,7 +195,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
         }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
+          // the high half is written by the second convert: any old value
+          // does, and e's own register avoids zeroing one first
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], as_int(e[4 * w]), false);
           pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], pk, true);
           pf[kb / 2][(kb % 2) * 4 + w] = pk;
         }

@@ -121,17 +121,36 @@ __device__ __forceinline__ void load_k_tile(const int8_t* kh, int key0, int N, c
   }
 }
 
+// The same K tile when every key is < N: each lane's address is a
+// wave-uniform base plus its fixed 32-bit offset `koff` = (L%32)*D + 16*(L/32)
+// (SGPR-base addressing, no per-load vector arithmetic).
+template <int D>
+__device__ __forceinline__ void load_k_tile_full(const int8_t* kh, int key0, uint32_t koff,
+                                                 char* lds_k, int wave) {
+  constexpr int NKC = D / 32;
+  constexpr int NB = (kKvTile / 32) * NKC;
+  static_assert(NB % kWaves == 0, "whole blocks per wave");
+#pragma unroll
+  for (int i = 0; i < NB / kWaves; ++i) {
+    const int blk = i * kWaves + wave;
+    const int kb32 = blk / NKC, kc = blk % NKC;
+    const int8_t* base = kh + (size_t)(key0 + kb32 * 32) * D + kc * 32;
+    __builtin_amdgcn_global_load_lds(base + koff, (lds_void*)(lds_k + blk * 1024), 16, 0, 0);
+  }
+}
+
 // V tile (already fragment-ordered in HBM, kKvTile*D bytes) -> LDS, a
 // straight copy with direct global->LDS loads.
 template <int D>
 __device__ __forceinline__ void load_v_tile(const uint8_t* vtile, char* lds_v, int wave, int lane) {
   constexpr int NB = kKvTile * D / 1024;
   static_assert(NB % kWaves == 0, "whole blocks per wave");
+  const uint32_t voff = (uint32_t)lane * 16;
 #pragma unroll
   for (int i = 0; i < NB / kWaves; ++i) {
     const int blk = i * kWaves + wave;
-    __builtin_amdgcn_global_load_lds(vtile + blk * 1024 + lane * 16,
-                                     (lds_void*)(lds_v + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vtile + blk * 1024 + voff, (lds_void*)(lds_v + blk * 1024),
+                                     16, 0, 0);
   }
 }
 
