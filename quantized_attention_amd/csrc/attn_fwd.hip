@@ -143,13 +143,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
     float xm = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      int fm = s[kb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) fm = max(fm, s[kb][r]);
+      // a depth-3 tree of max3 (short dependency chain)
+      const i32x16& v = s[kb];
+      const int m0 = max(max(v[0], v[1]), v[2]), m1 = max(max(v[3], v[4]), v[5]);
+      const int m2 = max(max(v[6], v[7]), v[8]), m3 = max(max(v[9], v[10]), v[11]);
+      const int m4 = max(max(v[12], v[13]), v[14]);
+      const int fm = max(max(max(m0, m1), m2), max(max(m3, m4), v[15]));
       const float x = (as_float(fm) - kMagic) * ck[kb];
       xm = MASK ? (fm != INT_MIN ? fmaxf(xm, x) : xm) : fmaxf(xm, x);
     }
-    xm = fmaxf(xm, __shfl_xor(xm, 32));
+    xm = max_xor32(xm);
     const float m_new = fmaxf(m_run, xm);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;

@@ -60,6 +60,18 @@ __host__ __device__ constexpr int fp8_slot_key(int g, int s) {
   return (s / 16) * 32 + ((s % 16) / 4) * 8 + g * 4 + (s % 4);
 }
 
+// max(x, x from lane L ^ 32) in every lane, on the VALU (v_permlane32_swap
+// exchanges the lane halves of two registers) instead of an LDS permute.
+// swap(x, y) returns {[x_lo, y_lo], [x_hi, y_hi]}; with y a copy of x the
+// max of the two is the cross-half max.  The copy goes through an empty asm
+// so the two operands are distinct values to the optimizer.
+__device__ __forceinline__ float max_xor32(float x) {
+  int a = __builtin_bit_cast(int, x), b = a;
+  asm volatile("" : "+v"(b));
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+
 // Map a linear workgroup id to a logical work id so that each XCD (ids are
 // dealt round-robin to the 8 XCDs) receives one contiguous range of logical
 // ids.  A bijection on [0, total).
