@@ -194,8 +194,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
                               : fmaf(as_float(s[kb][r]) - kMagic, ck[kb], -mq);
           e[r] = __builtin_amdgcn_exp2f(a);
           if constexpr (MASK) e[r] = (s[kb][r] == INT_MIN) ? 0.f : e[r];
-          l_part += e[r];
         }
+        // the block's share of l as a depth-4 tree (not a 16-long chain)
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = e[2 * j] + e[2 * j + 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+        l_part += (t[0] + t[1]) + (t[2] + t[3]);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           // the high half is written by the second convert: any old value
