@@ -182,51 +182,90 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
     };
     i32x8 va = vfrag(0), vb = vfrag(1);
     __builtin_amdgcn_sched_barrier(0);
-    auto exp_block = [&](auto fast_tag) {
+    // P~ of elements r0 .. r0+NE-1 of 32-key block kb into its FP8 slots.
+    auto exp_part = [&](int kb, int r0, auto ne_tag, auto fast_tag) __attribute__((always_inline)) {
+      constexpr int NE = decltype(ne_tag)::value;
+      const float off = fmaf(kMagic, ck[kb], mq);
+      float e[NE];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float off = fmaf(kMagic, ck[kb], mq);
-        float e[16];
+      for (int j = 0; j < NE; ++j) {
+        const int r = r0 + j;
+        const float a = decltype(fast_tag)::value
+                            ? fmaf(as_float(s[kb][r]), ck[kb], -off)
+                            : fmaf(as_float(s[kb][r]) - kMagic, ck[kb], -mq);
+        e[j] = __builtin_amdgcn_exp2f(a);
+        if constexpr (MASK) e[j] = (s[kb][r] == INT_MIN) ? 0.f : e[j];
+      }
+      // this part's share of l as a tree (not a chain)
+      float t[NE / 2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float a = decltype(fast_tag)::value
-                              ? fmaf(as_float(s[kb][r]), ck[kb], -off)
-                              : fmaf(as_float(s[kb][r]) - kMagic, ck[kb], -mq);
-          e[r] = __builtin_amdgcn_exp2f(a);
-          if constexpr (MASK) e[r] = (s[kb][r] == INT_MIN) ? 0.f : e[r];
+      for (int j = 0; j < NE / 2; ++j) t[j] = e[2 * j] + e[2 * j + 1];
+#pragma unroll
+      for (int w = NE / 4; w >= 1; w /= 2)
+#pragma unroll
+        for (int j = 0; j < w; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+      l_part += t[0];
+#pragma unroll
+      for (int w = 0; w < NE / 4; ++w) {
+        // the high half is written by the second convert: any old value
+        // does, and e's own register avoids zeroing one first
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], as_int(e[4 * w]), false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], pk, true);
+        pf[kb / 2][(kb % 2) * 4 + r0 / 4 + w] = pk;
+      }
+    };
+    // ---- P, then O^T += V^T P^T on the FP8 matrix cores.  With d = 64 the
+    // registers allow overlapping: the MFMAs of keys 0..63 go one at a time
+    // beside 1/NKC of the exponentials of keys 64..127 (a wave's MFMAs only
+    // overlap well with its own VALU work), then those of keys 64..127.
+    // With d = 128 there is no room for that (it spills); all of P first.
+    auto exp_pv = [&](auto fast_tag) __attribute__((always_inline)) {
+      using E16 = std::integral_constant<int, 16>;
+      using EC = std::integral_constant<int, 32 / NKC>;
+      if constexpr (D != 64) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) exp_part(kb, 0, E16{}, fast_tag);
+      } else {
+        exp_part(0, 0, E16{}, fast_tag);
+        exp_part(1, 0, E16{}, fast_tag);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) {
+          const i32x8 vn = vfrag(c + 2);
+          acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[0], acc_o[c], 0, 0, 0,
+                                                                       127, 0, 127);
+          const int e0 = c * (32 / NKC);               // element over blocks 2, 3
+          exp_part(2 + e0 / 16, e0 % 16, EC{}, fast_tag);
+          __builtin_amdgcn_sched_barrier(0);
+          va = vb;
+          vb = vn;
         }
-        // the block's share of l as a depth-4 tree (not a 16-long chain)
-        float t[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) t[j] = e[2 * j] + e[2 * j + 1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) t[j] = t[2 * j] + t[2 * j + 1];
-        l_part += (t[0] + t[1]) + (t[2] + t[3]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // the high half is written by the second convert: any old value
-          // does, and e's own register avoids zeroing one first
-          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], as_int(e[4 * w]), false);
-          pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], pk, true);
-          pf[kb / 2][(kb % 2) * 4 + w] = pk;
+        for (int c = 0; c < NKC; ++c) {
+          const i32x8 vn = (NKC + c + 2 < 2 * NKC) ? vfrag(NKC + c + 2) : i32x8{};
+          acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[1], acc_o[c], 0, 0, 0,
+                                                                       127, 0, 127);
+          __builtin_amdgcn_sched_barrier(0);
+          va = vb;
+          vb = vn;
         }
       }
     };
-    if (fast) exp_block(std::true_type{});
-    else exp_block(std::false_type{});
-
-    // ---- O^T += V^T P^T on the FP8 matrix cores (FP32 accumulation).
-    __builtin_amdgcn_sched_barrier(0);
+    if (fast) exp_pv(std::true_type{});
+    else exp_pv(std::false_type{});
+    if constexpr (D != 64) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int idx = 0; idx < 2 * NKC; ++idx) {
-      const int kb = idx / NKC, c = idx % NKC;
-      const i32x8 vn = (idx + 2 < 2 * NKC) ? vfrag(idx + 2) : i32x8{};
-      __builtin_amdgcn_sched_barrier(0);
-      acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[kb], acc_o[c], 0, 0, 0,
-                                                                   127, 0, 127);
-      __builtin_amdgcn_sched_barrier(0);
-      va = vb;
-      vb = vn;
+      for (int idx = 0; idx < 2 * NKC; ++idx) {
+        const int kb = idx / NKC, c = idx % NKC;
+        const i32x8 vn = (idx + 2 < 2 * NKC) ? vfrag(idx + 2) : i32x8{};
+        __builtin_amdgcn_sched_barrier(0);
+        acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[kb], acc_o[c], 0, 0, 0,
+                                                                     127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
+        va = vb;
+        vb = vn;
+      }
     }
   };
 
