@@ -5,7 +5,7 @@
 // per-channel scales, and P~ * 448 cast to FP8 before the P V product.
 //
 // Work decomposition: one workgroup = 4 waves = 128 queries of one head (one
-// Q scale block).  Each wave owns 32 queries and computes S^T = K Q^T for a
+// Q scale block); two (d = 128) or three (d = 64) workgroups share a CU.  Each wave owns 32 queries and computes S^T = K Q^T for a
 // 128-key tile as four 32x32 INT8 MFMA blocks, so every lane holds the
 // scores of ONE query (column L % 32) for 64 of the tile's keys; the other
 // 64 keys sit in lane L ^ 32.  Row max and row sum are therefore in-lane
@@ -26,7 +26,8 @@
 namespace sage {
 
 template <int D, bool CAUSAL, bool BF16>
-__global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
+// d = 64 fits three workgroups per CU (168 registers); d = 128 two.
+__global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_f8, const float* __restrict__ v_scale,
@@ -86,7 +87,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
 
   // One 128-key step of the online softmax.  MASK: the tile holds keys past
   // the diagonal (causal) or past N; only the last tile can.
-  auto step = [&](int t, auto mask_tag) {
+  // The exponent argument takes one FMA on the biased float of the int32
+  // sum when every dequant factor ck = cq * k_scale of the tiles this
+  // workgroup visits is <= kFastCk; otherwise kMagic is subtracted first.
+  // Decided once per workgroup, so each path is a loop of its own.
+  float kmax = 0.f;
+  for (int i = lane; i < min(nkb, ntiles * (kKvTile / kBlkK)); i += 64) kmax = fmaxf(kmax, ksc[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, o));
+  const bool fast_wg = cq * kmax <= kFastCk;
+
+  auto step = [&](int t, auto mask_tag, auto fast_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // Tile t has landed in buffer t&1 for every wave; buffer (t+1)&1 was
     // last read in iteration t-1, which every wave has finished.
@@ -170,7 +181,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
     // to ulp(kMagic*ck)/2 <= 2^-11 (log2 units); otherwise subtract kMagic
     // first (exact) and then apply ck.  ck is uniform over the wave.
     const float mq = m_new - kLog2_448;
-    const bool fast = fmaxf(fmaxf(ck[0], ck[1]), fmaxf(ck[2], ck[3])) <= kFastCk;
     i32x8 pf[2];
     // The first two V fragments are read before the exponentials, the rest
     // two MFMAs ahead, so no FP8 MFMA waits on LDS.
@@ -251,8 +261,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
         }
       }
     };
-    if (fast) exp_pv(std::true_type{});
-    else exp_pv(std::false_type{});
+    exp_pv(fast_tag);
     if constexpr (D != 64) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -271,8 +280,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_kernel(
 
   const bool last_masked = CAUSAL || (N % kKvTile) != 0;
   const int nfull = last_masked ? ntiles - 1 : ntiles;
-  for (int t = 0; t < nfull; ++t) step(t, std::false_type{});
-  if (last_masked) step(ntiles - 1, std::true_type{});
+  auto run = [&](auto fast_tag) __attribute__((always_inline)) {
+    for (int t = 0; t < nfull; ++t) step(t, std::false_type{}, fast_tag);
+    if (last_masked) step(ntiles - 1, std::true_type{}, fast_tag);
+  };
+  if (fast_wg) run(std::true_type{});
+  else run(std::false_type{});
 
   // ---- O = O / l * dV (l already carries the factor 448).
 #pragma unroll
