@@ -67,6 +67,10 @@ SMALL = [
     (1, 2, 2, 1, 64, torch.float16, False),
     (1, 2, 2, 17, 128, torch.float16, True),
     (1, 2, 1, 130, 64, torch.bfloat16, False),
+    (1, 2, 2, 64, 128, torch.float16, True),       # one K block, half a KV tile
+    (1, 1, 1, 128, 64, torch.bfloat16, True),      # exactly one tile
+    (1, 2, 2, 129, 128, torch.bfloat16, False),    # one key past a tile
+    (1, 8, 1, 255, 64, torch.float16, True),       # GQA group of 8, ragged
 ]
 
 
@@ -124,6 +128,42 @@ def test_large_magnitudes(gpu_lib):
     o = gpu_lib.sage_attn_fwd(qk, vq, causal=False, sm_scale=1 / 11.3, out_dtype=torch.float16)
     torch.cuda.synchronize()
     compare_output(o, _oracle_o(ref, refv, False, 1 / 11.3), max_abs=2e-2 * 1e-3 * 4)
+
+
+def test_quantization_ties_round_to_even(gpu_lib):
+    """Every x/scale lands exactly on a rounding midpoint: INT8 codes at k + 1/2 and FP8 codes
+    halfway between neighbours must round to even, bit-exactly as the oracle does."""
+    N, d = 256, 64
+    g = np.random.default_rng(21)
+    # Q: each 128-token block has amax 95.25 -> scale 0.75 exactly; the other values are
+    # (k + 1/2) * 0.75 for random k, so x / scale = k + 1/2 exactly (fp16 holds them).
+    kk = g.integers(-126, 126, size=(1, 2, N, d))
+    q = ((kk + 0.5) * 0.75).astype(np.float32)
+    q[:, :, ::128, 0] = 95.25
+    # V: per-channel amax 448 -> scale 1; values at FP8 midpoints (1 + (2j + 1)/16) * 2^e.
+    j = g.integers(0, 8, size=(1, 2, N, d))
+    e = g.integers(-3, 7, size=(1, 2, N, d))
+    sign = np.where(g.random((1, 2, N, d)) < 0.5, -1.0, 1.0)
+    v = (sign * (1 + (2 * j + 1) / 16.0) * 2.0 ** e).astype(np.float32)
+    v[:, :, 0, :] = 448.0
+    k = g.standard_normal((1, 2, N, d), dtype=np.float32)
+    qt, kt, vt = (torch.from_numpy(x).half() for x in (q, k, v))
+    assert torch.equal(qt.float(), torch.from_numpy(q)) and torch.equal(vt.float(), torch.from_numpy(v))
+    _check_quant(gpu_lib, qt, kt, vt)
+
+
+def test_one_large_k_block(gpu_lib):
+    """One K block with a huge scale: its workgroups take the exact exponent form, the others
+    the one-FMA form; both must agree with the oracle."""
+    q, k, v = _rand_inputs(1, 2, 2, 640, 128, torch.float16, seed=22)
+    k = k.float()
+    k[:, :, 192:256] *= 400.0
+    k = k.clamp(-60000, 60000).half()
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v)
+    for causal in (False, True):
+        o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=1 / 11.3, out_dtype=torch.float16)
+        torch.cuda.synchronize()
+        compare_output(o, _oracle_o(ref, refv, causal, 1 / 11.3))
 
 
 def test_deterministic(gpu_lib):
