@@ -101,6 +101,9 @@ def main():
                     help="workload name: tiny, llm_prefill, video_dit, sweep@N<n>, gqa_long")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--all", action="store_true",
+                    help="time every configuration (tiny, llm_prefill, video_dit, sweep N=1K..32K, "
+                         "gqa_long) and print one JSON line each instead of the single result line")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB (3 times), "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -131,7 +134,25 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     qa.load_library()
-    w = W.get(args.config)
+    if args.all:
+        names = ["tiny", "llm_prefill", "video_dit"] + [f"sweep@N{n}" for n in
+                                                        (1024, 2048, 4096, 8192, 16384, 32768)]
+        names.append("gqa_long")
+        for name in names:
+            r = run_config(W.get(name), max(args.steps, 5), args.warmup)
+            print(json.dumps(r), flush=True)
+        return
+    res = run_config(W.get(args.config), args.steps, args.warmup, full=True)
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(W.get(args.config), args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+def run_config(w, steps: int, warmup: int, full: bool = False) -> dict:
+    """Time `steps` whole steps of workload `w` (inputs resident on the GPU)."""
+    import torch
+    import quantized_attention_amd as qa
+    import workloads as W
     dev = torch.device("cuda:0")
     t = W.generate(w)
     q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
@@ -139,14 +160,14 @@ def main():
     plan = qa.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         plan(q, k, v)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         e = ev[s]
         e[0].record(stream)
         qa.sage_quant_qk(q, k, True, out=plan.qk, workspace=plan.ws_qk)
@@ -158,10 +179,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    t_qk = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    t_v = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    t_attn = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
-    ms_step = wall * 1e3 / args.steps
+    t_qk = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    t_v = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    t_attn = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    ms_step = wall * 1e3 / steps
     ops = w.ops()
     attn_tops = ops / (t_attn * 1e-3) / 1e12
     # algorithmic bytes of the quantizers: read 2 B + write 1 B per element of Q, K and V
@@ -173,8 +194,8 @@ def main():
         "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TOPS",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -199,9 +220,12 @@ def main():
             "traffic": traffic,
         },
     }
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
-    print(json.dumps(res), flush=True)
+    if not full:
+        keep = ("value", "ms_per_step", "config", "attn_tops", "attn_ms", "quant_qk_ms", "quant_v_ms",
+                "quant_gbs")
+        res = {k: res[k] for k in keep}
+        res["attn_frac_of_peak"] = round(res["attn_tops"] / PEAK_TOPS, 4)
+    return res
 
 
 if __name__ == "__main__":
