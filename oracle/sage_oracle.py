@@ -138,30 +138,38 @@ def quantize_v(v):
 # ---------------------------------------------------------------------------
 # (i) Exact attention: the plain definition, float64.
 
-def attn_exact(q, k, v, *, causal: bool, sm_scale: float, rows=None, heads=None):
+def attn_exact(q, k, v, *, causal: bool, sm_scale: float, rows=None, heads=None,
+               return_lse: bool = False):
     """O = softmax(sm_scale Q K^T + mask) V in float64.
 
     q [B,H,N,d]; k, v [B,H_kv,N,d]; query head h reads kv head h // (H/H_kv)
     (source-analysis page: num_qo_heads divisible by num_kv_heads).  Causal:
     key j is visible to query i iff j <= i.  ``rows``: optional index array
     of query rows to compute; ``heads``: optional list of (b, h).
-    Returns float64 [B,H,len(rows),d] (unselected heads are zero).
+    Returns float64 [B,H,len(rows),d] (unselected heads are zero); with
+    ``return_lse`` also the row log-sum-exp L_i = ln sum_j exp(s_ij) of the
+    logits s = sm_scale q k^T (natural log; the per-row state a forward pass
+    keeps in place of P, source-analysis page, FlashAttention section).
     """
     q64, k64, v64 = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q64.shape
     grp = H // k64.shape[1]
     rows = np.arange(N) if rows is None else np.asarray(rows)
     out = np.zeros((B, H, len(rows), d))
+    lse = np.zeros((B, H, len(rows)))
     for b, h in (heads or [(b, h) for b in range(B) for h in range(H)]):
         hk = h // grp
         s = (q64[b, h, rows] @ k64[b, hk].T) * sm_scale
         if causal:
             s = np.where(np.arange(N)[None, :] > rows[:, None], -np.inf, s)
-        s = s - s.max(axis=1, keepdims=True)
+        mx = s.max(axis=1, keepdims=True)
+        s = s - mx
         p = np.exp(s)
-        p /= p.sum(axis=1, keepdims=True)
+        ps = p.sum(axis=1, keepdims=True)
+        lse[b, h] = (mx + np.log(ps))[:, 0]
+        p /= ps
         out[b, h] = p @ v64[b, hk]
-    return out
+    return (out, lse) if return_lse else out
 
 
 def softmax_rows(q, k, *, causal: bool, sm_scale: float, b=0, h=0, hk=None):
@@ -195,13 +203,17 @@ def softmax_rows(q, k, *, causal: bool, sm_scale: float, b=0, h=0, hk=None):
 
 def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
                kv_tile: int = KV_TILE, rows=None, heads=None,
-               quantize_p: bool = True, blkq: int = BLKQ, blkk: int = BLKK):
+               quantize_p: bool = True, blkq: int = BLKQ, blkk: int = BLKK,
+               return_lse: bool = False):
     """Quantized attention, float64 result [B,H,len(rows),d].
 
     qc int8 [B,H,N,d], qs f32 [B,H,nq]; kc int8 [B,H_kv,N,d], ks f32
     [B,H_kv,nk]; vc uint8 E4M3 codes [B,H_kv,N,d] (natural layout), vs f32
     [B,H_kv,d].  ``quantize_p=False`` skips the FP8 rounding of 448*Pt (the
-    result is then exact attention on the dequantized inputs).
+    result is then exact attention on the dequantized inputs).  With
+    ``return_lse`` also L'_i = m_T + ln l (natural log) of the dequantized
+    scores S the recursion used -- of the smoothed K when the codes are of
+    K - mean(K); ``lse_correction`` restores the unsmoothed value.
     """
     B, H, N, d = qc.shape
     grp = H // kc.shape[1]
@@ -210,6 +222,7 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
     npad = nt * kv_tile
     key_blk = np.arange(N) // blkk
     out = np.zeros((B, H, len(rows), d))
+    lse = np.zeros((B, H, len(rows)))
     chunk = max(1, (1 << 24) // npad)               # bound the [rows, keys] temporaries
     for b, h in (heads or [(b, h) for b in range(B) for h in range(H)]):
         hk = h // grp
@@ -235,20 +248,36 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
             l = np.sum(pt.sum(axis=2) * carry, axis=1)
             w = (pq * carry[:, :, None]).reshape(len(rr), npad)[:, :N]
             out[b, h, r0:r0 + chunk] = (w @ vdq) / (P_SCALE * l)[:, None]
-    return out
+            lse[b, h, r0:r0 + chunk] = m_fin[:, 0] + np.log(l)
+    return (out, lse) if return_lse else out
+
+
+def lse_correction(q, k_mean, *, sm_scale: float):
+    """sm_scale * q_i . mean(K), float64 [B,H,N]: what smoothing K removed
+    from every logit of row i, added back to the log-sum-exp (source-analysis
+    page, "smooth_k 与 LSE 校正": the q @ mean(K) term).  q is the original
+    fp16/bf16 Q; k_mean the float32 K mean [B,H_kv,d] (query head h uses kv
+    head h // (H/H_kv))."""
+    q64 = _f64(q)
+    km = np.asarray(k_mean, dtype=np.float64)
+    grp = q64.shape[1] // km.shape[1]
+    km_h = np.repeat(km, grp, axis=1)                       # [B,H,d]
+    return np.einsum("bhnc,bhc->bhn", q64, km_h) * sm_scale
 
 
 def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
-                         b=0, h=0, hk=None, blkq=BLKQ, blkk=BLKK):
+                         b=0, h=0, hk=None, blkq=BLKQ, blkk=BLKK, return_lse=False):
     """Literal online recursion of Algorithm 1 in pure Python loops (tiny sizes).
 
     Used to pin ``attn_quant``'s closed form: the same steps, one key tile at
-    a time, with m, l and O updated in place.
+    a time, with m, l and O updated in place (and, with ``return_lse``, the
+    final m + ln l of each row).
     """
     n, d = qc.shape[2], qc.shape[3]
     hk = h if hk is None else hk
     vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
     out = np.zeros((n, d))
+    lse = np.zeros(n)
     for i in range(n):
         m, l = -math.inf, 0.0
         o = [0.0] * d
@@ -274,7 +303,8 @@ def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
                     o[c] += pq * vdq[j, c]
             m = m_new
         out[i] = [x / (P_SCALE * l) for x in o]
-    return out
+        lse[i] = m + math.log(l)
+    return (out, lse) if return_lse else out
 
 
 # ---------------------------------------------------------------------------

@@ -366,3 +366,76 @@ def test_quantized_vs_exact_tiny_full():
 ])
 def test_quantized_vs_exact_sampled(name, heads):
     _sample_check(name, heads, 96, 7)
+
+
+# ---------------------------------------------------------------- log-sum-exp (LSE)
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_lse_matches_logsumexp(causal):
+    """attn_exact's LSE equals scipy's logsumexp of the masked logits and a plain
+    math.log(sum(math.exp)) loop on a few rows."""
+    from scipy.special import logsumexp
+    g = np.random.default_rng(31)
+    q = torch.from_numpy(g.standard_normal((1, 2, 37, 16), dtype=np.float32)).half()
+    k = torch.from_numpy(g.standard_normal((1, 1, 37, 16), dtype=np.float32) * 2).half()
+    v = torch.zeros((1, 1, 37, 16), dtype=torch.float16)
+    _, lse = O.attn_exact(q, k, v, causal=causal, sm_scale=0.3, return_lse=True)
+    s = np.einsum("hnc,mc->hnm", q[0].double().numpy(), k[0, 0].double().numpy()) * 0.3
+    if causal:
+        s = np.where(np.arange(37)[None, None, :] > np.arange(37)[None, :, None], -np.inf, s)
+    assert np.allclose(lse[0], logsumexp(s, axis=2), rtol=0, atol=1e-12)
+    for i in (0, 5, 36):
+        n = i + 1 if causal else 37
+        ref = math.log(sum(math.exp(s[1, i, j]) for j in range(n)))
+        assert abs(lse[0, 1, i] - ref) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_quant_lse_matches_literal_recursion(causal):
+    """The closed form's m_T + ln l equals the final state of the literal recursion."""
+    g = np.random.default_rng(32)
+    q = torch.from_numpy(g.standard_normal((1, 1, 40, 32), dtype=np.float32)).half()
+    k = torch.from_numpy(g.standard_normal((1, 1, 40, 32), dtype=np.float32) + 2).half()
+    v = torch.from_numpy(g.standard_normal((1, 1, 40, 32), dtype=np.float32)).half()
+    z, zv = O.quantize_qk(q, k), O.quantize_v(v)
+    args = (z["q_i8"], z["q_scale"], z["k_i8"], z["k_scale"], zv["v_f8"], zv["v_scale"])
+    _, l1 = O.attn_quant(*args, causal=causal, sm_scale=0.2, kv_tile=16, return_lse=True)
+    _, l2 = O.attn_quant_recursive(*args, causal=causal, sm_scale=0.2, kv_tile=16,
+                                   return_lse=True)
+    assert np.allclose(l1[0, 0], l2, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_quant_lse_of_zero_q(causal):
+    """Q = 0: every logit is 0, so L_i = ln(number of visible keys) exactly."""
+    N = 200
+    q = torch.zeros((1, 1, N, 64), dtype=torch.float16)
+    g = np.random.default_rng(33)
+    k = torch.from_numpy(g.standard_normal((1, 1, N, 64), dtype=np.float32)).half()
+    z, zv = O.quantize_qk(q, k), O.quantize_v(k)
+    _, lse = O.attn_quant(z["q_i8"], z["q_scale"], z["k_i8"], z["k_scale"], zv["v_f8"],
+                          zv["v_scale"], causal=causal, sm_scale=0.125, return_lse=True)
+    nvis = np.arange(1, N + 1) if causal else np.full(N, N)
+    assert np.allclose(lse[0, 0], np.log(nvis), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_correction_restores_unsmoothed_lse(causal):
+    """Smoothing shifts every logit of row i by sm_scale q_i . mean(K); the quantized LSE of
+    the smoothed scores plus lse_correction matches the exact LSE of the original inputs
+    within the quantization error, and is far from it without the correction (a shared
+    K bias of sigma 3 makes the shift large).  Also with GQA (two query heads per kv head)."""
+    g = np.random.default_rng(34)
+    B, H, Hk, N, d = 1, 4, 2, 300, 64
+    q = torch.from_numpy(g.standard_normal((B, H, N, d), dtype=np.float32)).half()
+    k = g.standard_normal((B, Hk, N, d), dtype=np.float32)
+    k += g.standard_normal((B, Hk, 1, d), dtype=np.float32) * 3
+    k = torch.from_numpy(k).half()
+    v = torch.from_numpy(g.standard_normal((B, Hk, N, d), dtype=np.float32)).half()
+    _, lx = O.attn_exact(q, k, v, causal=causal, sm_scale=0.125, return_lse=True)
+    z, zv = O.quantize_qk(q, k, smooth_k=True), O.quantize_v(v)
+    _, ls = O.attn_quant(z["q_i8"], z["q_scale"], z["k_i8"], z["k_scale"], zv["v_f8"],
+                         zv["v_scale"], causal=causal, sm_scale=0.125, return_lse=True)
+    corr = O.lse_correction(q, z["k_mean"], sm_scale=0.125)
+    assert np.abs(ls + corr - lx).max() < 0.05
+    assert np.abs(ls - lx).max() > 1.0
