@@ -101,6 +101,9 @@ def main():
                     help="workload name: tiny, llm_prefill, video_dit, sweep@N<n>, gqa_long")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--lse", action="store_true",
+                    help="also time the log-sum-exp path (sage_lse_correction + "
+                         "sage_attn_fwd_lse) and report its cost beside the plain step")
     ap.add_argument("--all", action="store_true",
                     help="time every configuration (tiny, llm_prefill, video_dit, sweep N=1K..32K, "
                          "gqa_long) and print one JSON line each instead of the single result line")
@@ -143,9 +146,55 @@ def main():
             print(json.dumps(r), flush=True)
         return
     res = run_config(W.get(args.config), args.steps, args.warmup, full=True)
+    if args.lse:
+        res["lse"] = run_lse(W.get(args.config), args.steps, args.warmup)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(W.get(args.config), args.cpu_budget)
     print(json.dumps(res), flush=True)
+
+
+def run_lse(w, steps: int, warmup: int) -> dict:
+    """Time the log-sum-exp path: the correction kernel and the attention kernel
+    that also writes the LSE (against the plain attention kernel)."""
+    import torch
+    import quantized_attention_amd as qa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    t = W.generate(w)
+    q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
+    del t
+    plan = qa.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal, device=dev)
+    plan.quant(q, k, v)
+    corr = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    lse = torch.empty_like(corr)
+    stream = torch.cuda.current_stream(dev)
+    run = lambda: (qa.sage_lse_correction(q, plan.qk["k_mean"], plan.sm_scale, out=corr),
+                   qa.sage_attn_fwd_lse(plan.qk, plan.vq, causal=w.causal, sm_scale=plan.sm_scale,
+                                        out_dtype=w.torch_dtype, lse_corr=corr, out=plan.o,
+                                        lse=lse))
+    for _ in range(warmup):
+        run()
+        plan.attn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        qa.sage_lse_correction(q, plan.qk["k_mean"], plan.sm_scale, out=corr)
+        e[1].record(stream)
+        qa.sage_attn_fwd_lse(plan.qk, plan.vq, causal=w.causal, sm_scale=plan.sm_scale,
+                             out_dtype=w.torch_dtype, lse_corr=corr, out=plan.o, lse=lse)
+        e[2].record(stream)
+        plan.attn()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t_c = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    t_al = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    t_a = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    corr_bytes = w.B * w.H * w.N * (2 * w.d + 4)      # read Q, write one float per row
+    return {"lse_correction_ms": round(t_c, 4),
+            "lse_correction_gbs": round(corr_bytes / (t_c * 1e-3) / 1e9, 1),
+            "attn_fwd_lse_ms": round(t_al, 4), "attn_fwd_ms": round(t_a, 4),
+            "attn_fwd_lse_tops": round(w.ops() / (t_al * 1e-3) / 1e12, 2)}
 
 
 def run_config(w, steps: int, warmup: int, full: bool = False) -> dict:

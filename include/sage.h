@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 1
+#define SAGE_ABI_VERSION 2
 
 /* Q tokens per INT8 scale, K tokens per INT8 scale. */
 #define SAGE_BLKQ 128
@@ -149,6 +149,38 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
                           const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                           void* o, sage_dtype out_dtype, int B, int H, int H_kv, int N, int d,
                           int causal, float sm_scale, void* stream);
+
+/*
+ * Step 4 with the row log-sum-exp (the per-row softmax state a forward pass
+ * keeps in place of P: the FlashAttention section of the source-analysis
+ * page).  Same inputs, output and semantics as sage_attn_fwd, plus
+ *   lse: float [B][H][N], required (caller-owned):
+ *     lse[b][h][i] = ln sum_j exp(S_ij) + (lse_corr ? lse_corr[b][h][i] : 0)
+ *     with S the dequantized scores the softmax used (sm_scale applied, the
+ *     causal mask applied, K smoothed if sage_quant_qk smoothed it).
+ *   lse_corr: float [B][H][N] or NULL.  With smoothed K, pass the output of
+ *     sage_lse_correction to get the log-sum-exp of the unsmoothed logits
+ *     sm_scale * q . k (smoothing removed sm_scale * q . mean(K) from every
+ *     logit of a row; the source-analysis page, smooth_k and LSE correction).
+ * Accuracy: the one-FMA exponent form bounds the error of each exponent by
+ * 2^-11 in log2 units, so lse is within about 4e-4 of the same quantity in
+ * exact arithmetic.
+ */
+sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                              const float* k_scale, const uint8_t* v_f8, const float* v_scale,
+                              void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
+                              int B, int H, int H_kv, int N, int d, int causal, float sm_scale,
+                              void* stream);
+
+/*
+ * corr[b][h][i] = sm_scale * sum_c q[b][h][i][c] * k_mean[b][h / (H/H_kv)][c]
+ * in fp32 (fixed summation order), for sage_attn_fwd_lse.
+ *   q [B][H][N][d] in `dtype` (the original, unquantized Q); k_mean
+ *   [B][H_kv][d] from sage_quant_qk; corr float [B][H][N], caller-owned.
+ */
+sage_status sage_lse_correction(const void* q, sage_dtype dtype, const float* k_mean, int B, int H,
+                                int H_kv, int N, int d, float sm_scale, float* corr,
+                                void* stream);
 
 /*
  * Diagnostic: the exact int32 dot products sum_c q_i8[b][h][i][c] *

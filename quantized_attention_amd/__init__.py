@@ -15,8 +15,11 @@ Entry points (same names as the C ABI):
     sage_quant_qk(q, k, smooth_k=True) -> dict(q_i8, q_scale, k_i8, k_scale, k_mean)
     sage_quant_v(v) -> dict(v_f8, v_scale)
     sage_attn_fwd(qk, vq, causal=..., sm_scale=..., out_dtype=...) -> o
+    sage_attn_fwd_lse(qk, vq, causal=..., sm_scale=..., lse_corr=None) -> (o, lse)
+    sage_lse_correction(q, k_mean, sm_scale) -> fp32 [B, H, N]
     sage_qk_int32(q_i8, k_i8, b, h) -> int32 [N, N] (diagnostic)
-and the composition ``sageattn(q, k, v, is_causal=False, sm_scale=None)``.
+and the composition ``sageattn(q, k, v, is_causal=False, sm_scale=None,
+return_lse=False)``.
 """
 from __future__ import annotations
 
@@ -27,8 +30,8 @@ import os
 import torch
 
 __all__ = ["SageError", "library_path", "load_library", "sage_buffer_sizes", "sage_quant_qk",
-           "sage_quant_v", "sage_attn_fwd", "sage_qk_int32", "sageattn", "SagePlan",
-           "BLKQ", "BLKK", "KV_TILE"]
+           "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse", "sage_lse_correction",
+           "sage_qk_int32", "sageattn", "SagePlan", "BLKQ", "BLKK", "KV_TILE"]
 
 BLKQ, BLKK, KV_TILE = 128, 64, 128
 _FP16, _BF16 = 0, 1
@@ -72,9 +75,12 @@ def load_library():
     lib.sage_quant_v.argtypes = [vp, i, i, i, i, i, vp, vp, vp, sz, vp]
     lib.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                   ctypes.c_float, vp]
+    lib.sage_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i,
+                                      ctypes.c_float, vp]
+    lib.sage_lse_correction.argtypes = [vp, i, vp, i, i, i, i, i, ctypes.c_float, vp, vp]
     lib.sage_qk_int32.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp]
     for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_quant_v", "sage_attn_fwd",
-              "sage_qk_int32"):
+              "sage_attn_fwd_lse", "sage_lse_correction", "sage_qk_int32"):
         getattr(lib, f).restype = i
     _lib = lib
     return lib
@@ -195,6 +201,50 @@ def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
     return out
 
 
+def sage_attn_fwd_lse(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
+                      out_dtype=torch.float16, lse_corr=None, out=None, lse=None,
+                      stream=None):
+    """Attention on quantized inputs plus the row log-sum-exp; returns (o, lse).
+    lse [B, H, N] fp32 is ln sum_j exp(S_ij) of the scores the softmax used,
+    plus lse_corr (the output of sage_lse_correction) when given."""
+    q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
+    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"])
+    B, H, N, d = q_i8.shape
+    H_kv = k_i8.shape[1]
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q_i8.device)
+    _need_gpu(out, lse)
+    if lse_corr is not None:
+        _need_gpu(lse_corr)
+        if lse_corr.shape != (B, H, N) or lse_corr.dtype != torch.float32:
+            raise ValueError("lse_corr must be float32 [B, H, N]")
+    st = load_library().sage_attn_fwd_lse(
+        q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
+        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
+        lse.data_ptr(), _ptr(lse_corr), B, H, H_kv, N, d, int(bool(causal)), float(sm_scale),
+        _stream(stream, q_i8.device))
+    _check(st, "sage_attn_fwd_lse")
+    return out, lse
+
+
+def sage_lse_correction(q: torch.Tensor, k_mean: torch.Tensor, sm_scale: float, *, out=None,
+                        stream=None) -> torch.Tensor:
+    """sm_scale * q . mean(K) per row, fp32 [B, H, N] (for sage_attn_fwd_lse)."""
+    _need_gpu(q, k_mean)
+    B, H, N, d = q.shape
+    H_kv = k_mean.shape[1]
+    if out is None:
+        out = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _need_gpu(out)
+    st = load_library().sage_lse_correction(q.data_ptr(), _dt(q.dtype), k_mean.data_ptr(), B, H,
+                                            H_kv, N, d, float(sm_scale), out.data_ptr(),
+                                            _stream(stream, q.device))
+    _check(st, "sage_lse_correction")
+    return out
+
+
 def sage_qk_int32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, *,
                   stream=None) -> torch.Tensor:
     """Exact int32 Q^ K^T of query head (b, h) through the attention kernel's tile routine."""
@@ -209,13 +259,19 @@ def sage_qk_int32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, *,
 
 
 def sageattn(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
-             smooth_k: bool = True) -> torch.Tensor:
-    """The whole forward pass: quantize Q/K/V, then the attention kernel."""
+             smooth_k: bool = True, return_lse: bool = False):
+    """The whole forward pass: quantize Q/K/V, then the attention kernel.
+    With return_lse, also the row log-sum-exp of the logits sm_scale q . k
+    (corrected for the smoothing of K); returns (o, lse)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
     qk = sage_quant_qk(q, k, smooth_k)
     vq = sage_quant_v(v)
-    return sage_attn_fwd(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype)
+    if not return_lse:
+        return sage_attn_fwd(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype)
+    corr = sage_lse_correction(q, qk["k_mean"], sm_scale) if smooth_k else None
+    return sage_attn_fwd_lse(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype,
+                             lse_corr=corr)
 
 
 class SagePlan:

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_f8, const float* __restrict__ v_scale,
-    void* __restrict__ out, int H, int H_kv, int N, float sm_log2, int nqt, int total) {
+    void* __restrict__ out, float* __restrict__ lse, const float* __restrict__ lse_corr, int H,
+    int H_kv, int N, float sm_log2, int nqt, int total) {
   constexpr int NKC = D / 32;                 // 32-wide channel chunks
   constexpr int KBYTES = kKvTile * D;         // K tile bytes (== V tile bytes)
   __shared__ __attribute__((aligned(16))) char lds[2][2 * KBYTES];
@@ -292,6 +293,16 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
   for (int c = 0; c < NKC; ++c) pin(acc_o[c]);
   const float l_tot = l_part + __shfl_xor(l_part, 32);
   const float inv = 1.0f / l_tot;
+  // Row log-sum-exp (natural log) of the scores S the softmax used: the
+  // running max m (log2 units of S) and l = sum 448 * 2^(S log2 e - m) give
+  // ln sum exp(S) = ln 2 * (m + log2(l) - log2 448); plus the caller's
+  // correction for smoothed K (sm_scale * q . mean K) when given.
+  if (lse != nullptr && half == 0 && qi < N) {
+    const size_t row = (size_t)(b * H + h) * N + qi;
+    float v = 0.69314718055994531f * (m_run + log2f(l_tot) - kLog2_448);
+    if (lse_corr != nullptr) v += lse_corr[row];
+    lse[row] = v;
+  }
   if (qi < N) {
     char* orow = reinterpret_cast<char*>(out) + ((size_t)(b * H + h) * N + qi) * D * 2;
     const float* vs = v_scale + (size_t)(b * H_kv + hk) * D;
@@ -366,8 +377,9 @@ __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
 
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                                void* o, int bf16_out, int B, int H, int H_kv, int N, int d,
-                                int causal, float sm_scale, hipStream_t stream) {
+                                void* o, int bf16_out, float* lse, const float* lse_corr, int B,
+                                int H, int H_kv, int N, int d, int causal, float sm_scale,
+                                hipStream_t stream) {
   using namespace sage;
   const int nqt = (N + kBlockQ - 1) / kBlockQ;
   const long long total = (long long)B * H * nqt;
@@ -377,7 +389,8 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
 #define SAGE_ATTN_CASE(DD, CC, BB)                                                               \
   if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB) {                                 \
     hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB>), grid, block, 0, stream, q_i8, q_scale,     \
-                       k_i8, k_scale, v_f8, v_scale, o, H, H_kv, N, sm_log2, nqt, (int)total);  \
+                       k_i8, k_scale, v_f8, v_scale, o, lse, lse_corr, H, H_kv, N, sm_log2,      \
+                       nqt, (int)total);                                                         \
     return hipGetLastError();                                                                    \
   }
   SAGE_ATTN_CASE(64, false, false)

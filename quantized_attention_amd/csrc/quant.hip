@@ -292,6 +292,36 @@ __global__ __launch_bounds__(kQuantThreads) void quant_v_fp8(const void* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// corr[bh][n] = sm_scale * sum_c q[bh][n][c] * mean[bh_kv][c]: the part of
+// every logit of row n that smoothing K removed (source-analysis page,
+// smooth_k and LSE correction).  D/8 threads per row, 16-byte loads, fixed
+// reduction order.  grid (ceil(N / rows per block), B*H).
+template <int D, bool BF16>
+__global__ __launch_bounds__(kQuantThreads) void lse_correction(const void* __restrict__ q,
+                                                                const float* __restrict__ mean,
+                                                                float* __restrict__ corr, int H,
+                                                                int H_kv, int N, float sm_scale) {
+  constexpr int TPR = D / 8;                     // threads per row
+  constexpr int RPB = kQuantThreads / TPR;       // rows per block
+  const int bh = blockIdx.y, tid = threadIdx.x, cg = tid % TPR;
+  const int n = blockIdx.x * RPB + tid / TPR;
+  const int b = bh / H, h = bh % H, hk = h / (H / H_kv);
+  const float* mu = mean + (size_t)(b * H_kv + hk) * D + cg * 8;
+  float acc = 0.f;
+  if (n < N) {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) +
+                                                    ((size_t)bh * N + n) * D + cg * 8);
+    float x[8];
+    unpack8<BF16>(u, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(x[i], mu[i], acc);
+  }
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (n < N && cg == 0) corr[(size_t)bh * N + n] = acc * sm_scale;
+}
+
 }  // namespace sage
 
 // ---------------------------------------------------------------------------
@@ -369,5 +399,25 @@ hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, 
   if (d == 128)
     return bf16 ? quant_v_impl<128, true>(v, B, H_kv, N, v_f8, v_scale, ws, st)
                 : quant_v_impl<128, false>(v, B, H_kv, N, v_f8, v_scale, ws, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t sage_launch_lse_correction(const void* q, int bf16, const float* k_mean, int B, int H,
+                                      int H_kv, int N, int d, float sm_scale, float* corr,
+                                      hipStream_t st) {
+  using namespace sage;
+  const int rpb = kQuantThreads / (d / 8);
+  const dim3 grid((N + rpb - 1) / rpb, B * H), block(kQuantThreads);
+#define SAGE_LSEC(DD, BB)                                                                      \
+  if (d == DD && (bf16 != 0) == BB) {                                                          \
+    hipLaunchKernelGGL((lse_correction<DD, BB>), grid, block, 0, st, q, k_mean, corr, H, H_kv, \
+                       N, sm_scale);                                                           \
+    return hipGetLastError();                                                                  \
+  }
+  SAGE_LSEC(64, false)
+  SAGE_LSEC(64, true)
+  SAGE_LSEC(128, false)
+  SAGE_LSEC(128, true)
+#undef SAGE_LSEC
   return hipErrorInvalidValue;
 }

@@ -16,8 +16,12 @@ hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, 
                                uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st);
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                                void* o, int bf16_out, int B, int H, int H_kv, int N, int d,
-                                int causal, float sm_scale, hipStream_t stream);
+                                void* o, int bf16_out, float* lse, const float* lse_corr, int B,
+                                int H, int H_kv, int N, int d, int causal, float sm_scale,
+                                hipStream_t stream);
+hipError_t sage_launch_lse_correction(const void* q, int bf16, const float* k_mean, int B, int H,
+                                      int H_kv, int N, int d, float sm_scale, float* corr,
+                                      hipStream_t st);
 hipError_t sage_launch_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int H_kv,
                                 int N, int d, int b, int h, int32_t* s_out, hipStream_t stream);
 size_t sage_ws_quant_qk_bytes(int B, int H_kv, int N, int d);
@@ -130,8 +134,40 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
     return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, o,
-                                       out_dtype == SAGE_BF16, B, H, H_kv, N, d, causal,
-                                       sm_scale, (hipStream_t)stream));
+                                       out_dtype == SAGE_BF16, nullptr, nullptr, B, H, H_kv, N,
+                                       d, causal, sm_scale, (hipStream_t)stream));
+}
+
+sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                              const float* k_scale, const uint8_t* v_f8, const float* v_scale,
+                              void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
+                              int B, int H, int H_kv, int N, int d, int causal, float sm_scale,
+                              void* stream) {
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8 || !v_scale || !o || !lse)
+    return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return SAGE_ERR_ARG;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
+  if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
+    return SAGE_ERR_ALIGN;
+  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, o,
+                                       out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d,
+                                       causal, sm_scale, (hipStream_t)stream));
+}
+
+sage_status sage_lse_correction(const void* q, sage_dtype dtype, const float* k_mean, int B, int H,
+                                int H_kv, int N, int d, float sm_scale, float* corr,
+                                void* stream) {
+  if (!q || !k_mean || !corr) return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
+  if (!aligned16(q)) return SAGE_ERR_ALIGN;
+  return from_hip(sage_launch_lse_correction(q, dtype == SAGE_BF16, k_mean, B, H, H_kv, N, d,
+                                             sm_scale, corr, (hipStream_t)stream));
 }
 
 sage_status sage_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int H_kv, int N,

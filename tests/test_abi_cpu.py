@@ -24,11 +24,12 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = qa.load_library()
     names = _declared()
-    assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_buffer_sizes",
-            "sage_qk_int32", "sage_status_str", "sage_abi_version"} <= set(names)
+    assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse",
+            "sage_lse_correction", "sage_buffer_sizes", "sage_qk_int32", "sage_status_str",
+            "sage_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sage_abi_version() == 1
+    assert lib.sage_abi_version() == 2
 
 
 def test_status_strings():
@@ -86,6 +87,21 @@ def _attn(lib, **kw):
     return lib.sage_attn_fwd(*a.values())
 
 
+def _attn_lse(lib, **kw):
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, o=FAKE,
+             dt=0, lse=FAKE, corr=None, B=1, H=2, H_kv=2, N=256, d=64, causal=0, sm_scale=0.125,
+             stream=None)
+    a.update(kw)
+    return lib.sage_attn_fwd_lse(*a.values())
+
+
+def _lse_corr(lib, **kw):
+    a = dict(q=FAKE, dt=0, k_mean=FAKE, B=1, H=2, H_kv=2, N=256, d=64, sm_scale=0.125, corr=FAKE,
+             stream=None)
+    a.update(kw)
+    return lib.sage_lse_correction(*a.values())
+
+
 def _qk32(lib, **kw):
     a = dict(q_i8=FAKE, k_i8=FAKE, B=1, H=2, H_kv=2, N=256, d=64, b=0, h=0, s=FAKE, stream=None)
     a.update(kw)
@@ -122,6 +138,24 @@ def test_quant_v_rejects(kw, code):
 ])
 def test_attn_fwd_rejects(kw, code):
     assert _attn(qa.load_library(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), 1), (dict(o=None), 1), (dict(B=0), 2), (dict(d=96), 3),
+    (dict(H=4, H_kv=3), 4), (dict(dt=3), 5), (dict(causal=2), 6), (dict(sm_scale=0.0), 6),
+    (dict(sm_scale=float("nan")), 6), (dict(k_i8=FAKE + 4), 9),
+])
+def test_attn_fwd_lse_rejects(kw, code):
+    assert _attn_lse(qa.load_library(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k_mean=None), 1), (dict(corr=None), 1), (dict(N=0), 2),
+    (dict(d=48), 3), (dict(H=3), 4), (dict(dt=9), 5), (dict(sm_scale=-2.0), 6),
+    (dict(q=FAKE + 2), 9),
+])
+def test_lse_correction_rejects(kw, code):
+    assert _lse_corr(qa.load_library(), **kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -236,3 +236,60 @@ def _workload_check(gpu_lib, name, heads, nrows, seed=0):
 ])
 def test_workload_parity(gpu_lib, name, heads, nrows):
     _workload_check(gpu_lib, name, heads, nrows)
+
+
+# ------------------------------------------------------------------ log-sum-exp (LSE)
+
+def _lse_tol(N, corr):
+    """Bound on |lse_gpu - lse_oracle|: each exponent of the one-FMA form is off by at most
+    2^-11 log2 units (ln 2 * 2^-11 in the LSE), the FP32 sum of N positive terms is within
+    N * 2^-24 relative, and the FP32 correction dot product within ~1e-6 of its magnitude."""
+    return math.log(2) * 2.0 ** -11 + N * 2.0 ** -24 + 1e-6 * np.abs(corr) + 1e-6
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", [
+    (1, 2, 2, 256, 64, torch.float16, False),
+    (2, 4, 2, 700, 128, torch.bfloat16, True),
+    (1, 8, 1, 255, 64, torch.float16, True),
+    (1, 2, 2, 129, 128, torch.float16, False),
+])
+def test_lse_parity(gpu_lib, B, H, H_kv, N, d, dtype, causal):
+    """sage_attn_fwd_lse: O identical to sage_attn_fwd; lse = ln sum exp of the scores used
+    (+ the q . mean(K) correction) against the oracle's m_T + ln l (+ lse_correction)."""
+    print(f"lse case B{B} H{H}/{H_kv} N{N} d{d} {dtype} causal={causal}", flush=True)
+    q, k, v = _rand_inputs(B, H, H_kv, N, d, dtype, seed=N * 5 + d)
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v)
+    sm = 1 / math.sqrt(d)
+    o0 = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=sm, out_dtype=dtype)
+    corr = gpu_lib.sage_lse_correction(q.to(DEV), qk["k_mean"], sm)
+    o1, lse = gpu_lib.sage_attn_fwd_lse(qk, vq, causal=causal, sm_scale=sm, out_dtype=dtype,
+                                        lse_corr=corr)
+    _, lse_raw = gpu_lib.sage_attn_fwd_lse(qk, vq, causal=causal, sm_scale=sm, out_dtype=dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1)
+    _, l_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
+                            refv["v_f8"], refv["v_scale"], causal=causal, sm_scale=sm,
+                            return_lse=True)
+    c_ref = O.lse_correction(q, ref["k_mean"], sm_scale=sm)
+    c_gpu = to_np(corr).astype(np.float64)
+    # FP32 dot product of d terms: within (d + 2) * 2^-24 * sm * sum |q_c mean_c|
+    c_abs = O.lse_correction(q.float().abs(), np.abs(ref["k_mean"]), sm_scale=sm)
+    c_err = np.abs(c_gpu - c_ref)
+    assert np.all(c_err <= (d + 2) * 2.0 ** -24 * c_abs + 1e-9), c_err.max()
+    tol = _lse_tol(N, c_abs)
+    err = np.abs(to_np(lse).astype(np.float64) - (l_ref + c_ref))
+    assert np.all(err <= tol), (err.max(), np.unravel_index(err.argmax(), err.shape))
+    err_raw = np.abs(to_np(lse_raw).astype(np.float64) - l_ref)
+    assert np.all(err_raw <= _lse_tol(N, 0.0)), err_raw.max()
+
+
+def test_lse_tracks_exact_lse(gpu_lib):
+    """End to end (sageattn with return_lse): the corrected LSE of the quantized method is
+    close to the exact FP64 LSE of the original inputs (quantization error only), for a
+    workload with a large shared K bias (the correction is many units)."""
+    q, k, v = _rand_inputs(1, 4, 2, 512, 128, torch.float16, seed=41, bias=3.0)
+    o, lse = gpu_lib.sageattn(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=True,
+                              sm_scale=1 / math.sqrt(128), return_lse=True)
+    torch.cuda.synchronize()
+    _, l_exact = O.attn_exact(q, k, v, causal=True, sm_scale=1 / math.sqrt(128), return_lse=True)
+    assert np.abs(to_np(lse).astype(np.float64) - l_exact).max() < 0.05
