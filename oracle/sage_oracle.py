@@ -96,12 +96,27 @@ def quantize_int8_blocks(x32: np.ndarray, block: int):
     return codes, scales
 
 
-def quantize_qk(q, k, smooth_k: bool = True):
-    """Quantize Q per 128 tokens and smoothed K per 64 tokens.
+# Q scale granularity.  The detail page's per-thread quantization gives each
+# thread of the matrix-core instruction the Q tokens it holds, one scale per
+# such group (Figure 4, "Per-thread" paragraph; Table 6 compares per-token,
+# per-thread, per-block and per-tensor), and the source-analysis page's
+# quantization module lists per-block / per-warp / per-thread Q scales.
+# Reading: the groups are runs of consecutive tokens, `q_group` tokens each
+# (128 = the per-block scale; 32 = the queries one matrix-core column block
+# holds, the per-warp analogue; 1 = one query per scale, the per-thread
+# analogue when each lane holds one query).  The scale and code rules are
+# those of the block quantizer above, applied per group.
+Q_GROUPS = (BLKQ, 32, 1)
+
+
+def quantize_qk(q, k, smooth_k: bool = True, q_group: int = BLKQ):
+    """Quantize Q per `q_group` tokens and smoothed K per 64 tokens.
 
     q: [B, H, N, d], k: [B, H_kv, N, d] (fp16/bf16 values as torch or numpy).
-    Returns dict(q_i8, q_scale, k_i8, k_scale, k_mean).
+    Returns dict(q_i8, q_scale, k_i8, k_scale, k_mean); q_scale has
+    ceil(N / q_group) entries per head.
     """
+    assert q_group in Q_GROUPS, q_group
     q32 = _f32(q)
     k32 = _f32(k)
     if smooth_k:
@@ -110,7 +125,7 @@ def quantize_qk(q, k, smooth_k: bool = True):
     else:
         mean = np.zeros(k32.shape[:-2] + k32.shape[-1:], dtype=np.float32)
         ks = k32
-    qc, qs = quantize_int8_blocks(q32, BLKQ)
+    qc, qs = quantize_int8_blocks(q32, q_group)
     kc, ksc = quantize_int8_blocks(ks, BLKK)
     return dict(q_i8=qc, q_scale=qs, k_i8=kc, k_scale=ksc, k_mean=mean)
 

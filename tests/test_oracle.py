@@ -125,6 +125,65 @@ def test_int8_ties_go_to_even():
     assert codes[0, 0].tolist() == [127, 0, 2, 2, 0, -2, -2, 4]
 
 
+@pytest.mark.parametrize("q_group", [1, 32])
+def test_q_group_scales_cover_their_runs(q_group):
+    # each scale belongs to exactly the q_group consecutive tokens it covers:
+    # its group's amax lands on code 127, and changing a token moves only
+    # its own group's scale
+    g = np.random.default_rng(11)
+    n = 100
+    q = torch.from_numpy((g.standard_normal((1, 2, n, 64)) *
+                          np.exp(g.uniform(-3, 3, (1, 2, n, 1)))).astype(np.float32)).half()
+    k = torch.from_numpy(g.standard_normal((1, 2, n, 64)).astype(np.float32)).half()
+    z = O.quantize_qk(q, k, q_group=q_group)
+    qs = z["q_scale"]
+    assert qs.shape == (1, 2, -(-n // q_group))
+    q32 = q.float().numpy()
+    for h in range(2):
+        for i in range(qs.shape[2]):
+            rows = slice(i * q_group, min((i + 1) * q_group, n))
+            c = z["q_i8"][0, h, rows].astype(np.int64)
+            assert np.abs(c).max() == 127
+            assert abs(np.abs(q32[0, h, rows]).max() / float(qs[0, h, i]) - 127) < 127 * 2 ** -22
+    q2 = q.clone()
+    q2[0, 1, 70] = 500.0          # above every |q| of the input: its group's new amax
+    z2 = O.quantize_qk(q2, k, q_group=q_group)
+    changed = np.nonzero(z2["q_scale"] != qs)
+    assert set(zip(*changed)) == {(0, 1, 70 // q_group)}
+
+
+def test_q_group_128_is_the_block_quantizer():
+    g = np.random.default_rng(12)
+    q = torch.from_numpy(g.standard_normal((1, 1, 300, 64)).astype(np.float32)).half()
+    k = torch.from_numpy(g.standard_normal((1, 1, 300, 64)).astype(np.float32)).half()
+    a = O.quantize_qk(q, k)
+    b = O.quantize_qk(q, k, q_group=128)
+    assert (a["q_i8"] == b["q_i8"]).all() and (a["q_scale"] == b["q_scale"]).all()
+    with pytest.raises(AssertionError):
+        O.quantize_qk(q, k, q_group=16)
+
+
+def test_q_group_score_error_ordering():
+    # Table 6 of the detail page: finer Q groups quantize more accurately
+    # (per-token/per-thread below per-block).  On queries whose magnitudes
+    # vary from token to token, the dequantized scores' relative L1 error
+    # falls strictly as the group shrinks from 128 to 32 to 1 token.
+    g = np.random.default_rng(13)
+    n, d = 256, 64
+    q = torch.from_numpy((g.standard_normal((1, 1, n, d)) *
+                          np.exp(g.uniform(-2, 2, (1, 1, n, 1)))).astype(np.float32)).half()
+    k = torch.from_numpy(g.standard_normal((1, 1, n, d)).astype(np.float32)).half()
+    s_ref = q.double().numpy()[0, 0] @ k.double().numpy()[0, 0].T
+    err = {}
+    for qg in (128, 32, 1):
+        z = O.quantize_qk(q, k, smooth_k=False, q_group=qg)
+        qd = z["q_i8"][0, 0].astype(np.float64) * z["q_scale"][0, 0, np.arange(n) // qg, None]
+        kd = z["k_i8"][0, 0].astype(np.float64) * z["k_scale"][0, 0, np.arange(n) // 64, None]
+        err[qg] = np.abs(qd @ kd.T - s_ref).sum() / np.abs(s_ref).sum()
+    assert err[1] < err[32] < err[128]
+    assert err[1] < 0.5 * err[128]
+
+
 # --------------------------------------------------------------------- Smooth K
 
 def test_k_mean_equals_fsum():
@@ -347,6 +406,27 @@ def _sample_check(name, heads, nrows, seed):
     m = O.metrics(oq[sel[:, 0], sel[:, 1]], oe[sel[:, 0], sel[:, 1]])
     assert m["cos"] >= 0.998, m
     return m
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_per_token_q_scales_closed_form_matches_recursion(causal):
+    # the dequantization reads the scale of the query's own group: with one
+    # scale per token the closed form and the literal recursion agree
+    g = np.random.default_rng(14)
+    n, d = 40, 8
+    q = torch.from_numpy((g.standard_normal((1, 2, n, d)) *
+                          np.exp(g.uniform(-2, 2, (1, 2, n, 1)))).astype(np.float32)).half()
+    k = torch.from_numpy(g.standard_normal((1, 2, n, d)).astype(np.float32) + 1).half()
+    v = torch.from_numpy(g.standard_normal((1, 2, n, d)).astype(np.float32)).half()
+    qz = O.quantize_qk(q, k, q_group=1)
+    vz = O.quantize_v(v)
+    kw = dict(causal=causal, sm_scale=0.4, kv_tile=16, blkq=1)
+    a = O.attn_quant(qz["q_i8"], qz["q_scale"], qz["k_i8"], qz["k_scale"], vz["v_f8"],
+                     vz["v_scale"], **kw)
+    for h in range(2):
+        r = O.attn_quant_recursive(qz["q_i8"], qz["q_scale"], qz["k_i8"], qz["k_scale"],
+                                   vz["v_f8"], vz["v_scale"], h=h, **kw)
+        assert np.abs(a[0, h] - r).max() < 1e-12
 
 
 def test_quantized_vs_exact_tiny_full():
