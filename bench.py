@@ -107,6 +107,9 @@ def main():
     ap.add_argument("--all", action="store_true",
                     help="time every configuration (tiny, llm_prefill, video_dit, sweep N=1K..32K, "
                          "gqa_long) and print one JSON line each instead of the single result line")
+    ap.add_argument("--q-group", type=int, default=128, choices=(128, 32, 1),
+                    help="Q tokens per INT8 scale: 128 per block (default), 32 per wave, "
+                         "1 per query")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB (3 times), "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -142,10 +145,11 @@ def main():
                                                         (1024, 2048, 4096, 8192, 16384, 32768)]
         names.append("gqa_long")
         for name in names:
-            r = run_config(W.get(name), max(args.steps, 5), args.warmup)
+            r = run_config(W.get(name), max(args.steps, 5), args.warmup, q_group=args.q_group)
             print(json.dumps(r), flush=True)
         return
-    res = run_config(W.get(args.config), args.steps, args.warmup, full=True)
+    res = run_config(W.get(args.config), args.steps, args.warmup, full=True,
+                     q_group=args.q_group)
     if args.lse:
         res["lse"] = run_lse(W.get(args.config), args.steps, args.warmup)
     if not args.no_cpu:
@@ -197,7 +201,7 @@ def run_lse(w, steps: int, warmup: int) -> dict:
             "attn_fwd_lse_tops": round(w.ops() / (t_al * 1e-3) / 1e12, 2)}
 
 
-def run_config(w, steps: int, warmup: int, full: bool = False) -> dict:
+def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 128) -> dict:
     """Time `steps` whole steps of workload `w` (inputs resident on the GPU)."""
     import torch
     import quantized_attention_amd as qa
@@ -206,7 +210,8 @@ def run_config(w, steps: int, warmup: int, full: bool = False) -> dict:
     t = W.generate(w)
     q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
     del t
-    plan = qa.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal, device=dev)
+    plan = qa.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal, device=dev,
+                       q_group=q_group)
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(warmup):
@@ -219,7 +224,7 @@ def run_config(w, steps: int, warmup: int, full: bool = False) -> dict:
     for s in range(steps):
         e = ev[s]
         e[0].record(stream)
-        qa.sage_quant_qk(q, k, True, out=plan.qk, workspace=plan.ws_qk)
+        qa.sage_quant_qk(q, k, True, q_group=q_group, out=plan.qk, workspace=plan.ws_qk)
         e[1].record(stream)
         qa.sage_quant_v(v, out=plan.vq, workspace=plan.ws_v)
         e[2].record(stream)
@@ -236,7 +241,8 @@ def run_config(w, steps: int, warmup: int, full: bool = False) -> dict:
     attn_tops = ops / (t_attn * 1e-3) / 1e12
     # algorithmic bytes of the quantizers: read 2 B + write 1 B per element of Q, K and V
     quant_bytes = 3 * (w.B * w.H * w.N * w.d + 2 * w.B * w.H_kv * w.N * w.d)
-    traffic = traffic_from_profile(w.name)
+    # the committed counters were taken with the default 128-token Q groups
+    traffic = traffic_from_profile(w.name) if q_group == 128 else None
 
     res = {
         "metric": "quantized attn fwd TOPS at N=32K hd128 (4BHN^2d/t); % of MFMA INT8/FP8 peak",
@@ -253,7 +259,7 @@ def run_config(w, steps: int, warmup: int, full: bool = False) -> dict:
         "data": "synthetic (seeded normals, shared K channel bias)",
         "config": {"workload": w.description, "name": w.name, "B": w.B, "H": w.H,
                    "H_kv": w.H_kv, "N": w.N, "d": w.d, "causal": w.causal,
-                   "in_dtype": w.dtype},
+                   "in_dtype": w.dtype, "q_group": q_group},
         "attn_tops": round(attn_tops, 2),
         "attn_ms": round(t_attn, 4),
         "quant_qk_ms": round(t_qk, 4),

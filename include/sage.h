@@ -5,11 +5,12 @@
  * source-analysis page's "Q/K 统一走 INT8" and without smoothing Q):
  *   1. Smooth K: subtract the per-channel mean of K over tokens
  *      (SageAttention synthesis page, Smooth K; Algorithm 1 preprocessing).
- *   2. Quantize Q per block of 128 tokens and smoothed K per block of 64
- *      tokens to INT8 with one FP32 scale per block: scale = amax / 127,
- *      code = round-half-even(x / scale) (deployment-guide page, quantization
- *      formula; block sizes b_q = 128, b_kv = 64 from the detail page's
- *      "Optimization Techniques" table).
+ *   2. Quantize Q per group of 128, 32 or 1 tokens and smoothed K per block
+ *      of 64 tokens to INT8 with one FP32 scale per group: scale = amax /
+ *      127, code = round-half-even(x / scale) (deployment-guide page,
+ *      quantization formula; block sizes b_q = 128, b_kv = 64 from the
+ *      detail page's "Optimization Techniques" table; the finer Q groups are
+ *      the per-warp / per-thread granularities, below).
  *   3. Quantize V per channel to FP8 E4M3 with one FP32 scale per channel:
  *      scale = amax / 448 (Algorithm 1's psi_V; source-analysis page: V is
  *      transposed, padded and permuted before the per-channel FP8 cast).
@@ -48,11 +49,28 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 2
+#define SAGE_ABI_VERSION 3
 
-/* Q tokens per INT8 scale, K tokens per INT8 scale. */
+/* Q tokens per INT8 scale (default), K tokens per INT8 scale. */
 #define SAGE_BLKQ 128
 #define SAGE_BLKK 64
+
+/*
+ * Q scale granularity (`q_group`: consecutive Q tokens per scale).  The
+ * SageAttention2 detail page quantizes Q per thread of the matrix-core
+ * instruction (Figure 4; Table 6: per-thread is as accurate as per-token
+ * and clearly better than per-block); the source-analysis page's
+ * quantization module lists per-block, per-warp and per-thread Q scales.
+ * Here a wave's matrix cores hold 32 queries, one per lane, so:
+ *   SAGE_QGROUP_BLOCK (128): one scale per workgroup's 128 queries;
+ *   SAGE_QGROUP_WAVE  (32):  one scale per wave's 32 queries (per-warp);
+ *   SAGE_QGROUP_TOKEN (1):   one scale per query, the lane that holds it
+ *                            (per-thread).
+ * The attention kernel costs the same for all three.
+ */
+#define SAGE_QGROUP_BLOCK 128
+#define SAGE_QGROUP_WAVE 32
+#define SAGE_QGROUP_TOKEN 1
 /* Keys per online-softmax step; also the padding unit of the FP8 V layout. */
 #define SAGE_KV_TILE 128
 
@@ -74,7 +92,7 @@ typedef enum { SAGE_FP16 = 0, SAGE_BF16 = 1 } sage_dtype;
 /* Byte sizes of every buffer the entry points take, for given shapes. */
 typedef struct {
   size_t q_i8;      /* int8  [B][H][N][d]                                       */
-  size_t q_scale;   /* float [B][H][ceil(N/128)]                                */
+  size_t q_scale;   /* float [B][H][ceil(N/q_group)]                            */
   size_t k_i8;      /* int8  [B][H_kv][N][d]                                    */
   size_t k_scale;   /* float [B][H_kv][ceil(N/64)]                              */
   size_t k_mean;    /* float [B][H_kv][d]                                       */
@@ -101,12 +119,17 @@ typedef struct {
  * leaves P in registers.)
  */
 
-/* Fill *out with buffer sizes.  Host only; touches no device. */
-sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, sage_sizes* out);
+/* Fill *out with buffer sizes (q_group: see above; else SAGE_ERR_ARG).
+ * Host only; touches no device. */
+sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, int q_group,
+                              sage_sizes* out);
 
 /*
  * Steps 1-2: smooth K and quantize Q and K to INT8.
  *   q [B][H][N][d], k [B][H_kv][N][d] in `dtype` (read only).
+ *   q_group: Q tokens per scale, SAGE_QGROUP_BLOCK / _WAVE / _TOKEN (else
+ *     SAGE_ERR_ARG); q_scale holds ceil(N / q_group) scales per head, group
+ *     i covering tokens i*q_group .. min(N, (i+1)*q_group) - 1.
  *   smooth_k: 1 = subtract the per-channel token mean of K before
  *     quantizing (the mean is the exact sum over all N tokens, divided by N
  *     and rounded to float32); 0 = no smoothing (k_mean is written as 0).
@@ -118,7 +141,7 @@ sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, sage_sizes* 
  *     contents on entry do not matter).
  */
 sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype,
-                          int B, int H, int H_kv, int N, int d, int smooth_k,
+                          int B, int H, int H_kv, int N, int d, int q_group, int smooth_k,
                           int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
                           float* k_mean, void* workspace, size_t ws_bytes, void* stream);
 
@@ -138,7 +161,8 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N
 /*
  * Step 4: the attention kernel.
  *   Inputs are the outputs of sage_quant_qk / sage_quant_v for the same
- *   shapes.  o [B][H][N][d] is written in `out_dtype` (round to nearest even).
+ *   shapes and q_group.  o [B][H][N][d] is written in `out_dtype` (round to
+ *   nearest even).
  *   causal: 1 = key j visible to query i iff j <= i; fully masked key tiles
  *     are skipped.  sm_scale: the softmax scale (> 0, finite), commonly
  *     1/sqrt(d).
@@ -148,7 +172,7 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                           const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                           void* o, sage_dtype out_dtype, int B, int H, int H_kv, int N, int d,
-                          int causal, float sm_scale, void* stream);
+                          int q_group, int causal, float sm_scale, void* stream);
 
 /*
  * Step 4 with the row log-sum-exp (the per-row softmax state a forward pass
@@ -169,8 +193,8 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
 sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                               const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                               void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
-                              int B, int H, int H_kv, int N, int d, int causal, float sm_scale,
-                              void* stream);
+                              int B, int H, int H_kv, int N, int d, int q_group, int causal,
+                              float sm_scale, void* stream);
 
 /*
  * corr[b][h][i] = sm_scale * sum_c q[b][h][i][c] * k_mean[b][h / (H/H_kv)][c]

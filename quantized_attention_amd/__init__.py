@@ -6,20 +6,24 @@ kernels; PyTorch provides device memory and the current stream.  There is no
 CPU fallback -- if the library is not built or no GPU is visible, calls fail.
 
 The method (SageAttention2 detail page, Algorithm 1, with INT8 Q/K):
-smooth K by its token mean, quantize Q (per 128 tokens) and K (per 64 tokens)
-to INT8 with FP32 scales, quantize V per channel to FP8 E4M3, then run a tiled
+smooth K by its token mean, quantize Q (per 128, 32 or 1 tokens) and K (per 64
+tokens) to INT8 with FP32 scales, quantize V per channel to FP8 E4M3, then run a tiled
 online-softmax attention with INT8 QK^T and FP8 PV (P scaled by 448).
 
 Entry points (same names as the C ABI):
-    sage_buffer_sizes(B, H, H_kv, N, d) -> dict of byte sizes
-    sage_quant_qk(q, k, smooth_k=True) -> dict(q_i8, q_scale, k_i8, k_scale, k_mean)
+    sage_buffer_sizes(B, H, H_kv, N, d, q_group=128) -> dict of byte sizes
+    sage_quant_qk(q, k, smooth_k=True, q_group=128)
+        -> dict(q_i8, q_scale, k_i8, k_scale, k_mean)
     sage_quant_v(v) -> dict(v_f8, v_scale)
     sage_attn_fwd(qk, vq, causal=..., sm_scale=..., out_dtype=...) -> o
     sage_attn_fwd_lse(qk, vq, causal=..., sm_scale=..., lse_corr=None) -> (o, lse)
     sage_lse_correction(q, k_mean, sm_scale) -> fp32 [B, H, N]
     sage_qk_int32(q_i8, k_i8, b, h) -> int32 [N, N] (diagnostic)
 and the composition ``sageattn(q, k, v, is_causal=False, sm_scale=None,
-return_lse=False)``.
+smooth_k=True, return_lse=False, q_group=128)``.  ``q_group`` is the number of
+consecutive Q tokens per scale: 128 (per block), 32 (per wave, the per-warp
+granularity) or 1 (per query, the per-thread granularity); the attention
+entry points read it from the length of ``q_scale``.
 """
 from __future__ import annotations
 
@@ -31,9 +35,10 @@ import torch
 
 __all__ = ["SageError", "library_path", "load_library", "sage_buffer_sizes", "sage_quant_qk",
            "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse", "sage_lse_correction",
-           "sage_qk_int32", "sageattn", "SagePlan", "BLKQ", "BLKK", "KV_TILE"]
+           "sage_qk_int32", "sageattn", "SagePlan", "BLKQ", "BLKK", "KV_TILE", "Q_GROUPS"]
 
 BLKQ, BLKK, KV_TILE = 128, 64, 128
+Q_GROUPS = (128, 32, 1)   # Q tokens per scale: per block, per wave, per query
 _FP16, _BF16 = 0, 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -70,13 +75,13 @@ def load_library():
     lib.sage_abi_version.restype = i
     lib.sage_status_str.argtypes = [i]
     lib.sage_status_str.restype = ctypes.c_char_p
-    lib.sage_buffer_sizes.argtypes = [i, i, i, i, i, ctypes.POINTER(_Sizes)]
-    lib.sage_quant_qk.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sage_buffer_sizes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(_Sizes)]
+    lib.sage_quant_qk.argtypes = [vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sage_quant_v.argtypes = [vp, i, i, i, i, i, vp, vp, vp, sz, vp]
-    lib.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+    lib.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                   ctypes.c_float, vp]
     lib.sage_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i,
-                                      ctypes.c_float, vp]
+                                      i, ctypes.c_float, vp]
     lib.sage_lse_correction.argtypes = [vp, i, vp, i, i, i, i, i, ctypes.c_float, vp, vp]
     lib.sage_qk_int32.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp]
     for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_quant_v", "sage_attn_fwd",
@@ -118,14 +123,26 @@ def _need_gpu(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
-def sage_buffer_sizes(B: int, H: int, H_kv: int, N: int, d: int) -> dict:
+def sage_buffer_sizes(B: int, H: int, H_kv: int, N: int, d: int, q_group: int = BLKQ) -> dict:
     s = _Sizes()
-    _check(load_library().sage_buffer_sizes(B, H, H_kv, N, d, ctypes.byref(s)), "sage_buffer_sizes")
+    _check(load_library().sage_buffer_sizes(B, H, H_kv, N, d, q_group, ctypes.byref(s)),
+           "sage_buffer_sizes")
     return {n: getattr(s, n) for n, _ in _Sizes._fields_}
 
 
-def _alloc_qk(B, H, H_kv, N, d, device):
-    nq, nk = -(-N // BLKQ), -(-N // BLKK)
+def _q_group_of(q_scale: torch.Tensor, N: int) -> int:
+    """The Q granularity a q_scale tensor was written for.  Where two
+    groupings give the same length (N <= 32) every query reads scale 0 under
+    either, so the choice does not matter."""
+    for g in Q_GROUPS:
+        if q_scale.shape[-1] == -(-N // g):
+            return g
+    raise ValueError(f"q_scale has {q_scale.shape[-1]} scales per head; expected "
+                     f"ceil(N / g) for g in {Q_GROUPS} with N = {N}")
+
+
+def _alloc_qk(B, H, H_kv, N, d, device, q_group=BLKQ):
+    nq, nk = -(-N // q_group), -(-N // BLKK)
     return dict(
         q_i8=torch.empty((B, H, N, d), dtype=torch.int8, device=device),
         q_scale=torch.empty((B, H, nq), dtype=torch.float32, device=device),
@@ -143,9 +160,10 @@ def _alloc_v(B, H_kv, N, d, device):
     )
 
 
-def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *, out=None,
-                  workspace=None, stream=None) -> dict:
-    """Smooth K and quantize Q, K to INT8 (see sage.h for exact semantics)."""
+def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *,
+                  q_group: int = BLKQ, out=None, workspace=None, stream=None) -> dict:
+    """Smooth K and quantize Q (q_group tokens per scale), K to INT8 (see sage.h
+    for exact semantics)."""
     _need_gpu(q, k)
     if q.dtype != k.dtype:
         raise TypeError("q and k must share a dtype")
@@ -153,12 +171,16 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *, ou
     H_kv = k.shape[1]
     if k.shape != (B, H_kv, N, d):
         raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
-    out = out or _alloc_qk(B, H, H_kv, N, d, q.device)
+    if q_group not in Q_GROUPS:
+        raise ValueError(f"q_group must be one of {Q_GROUPS}")
+    out = out or _alloc_qk(B, H, H_kv, N, d, q.device, q_group)
+    if out["q_scale"].numel() != B * H * -(-N // q_group):
+        raise ValueError("out['q_scale'] does not hold ceil(N / q_group) scales per head")
     if workspace is None and smooth_k:
         ws = sage_buffer_sizes(B, H, H_kv, N, d)["ws_quant_qk"]
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     st = load_library().sage_quant_qk(
-        q.data_ptr(), k.data_ptr(), _dt(q.dtype), B, H, H_kv, N, d, int(bool(smooth_k)),
+        q.data_ptr(), k.data_ptr(), _dt(q.dtype), B, H, H_kv, N, d, q_group, int(bool(smooth_k)),
         out["q_i8"].data_ptr(), out["q_scale"].data_ptr(), out["k_i8"].data_ptr(),
         out["k_scale"].data_ptr(), out["k_mean"].data_ptr(), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(),
@@ -196,7 +218,8 @@ def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
     st = load_library().sage_attn_fwd(
         q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
         vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
-        B, H, H_kv, N, d, int(bool(causal)), float(sm_scale), _stream(stream, q_i8.device))
+        B, H, H_kv, N, d, _q_group_of(qk["q_scale"], N), int(bool(causal)), float(sm_scale),
+        _stream(stream, q_i8.device))
     _check(st, "sage_attn_fwd")
     return out
 
@@ -223,8 +246,8 @@ def sage_attn_fwd_lse(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
     st = load_library().sage_attn_fwd_lse(
         q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
         vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
-        lse.data_ptr(), _ptr(lse_corr), B, H, H_kv, N, d, int(bool(causal)), float(sm_scale),
-        _stream(stream, q_i8.device))
+        lse.data_ptr(), _ptr(lse_corr), B, H, H_kv, N, d, _q_group_of(qk["q_scale"], N),
+        int(bool(causal)), float(sm_scale), _stream(stream, q_i8.device))
     _check(st, "sage_attn_fwd_lse")
     return out, lse
 
@@ -259,13 +282,13 @@ def sage_qk_int32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, *,
 
 
 def sageattn(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
-             smooth_k: bool = True, return_lse: bool = False):
+             smooth_k: bool = True, return_lse: bool = False, q_group: int = BLKQ):
     """The whole forward pass: quantize Q/K/V, then the attention kernel.
     With return_lse, also the row log-sum-exp of the logits sm_scale q . k
     (corrected for the smoothing of K); returns (o, lse)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
-    qk = sage_quant_qk(q, k, smooth_k)
+    qk = sage_quant_qk(q, k, smooth_k, q_group=q_group)
     vq = sage_quant_v(v)
     if not return_lse:
         return sage_attn_fwd(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype)
@@ -277,19 +300,21 @@ def sageattn(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
 class SagePlan:
     """Preallocated buffers for repeated calls on fixed shapes (no allocation per call)."""
 
-    def __init__(self, B, H, H_kv, N, d, dtype, causal, sm_scale=None, device="cuda"):
+    def __init__(self, B, H, H_kv, N, d, dtype, causal, sm_scale=None, device="cuda",
+                 q_group=BLKQ):
         self.shape = (B, H, H_kv, N, d)
-        self.dtype, self.causal = dtype, causal
+        self.dtype, self.causal, self.q_group = dtype, causal, q_group
         self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
-        sz = sage_buffer_sizes(B, H, H_kv, N, d)
-        self.qk = _alloc_qk(B, H, H_kv, N, d, device)
+        sz = sage_buffer_sizes(B, H, H_kv, N, d, q_group)
+        self.qk = _alloc_qk(B, H, H_kv, N, d, device, q_group)
         self.vq = _alloc_v(B, H_kv, N, d, device)
         self.ws_qk = torch.empty(max(sz["ws_quant_qk"], 16), dtype=torch.uint8, device=device)
         self.ws_v = torch.empty(max(sz["ws_quant_v"], 16), dtype=torch.uint8, device=device)
         self.o = torch.empty((B, H, N, d), dtype=dtype, device=device)
 
     def quant(self, q, k, v, stream=None):
-        sage_quant_qk(q, k, True, out=self.qk, workspace=self.ws_qk, stream=stream)
+        sage_quant_qk(q, k, True, q_group=self.q_group, out=self.qk, workspace=self.ws_qk,
+                      stream=stream)
         sage_quant_v(v, out=self.vq, workspace=self.ws_v, stream=stream)
 
     def attn(self, stream=None):

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_f8, const float* __restrict__ v_scale,
     void* __restrict__ out, float* __restrict__ lse, const float* __restrict__ lse_corr, int H,
-    int H_kv, int N, float sm_log2, int nqt, int total) {
+    int H_kv, int N, float sm_log2, int qg_shift, int nqt, int total) {
   constexpr int NKC = D / 32;                 // 32-wide channel chunks
   constexpr int KBYTES = kKvTile * D;         // K tile bytes (== V tile bytes)
   __shared__ __attribute__((aligned(16))) char lds[2][2 * KBYTES];
@@ -71,7 +71,10 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
   for (int kc = 0; kc < NKC; ++kc)
     qf[kc] = (qi < N) ? *reinterpret_cast<const i32x4*>(qh + (size_t)qi * D + kc * 32 + half * 16)
                       : i32x4{0, 0, 0, 0};
-  const float cq = q_scale[(size_t)(b * H + h) * nqt + qt] * sm_log2;
+  // this lane's Q scale: groups of 2^qg_shift consecutive queries (128, 32
+  // or 1; rows past N read the last row's group)
+  const int nqs = ((N - 1) >> qg_shift) + 1;
+  const float cq = q_scale[(size_t)(b * H + h) * nqs + (min(qi, N - 1) >> qg_shift)] * sm_log2;
 
   f32x16 acc_o[NKC];
 #pragma unroll
@@ -90,13 +93,17 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
   // the diagonal (causal) or past N; only the last tile can.
   // The exponent argument takes one FMA on the biased float of the int32
   // sum when every dequant factor ck = cq * k_scale of the tiles this
-  // workgroup visits is <= kFastCk; otherwise kMagic is subtracted first.
-  // Decided once per workgroup, so each path is a loop of its own.
+  // wave visits is <= kFastCk; otherwise kMagic is subtracted first.
+  // Decided once per wave, so each path is a loop of its own (both paths
+  // pass the same barriers).
   float kmax = 0.f;
   for (int i = lane; i < min(nkb, ntiles * (kKvTile / kBlkK)); i += 64) kmax = fmaxf(kmax, ksc[i]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, o));
-  const bool fast_wg = cq * kmax <= kFastCk;
+  float cmax = cq;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, o));
+  const bool fast_wg = cmax * kmax <= kFastCk;
 
   auto step = [&](int t, auto mask_tag, auto fast_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -378,9 +385,11 @@ __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                                 void* o, int bf16_out, float* lse, const float* lse_corr, int B,
-                                int H, int H_kv, int N, int d, int causal, float sm_scale,
-                                hipStream_t stream) {
+                                int H, int H_kv, int N, int d, int q_group, int causal,
+                                float sm_scale, hipStream_t stream) {
   using namespace sage;
+  const int qg_shift = q_group == kBlkQ ? 7 : q_group == kWaveQ ? 5 : q_group == 1 ? 0 : -1;
+  if (qg_shift < 0) return hipErrorInvalidValue;
   const int nqt = (N + kBlockQ - 1) / kBlockQ;
   const long long total = (long long)B * H * nqt;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
@@ -390,7 +399,7 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
   if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB) {                                 \
     hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB>), grid, block, 0, stream, q_i8, q_scale,     \
                        k_i8, k_scale, v_f8, v_scale, o, lse, lse_corr, H, H_kv, N, sm_log2,      \
-                       nqt, (int)total);                                                         \
+                       qg_shift, nqt, (int)total);                                               \
     return hipGetLastError();                                                                    \
   }
   SAGE_ATTN_CASE(64, false, false)

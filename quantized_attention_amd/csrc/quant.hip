@@ -5,9 +5,12 @@
 //       SageAttention synthesis page's Smooth K, Algorithm 1 preprocessing
 //       on the SageAttention2 detail page) or the absolute max of V (the
 //       per-channel FP8 scale of Algorithm 1's psi_V).
-//   quant_int8        : per-block INT8 quantization of Q (128 tokens) and of
-//       smoothed K (64 tokens): scale = amax/127, code = RNE(x/scale)
+//   quant_int8        : per-block INT8 quantization of Q (128 or 32 tokens)
+//       and of smoothed K (64 tokens): scale = amax/127, code = RNE(x/scale)
 //       (deployment-guide page, quantization formula).
+//   quant_int8_tok    : the same rules with one scale per Q token (the
+//       per-thread granularity of the SageAttention2 detail page, Figure 4,
+//       when each matrix-core lane holds one query).
 //   quant_v_fp8       : per-channel FP8 E4M3 quantization of V, written
 //       transposed and key-permuted in the fragment layout of sage.h.
 //
@@ -228,6 +231,56 @@ __global__ __launch_bounds__(kQuantThreads) void quant_int8(const void* __restri
     emit(std::false_type{});
 }
 
+// Per-token INT8 quantization: one scale per token.  The D/8 consecutive
+// threads of a token each load 8 channels; the token's amax is reduced by
+// xor-shuffles among them.  grid (ceil(N / tokens per workgroup), B*heads).
+template <int D, bool BF16>
+__global__ __launch_bounds__(kQuantThreads) void quant_int8_tok(const void* __restrict__ x,
+                                                                int8_t* __restrict__ codes,
+                                                                float* __restrict__ scales, int N) {
+  constexpr int TPR = D / 8;
+  constexpr int TPB = kQuantThreads / TPR;   // tokens per workgroup
+  static_assert(TPR <= 64 && (TPR & (TPR - 1)) == 0, "a token's threads share one wave");
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int row = blockIdx.x * TPB + tid / TPR, cg = tid % TPR;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
+  float v[8];
+  float amax = 0.f;
+  if (row < N) {
+    unpack8<BF16>(*reinterpret_cast<const uint4*>(xs + (size_t)row * D + cg * 8), v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const float sc = amax / 127.0f;            // IEEE division
+  auto emit = [&](auto fast_tag) __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    uint32_t w[2] = {0u, 0u};
+    const float rs = FAST ? 1.0f / sc : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q = 0.f;
+      if (FAST || sc > 0.f) {
+        const float y = FAST ? div_rn(v[i], sc, rs) : v[i] / sc;
+        q = fminf(fmaxf(__builtin_rintf(y), -127.f), 127.f);
+      }
+      w[i / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (i % 4));
+    }
+    *reinterpret_cast<uint2*>(codes + (size_t)bh * N * D + (size_t)row * D + cg * 8) =
+        uint2{w[0], w[1]};
+  };
+  if (row < N) {
+    if (cg == 0) scales[(size_t)bh * N + row] = sc;
+    // the three-operation division when every token of the wave allows it
+    if (__builtin_amdgcn_ballot_w64(!(sc >= kDivRnMinScale)) == 0) emit(std::true_type{});
+    else emit(std::false_type{});
+  }
+}
+
 // ---------------------------------------------------------------------------
 // FP8 V.  Each 16-byte chunk of the v_f8 layout (sage.h) holds one channel
 // and 16 keys, so one wave writes the 64 chunks (kb, cb, p, L = lane) of a
@@ -340,19 +393,33 @@ size_t sage_ws_quant_v_bytes(int B, int H_kv, int N, int d) {
 
 template <int D, bool BF16>
 static hipError_t quant_qk_impl(const void* q, const void* k, int B, int H, int H_kv, int N,
-                                int smooth_k, int8_t* q_i8, float* q_scale, int8_t* k_i8,
-                                float* k_scale, float* k_mean, void* ws, hipStream_t st) {
+                                int q_group, int smooth_k, int8_t* q_i8, float* q_scale,
+                                int8_t* k_i8, float* k_scale, float* k_mean, void* ws,
+                                hipStream_t st) {
   using namespace sage;
   const int nc = nchunks(N);
-  const int nbq = (N + kBlkQ - 1) / kBlkQ, nbk = (N + kBlkK - 1) / kBlkK;
+  const int nbk = (N + kBlkK - 1) / kBlkK;
   if (smooth_k) {
     hipLaunchKernelGGL((colstats_partial<D, BF16, 0>), dim3(nc, B * H_kv), dim3(kQuantThreads), 0,
                        st, k, ws, N, nc);
   }
   hipLaunchKernelGGL((colstats_final<D, 0>), dim3(B * H_kv), dim3(kQuantThreads), 0, st, ws, k_mean,
                      N, nc, smooth_k);
-  hipLaunchKernelGGL((quant_int8<D, kBlkQ, BF16, false>), dim3(nbq, B * H), dim3(kQuantThreads), 0,
-                     st, q, nullptr, q_i8, q_scale, N, nbq);
+  if (q_group == kBlkQ) {
+    const int nbq = (N + kBlkQ - 1) / kBlkQ;
+    hipLaunchKernelGGL((quant_int8<D, kBlkQ, BF16, false>), dim3(nbq, B * H), dim3(kQuantThreads),
+                       0, st, q, nullptr, q_i8, q_scale, N, nbq);
+  } else if (q_group == kWaveQ) {
+    const int nbq = (N + kWaveQ - 1) / kWaveQ;
+    hipLaunchKernelGGL((quant_int8<D, kWaveQ, BF16, false>), dim3(nbq, B * H), dim3(kQuantThreads),
+                       0, st, q, nullptr, q_i8, q_scale, N, nbq);
+  } else if (q_group == 1) {
+    constexpr int tpb = kQuantThreads / (D / 8);
+    hipLaunchKernelGGL((quant_int8_tok<D, BF16>), dim3((N + tpb - 1) / tpb, B * H),
+                       dim3(kQuantThreads), 0, st, q, q_i8, q_scale, N);
+  } else {
+    return hipErrorInvalidValue;
+  }
   if (smooth_k)
     hipLaunchKernelGGL((quant_int8<D, kBlkK, BF16, true>), dim3(nbk, B * H_kv),
                        dim3(kQuantThreads), 0, st, k, k_mean, k_i8, k_scale, N, nbk);
@@ -379,15 +446,18 @@ static hipError_t quant_v_impl(const void* v, int B, int H_kv, int N, uint8_t* v
 }
 
 hipError_t sage_launch_quant_qk(const void* q, const void* k, int bf16, int B, int H, int H_kv,
-                                int N, int d, int smooth_k, int8_t* q_i8, float* q_scale,
-                                int8_t* k_i8, float* k_scale, float* k_mean, void* ws,
-                                hipStream_t st) {
-  if (d == 64)
-    return bf16 ? quant_qk_impl<64, true>(q, k, B, H, H_kv, N, smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st)
-                : quant_qk_impl<64, false>(q, k, B, H, H_kv, N, smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
-  if (d == 128)
-    return bf16 ? quant_qk_impl<128, true>(q, k, B, H, H_kv, N, smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st)
-                : quant_qk_impl<128, false>(q, k, B, H, H_kv, N, smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
+                                int N, int d, int q_group, int smooth_k, int8_t* q_i8,
+                                float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                                void* ws, hipStream_t st) {
+#define SAGE_QQK(DD, BB)                                                                       \
+  if (d == DD && (bf16 != 0) == BB)                                                            \
+    return quant_qk_impl<DD, BB>(q, k, B, H, H_kv, N, q_group, smooth_k, q_i8, q_scale, k_i8,  \
+                                 k_scale, k_mean, ws, st);
+  SAGE_QQK(64, false)
+  SAGE_QQK(64, true)
+  SAGE_QQK(128, false)
+  SAGE_QQK(128, true)
+#undef SAGE_QQK
   return hipErrorInvalidValue;
 }
 

@@ -9,16 +9,16 @@
 #include "sage.h"
 
 hipError_t sage_launch_quant_qk(const void* q, const void* k, int bf16, int B, int H, int H_kv,
-                                int N, int d, int smooth_k, int8_t* q_i8, float* q_scale,
-                                int8_t* k_i8, float* k_scale, float* k_mean, void* ws,
-                                hipStream_t st);
+                                int N, int d, int q_group, int smooth_k, int8_t* q_i8,
+                                float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                                void* ws, hipStream_t st);
 hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, int d,
                                uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st);
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                                 void* o, int bf16_out, float* lse, const float* lse_corr, int B,
-                                int H, int H_kv, int N, int d, int causal, float sm_scale,
-                                hipStream_t stream);
+                                int H, int H_kv, int N, int d, int q_group, int causal,
+                                float sm_scale, hipStream_t stream);
 hipError_t sage_launch_lse_correction(const void* q, int bf16, const float* k_mean, int B, int H,
                                       int H_kv, int N, int d, float sm_scale, float* corr,
                                       hipStream_t st);
@@ -44,6 +44,10 @@ sage_status check_shape(int B, int H, int H_kv, int N, int d) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+bool valid_q_group(int g) {
+  return g == SAGE_QGROUP_BLOCK || g == SAGE_QGROUP_WAVE || g == SAGE_QGROUP_TOKEN;
+}
+
 sage_status from_hip(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
 }  // namespace
@@ -68,12 +72,14 @@ const char* sage_status_str(sage_status s) {
   return "unknown status";
 }
 
-sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, sage_sizes* out) {
+sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, int q_group,
+                              sage_sizes* out) {
   if (!out) return SAGE_ERR_NULL;
   const sage_status st = check_shape(B, H, H_kv, N, d);
   if (st != SAGE_OK) return st;
-  const size_t b = B, h = H, hk = H_kv, n = N, dd = d;
-  const size_t nq = (n + SAGE_BLKQ - 1) / SAGE_BLKQ, nk = (n + SAGE_BLKK - 1) / SAGE_BLKK;
+  if (!valid_q_group(q_group)) return SAGE_ERR_ARG;
+  const size_t b = B, h = H, hk = H_kv, n = N, dd = d, qg = q_group;
+  const size_t nq = (n + qg - 1) / qg, nk = (n + SAGE_BLKK - 1) / SAGE_BLKK;
   const size_t npad = (n + SAGE_KV_TILE - 1) / SAGE_KV_TILE * SAGE_KV_TILE;
   out->q_i8 = b * h * n * dd;
   out->q_scale = b * h * nq * sizeof(float);
@@ -89,21 +95,22 @@ sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, sage_sizes* 
 }
 
 sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype, int B, int H, int H_kv,
-                          int N, int d, int smooth_k, int8_t* q_i8, float* q_scale, int8_t* k_i8,
-                          float* k_scale, float* k_mean, void* workspace, size_t ws_bytes,
-                          void* stream) {
+                          int N, int d, int q_group, int smooth_k, int8_t* q_i8, float* q_scale,
+                          int8_t* k_i8, float* k_scale, float* k_mean, void* workspace,
+                          size_t ws_bytes, void* stream) {
   if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean) return SAGE_ERR_NULL;
   sage_status st = check_shape(B, H, H_kv, N, d);
   if (st != SAGE_OK) return st;
   if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!valid_q_group(q_group)) return SAGE_ERR_ARG;
   if (smooth_k != 0 && smooth_k != 1) return SAGE_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8)) return SAGE_ERR_ALIGN;
   if (smooth_k) {
     if (!workspace) return SAGE_ERR_WORKSPACE;
     if (ws_bytes < sage_ws_quant_qk_bytes(B, H_kv, N, d)) return SAGE_ERR_WORKSPACE;
   }
-  return from_hip(sage_launch_quant_qk(q, k, dtype == SAGE_BF16, B, H, H_kv, N, d, smooth_k, q_i8,
-                                       q_scale, k_i8, k_scale, k_mean, workspace,
+  return from_hip(sage_launch_quant_qk(q, k, dtype == SAGE_BF16, B, H, H_kv, N, d, q_group,
+                                       smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, workspace,
                                        (hipStream_t)stream));
 }
 
@@ -124,37 +131,39 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                           const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                           void* o, sage_dtype out_dtype, int B, int H, int H_kv, int N, int d,
-                          int causal, float sm_scale, void* stream) {
+                          int q_group, int causal, float sm_scale, void* stream) {
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8 || !v_scale || !o) return SAGE_ERR_NULL;
   sage_status st = check_shape(B, H, H_kv, N, d);
   if (st != SAGE_OK) return st;
   if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!valid_q_group(q_group)) return SAGE_ERR_ARG;
   if (causal != 0 && causal != 1) return SAGE_ERR_ARG;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
     return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, o,
                                        out_dtype == SAGE_BF16, nullptr, nullptr, B, H, H_kv, N,
-                                       d, causal, sm_scale, (hipStream_t)stream));
+                                       d, q_group, causal, sm_scale, (hipStream_t)stream));
 }
 
 sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                               const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                               void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
-                              int B, int H, int H_kv, int N, int d, int causal, float sm_scale,
-                              void* stream) {
+                              int B, int H, int H_kv, int N, int d, int q_group, int causal,
+                              float sm_scale, void* stream) {
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8 || !v_scale || !o || !lse)
     return SAGE_ERR_NULL;
   sage_status st = check_shape(B, H, H_kv, N, d);
   if (st != SAGE_OK) return st;
   if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!valid_q_group(q_group)) return SAGE_ERR_ARG;
   if (causal != 0 && causal != 1) return SAGE_ERR_ARG;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
     return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, o,
                                        out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d,
-                                       causal, sm_scale, (hipStream_t)stream));
+                                       q_group, causal, sm_scale, (hipStream_t)stream));
 }
 
 sage_status sage_lse_correction(const void* q, sage_dtype dtype, const float* k_mean, int B, int H,

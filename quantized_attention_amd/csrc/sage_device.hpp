@@ -19,13 +19,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBlkQ = 128;     // Q tokens per INT8 scale
+constexpr int kBlkQ = 128;     // Q tokens per INT8 scale (the default Q granularity)
 constexpr int kBlkK = 64;      // K tokens per INT8 scale
 constexpr int kKvTile = 128;   // keys per online-softmax step / V tile
 constexpr int kWaveQ = 32;     // queries per wave (one 32-wide MFMA column block)
 constexpr int kWaves = 4;      // waves per workgroup
 constexpr int kBlockQ = kWaveQ * kWaves;   // queries per workgroup (== kBlkQ)
-static_assert(kBlockQ == kBlkQ, "one Q scale per workgroup");
+static_assert(kBlockQ == kBlkQ, "a 128-token Q scale block is one workgroup's queries");
+static_assert(kBlkQ == 1 << 7 && kWaveQ == 1 << 5, "Q scale groups are shifts of the query index");
 
 // 1.5 * 2^23: for |n| < 2^22 the float with bits (0x4B400000 + n) equals
 // 12582912 + n exactly.  Seeding the INT8 accumulator with these bits makes

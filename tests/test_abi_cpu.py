@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
             "sage_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sage_abi_version() == 2
+    assert lib.sage_abi_version() == 3
 
 
 def test_status_strings():
@@ -39,12 +39,13 @@ def test_status_strings():
     assert lib.sage_status_str(0) == b"ok"
 
 
+@pytest.mark.parametrize("q_group", [128, 32, 1])
 @pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 256, 64), (4, 32, 8, 17550, 128),
                                           (1, 1, 1, 1, 64), (2, 6, 3, 129, 128)])
-def test_buffer_sizes(B, H, H_kv, N, d):
-    s = qa.sage_buffer_sizes(B, H, H_kv, N, d)
+def test_buffer_sizes(B, H, H_kv, N, d, q_group):
+    s = qa.sage_buffer_sizes(B, H, H_kv, N, d, q_group)
     assert s["q_i8"] == B * H * N * d
-    assert s["q_scale"] == 4 * B * H * math.ceil(N / 128)
+    assert s["q_scale"] == 4 * B * H * math.ceil(N / q_group)
     assert s["k_i8"] == B * H_kv * N * d
     assert s["k_scale"] == 4 * B * H_kv * math.ceil(N / 64)
     assert s["k_mean"] == s["v_scale"] == 4 * B * H_kv * d
@@ -58,6 +59,7 @@ def test_buffer_sizes(B, H, H_kv, N, d):
     ((0, 2, 2, 256, 64), 2), ((1, 2, 2, 0, 64), 2), ((1, 0, 1, 256, 64), 2),
     ((1, 2, 2, 256, 96), 3), ((1, 2, 2, 256, 256), 3), ((1, 6, 4, 256, 64), 4),
     ((1, 70000, 1, 16, 64), 2), ((64, 512, 512, 1 << 30, 128), 2),
+    ((1, 2, 2, 256, 64, 64), 6), ((1, 2, 2, 256, 64, 0), 6), ((1, 2, 2, 256, 64, -32), 6),
 ])
 def test_buffer_sizes_rejects(args, code):
     with pytest.raises(qa.SageError) as e:
@@ -66,7 +68,7 @@ def test_buffer_sizes_rejects(args, code):
 
 
 def _qk(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, dt=0, B=1, H=2, H_kv=2, N=256, d=64, smooth=1, q_i8=FAKE,
+    a = dict(q=FAKE, k=FAKE, dt=0, B=1, H=2, H_kv=2, N=256, d=64, qg=128, smooth=1, q_i8=FAKE,
              q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, ws=FAKE, ws_bytes=1 << 20,
              stream=None)
     a.update(kw)
@@ -82,15 +84,15 @@ def _v(lib, **kw):
 
 def _attn(lib, **kw):
     a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, o=FAKE,
-             dt=0, B=1, H=2, H_kv=2, N=256, d=64, causal=0, sm_scale=0.125, stream=None)
+             dt=0, B=1, H=2, H_kv=2, N=256, d=64, qg=128, causal=0, sm_scale=0.125, stream=None)
     a.update(kw)
     return lib.sage_attn_fwd(*a.values())
 
 
 def _attn_lse(lib, **kw):
     a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, o=FAKE,
-             dt=0, lse=FAKE, corr=None, B=1, H=2, H_kv=2, N=256, d=64, causal=0, sm_scale=0.125,
-             stream=None)
+             dt=0, lse=FAKE, corr=None, B=1, H=2, H_kv=2, N=256, d=64, qg=128, causal=0,
+             sm_scale=0.125, stream=None)
     a.update(kw)
     return lib.sage_attn_fwd_lse(*a.values())
 
@@ -112,6 +114,7 @@ def _qk32(lib, **kw):
     (dict(q=None), 1), (dict(k_mean=None), 1), (dict(B=0), 2), (dict(N=-5), 2),
     (dict(d=32), 3), (dict(H=3), 4), (dict(dt=2), 5), (dict(smooth=2), 6),
     (dict(q=FAKE + 8), 9), (dict(k_i8=FAKE + 4), 9), (dict(ws=None), 7), (dict(ws_bytes=1023), 7),
+    (dict(qg=64), 6), (dict(qg=0), 6), (dict(qg=2), 6),
 ])
 def test_quant_qk_rejects(kw, code):
     assert _qk(qa.load_library(), **kw) == code
@@ -134,7 +137,7 @@ def test_quant_v_rejects(kw, code):
     (dict(o=None), 1), (dict(v_scale=None), 1), (dict(H_kv=0), 2), (dict(d=16), 3),
     (dict(H=4, H_kv=3), 4), (dict(dt=7), 5), (dict(causal=3), 6), (dict(sm_scale=0.0), 6),
     (dict(sm_scale=-1.0), 6), (dict(sm_scale=float("inf")), 6), (dict(sm_scale=float("nan")), 6),
-    (dict(o=FAKE + 2), 9),
+    (dict(o=FAKE + 2), 9), (dict(qg=16), 6), (dict(qg=-1), 6),
 ])
 def test_attn_fwd_rejects(kw, code):
     assert _attn(qa.load_library(), **kw) == code
@@ -143,7 +146,7 @@ def test_attn_fwd_rejects(kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(lse=None), 1), (dict(o=None), 1), (dict(B=0), 2), (dict(d=96), 3),
     (dict(H=4, H_kv=3), 4), (dict(dt=3), 5), (dict(causal=2), 6), (dict(sm_scale=0.0), 6),
-    (dict(sm_scale=float("nan")), 6), (dict(k_i8=FAKE + 4), 9),
+    (dict(sm_scale=float("nan")), 6), (dict(k_i8=FAKE + 4), 9), (dict(qg=256), 6),
 ])
 def test_attn_fwd_lse_rejects(kw, code):
     assert _attn_lse(qa.load_library(), **kw) == code
@@ -173,3 +176,15 @@ def test_binding_refuses_cpu_tensors():
         qa.sage_quant_qk(q, q)
     with pytest.raises(ValueError):
         qa.sage_quant_v(q)
+
+
+def test_q_group_inferred_from_scale_length():
+    import torch
+    for N in (1, 17, 32, 33, 129, 17550):
+        for g in qa.Q_GROUPS:
+            qs = torch.zeros(1, 2, -(-N // g))
+            got = qa._q_group_of(qs, N)
+            # the inferred group indexes every query to the same scale as g
+            assert all(i // got == i // g for i in range(min(N, 300)))
+    with pytest.raises(ValueError):
+        qa._q_group_of(torch.zeros(1, 2, 5), 300)

@@ -30,11 +30,11 @@ def _rand_inputs(B, H, H_kv, N, d, dtype, seed, bias=3.0):
     return q, k, v
 
 
-def _check_quant(qa, q, k, v, smooth=True, heads_kv=None):
-    qk = qa.sage_quant_qk(q.to(DEV), k.to(DEV), smooth)
+def _check_quant(qa, q, k, v, smooth=True, heads_kv=None, q_group=128):
+    qk = qa.sage_quant_qk(q.to(DEV), k.to(DEV), smooth, q_group=q_group)
     vq = qa.sage_quant_v(v.to(DEV))
     torch.cuda.synchronize()
-    ref = O.quantize_qk(q, k, smooth_k=smooth)
+    ref = O.quantize_qk(q, k, smooth_k=smooth, q_group=q_group)
     refv = O.quantize_v(v)
     assert np.array_equal(to_np(qk["k_mean"]), ref["k_mean"])
     assert np.array_equal(to_np(qk["q_scale"]), ref["q_scale"])
@@ -50,10 +50,10 @@ def _check_quant(qa, q, k, v, smooth=True, heads_kv=None):
     return qk, vq, ref, refv
 
 
-def _oracle_o(ref, refv, causal, sm_scale, rows=None, heads=None):
+def _oracle_o(ref, refv, causal, sm_scale, rows=None, heads=None, q_group=128):
     return O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
                         refv["v_f8"], refv["v_scale"], causal=causal, sm_scale=sm_scale,
-                        rows=rows, heads=heads)
+                        rows=rows, heads=heads, blkq=q_group)
 
 
 # ------------------------------------------------------------------ small full parity
@@ -83,6 +83,61 @@ def test_small_full_parity(gpu_lib, B, H, H_kv, N, d, dtype, causal):
     o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=sm, out_dtype=dtype)
     torch.cuda.synchronize()
     compare_output(o, _oracle_o(ref, refv, causal, sm))
+
+
+Q_GROUP_CASES = [SMALL[i] for i in (1, 3, 4, 5, 9, 10)]
+
+
+@pytest.mark.parametrize("q_group", [32, 1])
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", Q_GROUP_CASES)
+def test_q_group_parity(gpu_lib, B, H, H_kv, N, d, dtype, causal, q_group):
+    """Q scales per 32 queries (one wave) or per query (one lane): codes and scales
+    bit-exact, output against the oracle with the same grouping."""
+    print(f"q_group {q_group} case B{B} H{H}/{H_kv} N{N} d{d} {dtype} causal={causal}",
+          flush=True)
+    q, k, v = _rand_inputs(B, H, H_kv, N, d, dtype, seed=N * 3 + d + q_group)
+    # token magnitudes that differ by up to e^2.5, so the groups' scales differ (scaled
+    # down only: sharper softmax rows would put |o| where one bf16 ulp exceeds 2e-2)
+    g = np.random.default_rng(N + q_group)
+    q = (q.float() * torch.from_numpy(np.exp(g.uniform(-2.5, 0, (B, H, N, 1))).astype(np.float32))
+         ).to(dtype)
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v, q_group=q_group)
+    assert qk["q_scale"].shape == (B, H, -(-N // q_group))
+    sm = 1 / math.sqrt(d)
+    o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=sm, out_dtype=dtype)
+    torch.cuda.synchronize()
+    compare_output(o, _oracle_o(ref, refv, causal, sm, q_group=q_group))
+
+
+def test_q_group_token_scales_mixed_exponent_forms(gpu_lib):
+    """Per-query scales where one query of a wave is so large that its wave takes the exact
+    exponent form while the other waves of the workgroup take the one-FMA form."""
+    q, k, v = _rand_inputs(1, 2, 2, 384, 128, torch.float16, seed=23)
+    q = q.float()
+    q[:, :, 40] *= 3000.0                     # query 40: wave 1 of the first workgroup
+    q = q.clamp(-60000, 60000).half()
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v, q_group=1)
+    for causal in (False, True):
+        o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=1 / 11.3,
+                                  out_dtype=torch.float16)
+        torch.cuda.synchronize()
+        compare_output(o, _oracle_o(ref, refv, causal, 1 / 11.3, q_group=1))
+
+
+def test_q_group_lse(gpu_lib):
+    q, k, v = _rand_inputs(1, 4, 2, 300, 128, torch.bfloat16, seed=24)
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v, q_group=1)
+    sm = 1 / math.sqrt(128)
+    o0 = gpu_lib.sage_attn_fwd(qk, vq, causal=True, sm_scale=sm, out_dtype=torch.bfloat16)
+    o1, lse = gpu_lib.sage_attn_fwd_lse(qk, vq, causal=True, sm_scale=sm,
+                                        out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1)
+    _, l_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
+                            refv["v_f8"], refv["v_scale"], causal=True, sm_scale=sm,
+                            return_lse=True, blkq=1)
+    err = np.abs(to_np(lse).astype(np.float64) - l_ref)
+    assert np.all(err <= _lse_tol(300, 0.0)), err.max()
 
 
 @pytest.mark.parametrize("N,d", [(256, 64), (300, 128), (129, 64)])
@@ -180,11 +235,12 @@ def test_deterministic(gpu_lib):
 
 # ------------------------------------------------------------------ the workloads
 
-def _workload_check(gpu_lib, name, heads, nrows, seed=0):
+def _workload_check(gpu_lib, name, heads, nrows, seed=0, q_group=128):
     w = W.get(name)
-    print(f"workload {name}: generating", flush=True)
+    print(f"workload {name} q_group {q_group}: generating", flush=True)
     t = W.generate(w)
-    plan = gpu_lib.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal)
+    plan = gpu_lib.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal,
+                            q_group=q_group)
     qd, kd, vd = t["q"].to(DEV), t["k"].to(DEV), t["v"].to(DEV)
     o = plan(qd, kd, vd)
     torch.cuda.synchronize()
@@ -195,7 +251,7 @@ def _workload_check(gpu_lib, name, heads, nrows, seed=0):
     qsel = torch.stack([t["q"][b, h] for b, h in heads])[None]
     ksel = torch.stack([t["k"][b, h] for b, h in hk_set])[None]
     vsel = torch.stack([t["v"][b, h] for b, h in hk_set])[None]
-    ref = O.quantize_qk(qsel, ksel)
+    ref = O.quantize_qk(qsel, ksel, q_group=q_group)
     refv = O.quantize_v(vsel)
     assert np.array_equal(sub(to_np(plan.qk["k_mean"]), hk_set), ref["k_mean"][0])
     assert np.array_equal(sub(to_np(plan.qk["q_i8"]), heads), ref["q_i8"][0])
@@ -218,7 +274,7 @@ def _workload_check(gpu_lib, name, heads, nrows, seed=0):
         o1 = O.attn_quant(qsel_i8[:, j:j + 1], ref["q_scale"][:, j:j + 1],
                           ref["k_i8"][:, kvj:kvj + 1], ref["k_scale"][:, kvj:kvj + 1],
                           refv["v_f8"][:, kvj:kvj + 1], refv["v_scale"][:, kvj:kvj + 1],
-                          causal=w.causal, sm_scale=w.sm_scale, rows=rows)
+                          causal=w.causal, sm_scale=w.sm_scale, rows=rows, blkq=q_group)
         o_ref[j] = o1[0, 0]
     o_gpu = torch.stack([o[b, h, torch.from_numpy(rows).to(DEV)] for b, h in heads])
     m = compare_output(o_gpu, o_ref)
@@ -236,6 +292,16 @@ def _workload_check(gpu_lib, name, heads, nrows, seed=0):
 ])
 def test_workload_parity(gpu_lib, name, heads, nrows):
     _workload_check(gpu_lib, name, heads, nrows)
+
+
+@pytest.mark.parametrize("name,heads,nrows,q_group", [
+    ("llm_prefill", [(0, 0), (0, 31)], 128, 1),
+    ("video_dit", [(0, 5)], 96, 32),
+    ("sweep@N4096", [(2, 9)], 96, 1),
+    ("gqa_long", [(0, 6)], 32, 32),
+])
+def test_workload_parity_q_group(gpu_lib, name, heads, nrows, q_group):
+    _workload_check(gpu_lib, name, heads, nrows, q_group=q_group)
 
 
 # ------------------------------------------------------------------ log-sum-exp (LSE)
