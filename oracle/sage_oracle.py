@@ -13,7 +13,8 @@ Two results are computed:
      in float64 on the unquantized fp16/bf16 inputs.
 (ii) ``quantize_qk`` / ``quantize_v`` / ``attn_quant`` -- the quantized
      method step by step, in the order of Algorithm 1 on the SageAttention2
-     detail page (with INT8 codes for Q and K, and without smoothing Q).
+     detail page (with INT8 codes for Q and K; smoothing Q with the Delta S
+     compensation is optional: ``smooth_q`` and ``delta_s``).
 
 Where the pages leave a step open the reading taken is stated at the step.
 """
@@ -109,12 +110,34 @@ def quantize_int8_blocks(x32: np.ndarray, block: int):
 Q_GROUPS = (BLKQ, 32, 1)
 
 
-def quantize_qk(q, k, smooth_k: bool = True, q_group: int = BLKQ):
+# Smooth Q (SageAttention2 detail page, Algorithm 1: q_bar_i = mean(Q_i),
+# then Q_i - q_bar_i is quantized; the pipeline figure (Figure 3's stages
+# 1-3) smooths Q, computes the Delta S GEMV, then quantizes).  Readings: the
+# mean's block is Algorithm 1's b_q = 128 tokens whatever the scale
+# granularity (a tail block averages its valid tokens); q_bar =
+# float32(exact sum / count), as for K; Q - q_bar is the float32
+# subtraction.
+
+def q_block_mean(q32: np.ndarray, block: int = BLKQ) -> np.ndarray:
+    """Per-channel mean of each block of `block` tokens, float32
+    [..., N, d] -> [..., ceil(N/block), d] (float64 sums: exact for fp16/bf16
+    inputs under the same condition as the K mean)."""
+    *lead, n, d = q32.shape
+    nb = -(-n // block)
+    out = np.zeros((*lead, nb, d), dtype=np.float32)
+    for i in range(nb):
+        xb = np.asarray(q32[..., i * block:(i + 1) * block, :], dtype=np.float64)
+        out[..., i, :] = (xb.sum(axis=-2) / xb.shape[-2]).astype(np.float32)
+    return out
+
+
+def quantize_qk(q, k, smooth_k: bool = True, q_group: int = BLKQ, smooth_q: bool = False):
     """Quantize Q per `q_group` tokens and smoothed K per 64 tokens.
 
     q: [B, H, N, d], k: [B, H_kv, N, d] (fp16/bf16 values as torch or numpy).
     Returns dict(q_i8, q_scale, k_i8, k_scale, k_mean); q_scale has
-    ceil(N / q_group) entries per head.
+    ceil(N / q_group) entries per head.  With ``smooth_q`` the codes are of
+    Q - q_bar and the dict also holds q_mean [B, H, ceil(N/128), d] float32.
     """
     assert q_group in Q_GROUPS, q_group
     q32 = _f32(q)
@@ -125,9 +148,34 @@ def quantize_qk(q, k, smooth_k: bool = True, q_group: int = BLKQ):
     else:
         mean = np.zeros(k32.shape[:-2] + k32.shape[-1:], dtype=np.float32)
         ks = k32
+    if smooth_q:
+        qm = q_block_mean(q32)
+        n = q32.shape[-2]
+        q32 = (q32 - np.repeat(qm, BLKQ, axis=-2)[..., :n, :]).astype(np.float32)
     qc, qs = quantize_int8_blocks(q32, q_group)
     kc, ksc = quantize_int8_blocks(ks, BLKK)
-    return dict(q_i8=qc, q_scale=qs, k_i8=kc, k_scale=ksc, k_mean=mean)
+    out = dict(q_i8=qc, q_scale=qs, k_i8=kc, k_scale=ksc, k_mean=mean)
+    if smooth_q:
+        out["q_mean"] = qm
+    return out
+
+
+# The Delta S compensation (SageAttention2 detail page, Algorithm 1:
+# S_ij = dequant(Q^_i K^_j^T) + GEMV(q_bar_i, K_j^T); "GEMV补偿" in its
+# line-by-line notes: a 1 x N vector per Q block, for every key).  Reading:
+# K_j is the K the quantizer sees (float32(K) - mean32 when K is smoothed,
+# float32(K) otherwise), before quantization; the product is exact here.
+
+def delta_s(q_mean, k, k_mean) -> np.ndarray:
+    """Delta S[b, h, i, j] = q_bar[b, h, i] . K_s[b, h // (H/H_kv), j], float64
+    [B, H, ceil(N/128), N].  k is the original K, k_mean its float32 mean
+    (zeros when K is not smoothed)."""
+    k32 = _f32(k)
+    ks = (k32 - np.asarray(k_mean, dtype=np.float32)[..., None, :]).astype(np.float32)
+    qm = np.asarray(q_mean, dtype=np.float64)
+    grp = qm.shape[1] // ks.shape[1]
+    ks_h = np.repeat(ks.astype(np.float64), grp, axis=1)          # [B, H, N, d]
+    return np.einsum("bhic,bhjc->bhij", qm, ks_h)
 
 
 # ---------------------------------------------------------------------------
@@ -219,7 +267,7 @@ def softmax_rows(q, k, *, causal: bool, sm_scale: float, b=0, h=0, hk=None):
 def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
                kv_tile: int = KV_TILE, rows=None, heads=None,
                quantize_p: bool = True, blkq: int = BLKQ, blkk: int = BLKK,
-               return_lse: bool = False):
+               return_lse: bool = False, delta_s=None):
     """Quantized attention, float64 result [B,H,len(rows),d].
 
     qc int8 [B,H,N,d], qs f32 [B,H,nq]; kc int8 [B,H_kv,N,d], ks f32
@@ -229,6 +277,8 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
     ``return_lse`` also L'_i = m_T + ln l (natural log) of the dequantized
     scores S the recursion used -- of the smoothed K when the codes are of
     K - mean(K); ``lse_correction`` restores the unsmoothed value.
+    ``delta_s`` ([B,H,ceil(N/128),N], from ``delta_s``): with smoothed-Q codes,
+    sm_scale * Delta S[query's 128-block, key] is added to every score.
     """
     B, H, N, d = qc.shape
     grp = H // kc.shape[1]
@@ -250,6 +300,8 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
             s = qc[b, h, rr].astype(np.float64) @ kf
             s = s * qs[b, h, rr // blkq].astype(np.float64)[:, None]
             s = s * ksc * sm_scale
+            if delta_s is not None:
+                s = s + np.asarray(delta_s[b, h], dtype=np.float64)[rr // BLKQ] * sm_scale
             if causal:
                 s = np.where(np.arange(N)[None, :] > rr[:, None], -np.inf, s)
             sp = np.full((len(rr), npad), -np.inf)
@@ -281,7 +333,8 @@ def lse_correction(q, k_mean, *, sm_scale: float):
 
 
 def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
-                         b=0, h=0, hk=None, blkq=BLKQ, blkk=BLKK, return_lse=False):
+                         b=0, h=0, hk=None, blkq=BLKQ, blkk=BLKK, return_lse=False,
+                         delta_s=None):
     """Literal online recursion of Algorithm 1 in pure Python loops (tiny sizes).
 
     Used to pin ``attn_quant``'s closed form: the same steps, one key tile at
@@ -304,6 +357,8 @@ def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
                     continue
                 acc = sum(int(qc[b, h, i, c]) * int(kc[b, hk, j, c]) for c in range(d))
                 srow[j] = acc * float(qs[b, h, i // blkq]) * float(ks[b, hk, j // blkk]) * sm_scale
+                if delta_s is not None:
+                    srow[j] += float(delta_s[b, h, i // BLKQ, j]) * sm_scale
             if not srow:
                 continue
             m_new = max(m, max(srow.values()))

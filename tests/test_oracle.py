@@ -429,6 +429,112 @@ def test_per_token_q_scales_closed_form_matches_recursion(causal):
         assert np.abs(a[0, h] - r).max() < 1e-12
 
 
+# ------------------------------------------------------------ smooth Q + Delta S
+
+def _biased_q(shape, seed, bias=3.0):
+    """Q with a per-(head, channel) bias shared by all tokens: the outlier
+    structure smoothing Q removes (SageAttention2 detail page, Table 4)."""
+    g = np.random.default_rng(seed)
+    B, H, N, d = shape
+    x = g.standard_normal(shape) + g.standard_normal((B, H, 1, d)) * bias
+    return torch.from_numpy(x.astype(np.float32)).half()
+
+
+def test_q_block_mean_equals_fsum():
+    q = _biased_q((1, 2, 300, 16), 31)
+    qm = O.q_block_mean(q.float().numpy())
+    assert qm.shape == (1, 2, 3, 16) and qm.dtype == np.float32
+    for h in range(2):
+        for i in range(3):
+            rows = q[0, h, i * 128:(i + 1) * 128].double().numpy()
+            for c in range(16):
+                assert qm[0, h, i, c] == np.float32(math.fsum(rows[:, c]) / rows.shape[0])
+
+
+@pytest.mark.parametrize("smooth_k", [True, False])
+def test_smooth_q_delta_s_restores_the_scores(smooth_k):
+    # (Q - q_bar) K_s^T + Delta S = Q K_s^T: the compensation belongs to the
+    # query's own 128-block and to every key, with GQA's head mapping
+    g = np.random.default_rng(32)
+    B, H, H_kv, N, d = 1, 4, 2, 300, 32
+    q = _biased_q((B, H, N, d), 33)
+    k = torch.from_numpy((g.standard_normal((B, H_kv, N, d)) + 2).astype(np.float32)).half()
+    z = O.quantize_qk(q, k, smooth_k=smooth_k, smooth_q=True)
+    ds = O.delta_s(z["q_mean"], k, z["k_mean"])
+    assert ds.shape == (B, H, 3, N)
+    q32 = q.float().numpy()
+    qs = (q32 - np.repeat(z["q_mean"], 128, axis=-2)[..., :N, :]).astype(np.float32)
+    ks = (k.float().numpy() - z["k_mean"][..., None, :]).astype(np.float32).astype(np.float64)
+    for h in range(H):
+        hk = h // 2
+        recon = qs[0, h].astype(np.float64) @ ks[0, hk].T + ds[0, h][np.arange(N) // 128]
+        exact = q32[0, h].astype(np.float64) @ ks[0, hk].T
+        # only the float32 rounding of Q - q_bar separates the two
+        bound = np.abs(q32[0, h]).astype(np.float64) @ np.abs(ks[0, hk]).T * 2.0 ** -23
+        assert (np.abs(recon - exact) <= bound + 1e-12).all()
+
+
+def test_smooth_q_lowers_the_score_error():
+    # Table 4's direction: on Q with a shared channel bias, quantizing Q - q_bar
+    # and adding Delta S back gives smaller score errors than quantizing Q
+    g = np.random.default_rng(34)
+    n, d = 512, 64
+    q = _biased_q((1, 1, n, d), 35, bias=4.0)
+    k = torch.from_numpy(g.standard_normal((1, 1, n, d)).astype(np.float32)).half()
+    err = {}
+    for sq in (False, True):
+        z = O.quantize_qk(q, k, smooth_q=sq)
+        ks = (k.float().numpy() - z["k_mean"][..., None, :]).astype(np.float32)
+        exact = q.double().numpy()[0, 0] @ ks[0, 0].astype(np.float64).T
+        qd = z["q_i8"][0, 0].astype(np.float64) * z["q_scale"][0, 0, np.arange(n) // 128, None]
+        kd = z["k_i8"][0, 0].astype(np.float64) * z["k_scale"][0, 0, np.arange(n) // 64, None]
+        s = qd @ kd.T
+        if sq:
+            s = s + O.delta_s(z["q_mean"], k, z["k_mean"])[0, 0][np.arange(n) // 128]
+        err[sq] = np.abs(s - exact).sum() / np.abs(exact).sum()
+    assert err[True] < 0.5 * err[False], err
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_smooth_q_closed_form_matches_recursion(causal):
+    g = np.random.default_rng(36)
+    n, d = 150, 8
+    q = _biased_q((1, 2, n, d), 37)
+    k = torch.from_numpy((g.standard_normal((1, 1, n, d)) + 1).astype(np.float32)).half()
+    v = torch.from_numpy(g.standard_normal((1, 1, n, d)).astype(np.float32)).half()
+    z = O.quantize_qk(q, k, smooth_q=True, q_group=32)
+    vz = O.quantize_v(v)
+    ds = O.delta_s(z["q_mean"], k, z["k_mean"])
+    kw = dict(causal=causal, sm_scale=0.3, kv_tile=32, blkq=32)
+    args = (z["q_i8"], z["q_scale"], z["k_i8"], z["k_scale"], vz["v_f8"], vz["v_scale"])
+    a, la = O.attn_quant(*args, delta_s=ds, return_lse=True, **kw)
+    for h in range(2):
+        r, lr = O.attn_quant_recursive(*args, h=h, hk=0, delta_s=ds, return_lse=True, **kw)
+        assert np.abs(a[0, h] - r).max() < 1e-12
+        assert np.abs(la[0, h] - lr).max() < 1e-12
+
+
+def test_smooth_q_quantized_tracks_exact_attention():
+    # with Delta S the smoothed-Q method is still attention on the original
+    # inputs: close to exact attention, and closer than without smoothing Q
+    g = np.random.default_rng(38)
+    n, d = 384, 64
+    q = _biased_q((1, 2, n, d), 39, bias=4.0)
+    k = torch.from_numpy((g.standard_normal((1, 2, n, d)) + 2).astype(np.float32)).half()
+    v = torch.from_numpy(g.standard_normal((1, 2, n, d)).astype(np.float32)).half()
+    ex = O.attn_exact(q, k, v, causal=True, sm_scale=0.125)
+    vz = O.quantize_v(v)
+    rl1 = {}
+    for sq in (False, True):
+        z = O.quantize_qk(q, k, smooth_q=sq)
+        ds = O.delta_s(z["q_mean"], k, z["k_mean"]) if sq else None
+        o = O.attn_quant(z["q_i8"], z["q_scale"], z["k_i8"], z["k_scale"], vz["v_f8"],
+                         vz["v_scale"], causal=True, sm_scale=0.125, delta_s=ds)
+        rl1[sq] = O.metrics(o, ex)["rel_l1"]
+    assert O.metrics(o, ex)["cos"] >= 0.998
+    assert rl1[True] < rl1[False], rl1
+
+
 def test_quantized_vs_exact_tiny_full():
     w = W.get("tiny")
     t = W.generate(w)
