@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--q-group", type=int, default=128, choices=(128, 32, 1),
                     help="Q tokens per INT8 scale: 128 per block (default), 32 per wave, "
                          "1 per query")
+    ap.add_argument("--smooth-q", action="store_true",
+                    help="smooth Q by its 128-block means and add the Delta S table back "
+                         "(sage_delta_s, timed separately)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB (3 times), "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -145,11 +148,12 @@ def main():
                                                         (1024, 2048, 4096, 8192, 16384, 32768)]
         names.append("gqa_long")
         for name in names:
-            r = run_config(W.get(name), max(args.steps, 5), args.warmup, q_group=args.q_group)
+            r = run_config(W.get(name), max(args.steps, 5), args.warmup, q_group=args.q_group,
+                           smooth_q=args.smooth_q)
             print(json.dumps(r), flush=True)
         return
     res = run_config(W.get(args.config), args.steps, args.warmup, full=True,
-                     q_group=args.q_group)
+                     q_group=args.q_group, smooth_q=args.smooth_q)
     if args.lse:
         res["lse"] = run_lse(W.get(args.config), args.steps, args.warmup)
     if not args.no_cpu:
@@ -201,7 +205,8 @@ def run_lse(w, steps: int, warmup: int) -> dict:
             "attn_fwd_lse_tops": round(w.ops() / (t_al * 1e-3) / 1e12, 2)}
 
 
-def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 128) -> dict:
+def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 128,
+               smooth_q: bool = False) -> dict:
     """Time `steps` whole steps of workload `w` (inputs resident on the GPU)."""
     import torch
     import quantized_attention_amd as qa
@@ -211,38 +216,43 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
     q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
     del t
     plan = qa.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal, device=dev,
-                       q_group=q_group)
+                       q_group=q_group, smooth_q=smooth_q)
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(warmup):
         plan(q, k, v)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         e = ev[s]
         e[0].record(stream)
-        qa.sage_quant_qk(q, k, True, q_group=q_group, out=plan.qk, workspace=plan.ws_qk)
+        qa.sage_quant_qk(q, k, True, q_group=q_group, smooth_q=smooth_q, out=plan.qk,
+                         workspace=plan.ws_qk)
         e[1].record(stream)
-        qa.sage_quant_v(v, out=plan.vq, workspace=plan.ws_v)
+        if smooth_q:
+            qa.sage_delta_s(k, plan.qk, plan.sm_scale, out=plan.delta_s)
         e[2].record(stream)
-        plan.attn()
+        qa.sage_quant_v(v, out=plan.vq, workspace=plan.ws_v)
         e[3].record(stream)
+        plan.attn()
+        e[4].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     t_qk = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    t_v = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    t_attn = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    t_ds = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    t_v = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    t_attn = sum(e[3].elapsed_time(e[4]) for e in ev) / steps
     ms_step = wall * 1e3 / steps
     ops = w.ops()
     attn_tops = ops / (t_attn * 1e-3) / 1e12
     # algorithmic bytes of the quantizers: read 2 B + write 1 B per element of Q, K and V
     quant_bytes = 3 * (w.B * w.H * w.N * w.d + 2 * w.B * w.H_kv * w.N * w.d)
     # the committed counters were taken with the default 128-token Q groups
-    traffic = traffic_from_profile(w.name) if q_group == 128 else None
+    traffic = traffic_from_profile(w.name) if q_group == 128 and not smooth_q else None
 
     res = {
         "metric": "quantized attn fwd TOPS at N=32K hd128 (4BHN^2d/t); % of MFMA INT8/FP8 peak",
@@ -259,12 +269,13 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
         "data": "synthetic (seeded normals, shared K channel bias)",
         "config": {"workload": w.description, "name": w.name, "B": w.B, "H": w.H,
                    "H_kv": w.H_kv, "N": w.N, "d": w.d, "causal": w.causal,
-                   "in_dtype": w.dtype, "q_group": q_group},
+                   "in_dtype": w.dtype, "q_group": q_group, "smooth_q": smooth_q},
         "attn_tops": round(attn_tops, 2),
         "attn_ms": round(t_attn, 4),
         "quant_qk_ms": round(t_qk, 4),
         "quant_v_ms": round(t_v, 4),
         "quant_gbs": round(quant_bytes / ((t_qk + t_v) * 1e-3) / 1e9, 1),
+        "delta_s_ms": round(t_ds, 4) if smooth_q else None,
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_fwd_kernel",
@@ -277,7 +288,7 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
     }
     if not full:
         keep = ("value", "ms_per_step", "config", "attn_tops", "attn_ms", "quant_qk_ms", "quant_v_ms",
-                "quant_gbs")
+                "quant_gbs", "delta_s_ms")
         res = {k: res[k] for k in keep}
         res["attn_frac_of_peak"] = round(res["attn_tops"] / PEAK_TOPS, 4)
     return res

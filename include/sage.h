@@ -5,7 +5,10 @@
  * source-analysis page's "Q/K 统一走 INT8" and without smoothing Q):
  *   1. Smooth K: subtract the per-channel mean of K over tokens
  *      (SageAttention synthesis page, Smooth K; Algorithm 1 preprocessing).
- *   2. Quantize Q per group of 128, 32 or 1 tokens and smoothed K per block
+ *   2. Optionally smooth Q by the per-channel mean of each 128-token block
+ *      (Algorithm 1's q_bar_i); the Delta S table q_bar_i . K_j, computed
+ *      once by sage_delta_s, adds the removed part back to the scores.
+ *      Quantize Q (or Q - q_bar) per group of 128, 32 or 1 tokens and smoothed K per block
  *      of 64 tokens to INT8 with one FP32 scale per group: scale = amax /
  *      127, code = round-half-even(x / scale) (deployment-guide page,
  *      quantization formula; block sizes b_q = 128, b_kv = 64 from the
@@ -49,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 3
+#define SAGE_ABI_VERSION 4
 
 /* Q tokens per INT8 scale (default), K tokens per INT8 scale. */
 #define SAGE_BLKQ 128
@@ -101,6 +104,8 @@ typedef struct {
   size_t o;         /* fp16/bf16 [B][H][N][d]                                   */
   size_t ws_quant_qk; /* workspace bytes sage_quant_qk needs                    */
   size_t ws_quant_v;  /* workspace bytes sage_quant_v needs                     */
+  size_t q_mean;    /* float [B][H][ceil(N/128)][d]   (smooth Q only)           */
+  size_t delta_s;   /* float [B][H][ceil(N/128)][N]   (smooth Q only)           */
 } sage_sizes;
 
 /*
@@ -133,7 +138,12 @@ sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, int q_group,
  *   smooth_k: 1 = subtract the per-channel token mean of K before
  *     quantizing (the mean is the exact sum over all N tokens, divided by N
  *     and rounded to float32); 0 = no smoothing (k_mean is written as 0).
- *   Outputs: q_i8, q_scale, k_i8, k_scale, k_mean (shapes in sage_sizes).
+ *   smooth_q: 1 = write q_mean[b][h][i][c] = float32(exact sum / count) over
+ *     the valid tokens of 128-token block i (Algorithm 1's q_bar_i, whatever
+ *     q_group is) and quantize float32(q) - q_mean of the token's block;
+ *     q_mean is then required.  0 = plain Q (q_mean may be NULL).
+ *   Outputs: q_i8, q_scale, k_i8, k_scale, k_mean, q_mean (shapes in
+ *     sage_sizes).
  *     scale = float32(amax / 127) with IEEE division over the block's valid
  *     tokens; code = RNE(float32(x / scale)) clamped to [-127, 127]; an
  *     all-zero block has scale 0 and codes 0.  Deterministic, bit-exact.
@@ -142,8 +152,25 @@ sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, int q_group,
  */
 sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype,
                           int B, int H, int H_kv, int N, int d, int q_group, int smooth_k,
-                          int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
-                          float* k_mean, void* workspace, size_t ws_bytes, void* stream);
+                          int smooth_q, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                          float* k_scale, float* k_mean, float* q_mean, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * The Delta S table of smooth Q (SageAttention2 detail page, Algorithm 1:
+ * S_ij = dequant(Q^_i K^_j^T) + GEMV(q_bar_i, K_j^T); its pipeline figure
+ * computes the GEMV before quantization, on the smoothed K):
+ *   delta_s[b][h][i][j] = sm_scale * log2(e) * sum_c q_mean[b][h][i][c] *
+ *                         (float32(k[b][h/(H/H_kv)][j][c]) - k_mean[b][h/(H/H_kv)][c])
+ * for every 128-token Q block i and key j < N, in the attention kernel's
+ * log2 score units, FP32 products and sums (FP32 matrix cores).
+ *   k: the original K in `dtype`; k_mean, q_mean: from sage_quant_qk
+ *   (k_mean is zeros when K was not smoothed).  sm_scale must be the one
+ *   passed to sage_attn_fwd.  delta_s: float, sizes.delta_s bytes.
+ */
+sage_status sage_delta_s(const void* k, sage_dtype dtype, const float* k_mean,
+                         const float* q_mean, int B, int H, int H_kv, int N, int d,
+                         float sm_scale, float* delta_s, void* stream);
 
 /*
  * Step 3: per-channel FP8 E4M3 quantization of V.
@@ -163,6 +190,8 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N
  *   Inputs are the outputs of sage_quant_qk / sage_quant_v for the same
  *   shapes and q_group.  o [B][H][N][d] is written in `out_dtype` (round to
  *   nearest even).
+ *   delta_s: NULL for plain Q; for smoothed Q the table of sage_delta_s,
+ *     added to every score (the scores then take the exact exponent form).
  *   causal: 1 = key j visible to query i iff j <= i; fully masked key tiles
  *     are skipped.  sm_scale: the softmax scale (> 0, finite), commonly
  *     1/sqrt(d).
@@ -171,8 +200,9 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N
  */
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                           const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                          void* o, sage_dtype out_dtype, int B, int H, int H_kv, int N, int d,
-                          int q_group, int causal, float sm_scale, void* stream);
+                          const float* delta_s, void* o, sage_dtype out_dtype, int B, int H,
+                          int H_kv, int N, int d, int q_group, int causal, float sm_scale,
+                          void* stream);
 
 /*
  * Step 4 with the row log-sum-exp (the per-row softmax state a forward pass
@@ -181,7 +211,8 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
  *   lse: float [B][H][N], required (caller-owned):
  *     lse[b][h][i] = ln sum_j exp(S_ij) + (lse_corr ? lse_corr[b][h][i] : 0)
  *     with S the dequantized scores the softmax used (sm_scale applied, the
- *     causal mask applied, K smoothed if sage_quant_qk smoothed it).
+ *     causal mask applied, K smoothed if sage_quant_qk smoothed it, Delta S
+ *     added when given).
  *   lse_corr: float [B][H][N] or NULL.  With smoothed K, pass the output of
  *     sage_lse_correction to get the log-sum-exp of the unsmoothed logits
  *     sm_scale * q . k (smoothing removed sm_scale * q . mean(K) from every
@@ -192,7 +223,8 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
  */
 sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                               const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                              void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
+                              const float* delta_s, void* o, sage_dtype out_dtype, float* lse,
+                              const float* lse_corr,
                               int B, int H, int H_kv, int N, int d, int q_group, int causal,
                               float sm_scale, void* stream);
 

@@ -12,18 +12,22 @@ online-softmax attention with INT8 QK^T and FP8 PV (P scaled by 448).
 
 Entry points (same names as the C ABI):
     sage_buffer_sizes(B, H, H_kv, N, d, q_group=128) -> dict of byte sizes
-    sage_quant_qk(q, k, smooth_k=True, q_group=128)
-        -> dict(q_i8, q_scale, k_i8, k_scale, k_mean)
+    sage_quant_qk(q, k, smooth_k=True, q_group=128, smooth_q=False)
+        -> dict(q_i8, q_scale, k_i8, k_scale, k_mean[, q_mean])
+    sage_delta_s(k, qk, sm_scale) -> fp32 [B, H, ceil(N/128), N] (smooth Q)
     sage_quant_v(v) -> dict(v_f8, v_scale)
-    sage_attn_fwd(qk, vq, causal=..., sm_scale=..., out_dtype=...) -> o
-    sage_attn_fwd_lse(qk, vq, causal=..., sm_scale=..., lse_corr=None) -> (o, lse)
+    sage_attn_fwd(qk, vq, causal=..., sm_scale=..., out_dtype=..., delta_s=None) -> o
+    sage_attn_fwd_lse(qk, vq, causal=..., sm_scale=..., lse_corr=None, delta_s=None)
+        -> (o, lse)
     sage_lse_correction(q, k_mean, sm_scale) -> fp32 [B, H, N]
     sage_qk_int32(q_i8, k_i8, b, h) -> int32 [N, N] (diagnostic)
 and the composition ``sageattn(q, k, v, is_causal=False, sm_scale=None,
-smooth_k=True, return_lse=False, q_group=128)``.  ``q_group`` is the number of
+smooth_k=True, return_lse=False, q_group=128, smooth_q=False)``.  ``q_group`` is the number of
 consecutive Q tokens per scale: 128 (per block), 32 (per wave, the per-warp
 granularity) or 1 (per query, the per-thread granularity); the attention
-entry points read it from the length of ``q_scale``.
+entry points read it from the length of ``q_scale``.  ``smooth_q`` subtracts each
+128-token Q block's mean before quantizing and adds the Delta S table back to
+the scores (Algorithm 1's GEMV compensation).
 """
 from __future__ import annotations
 
@@ -34,7 +38,8 @@ import os
 import torch
 
 __all__ = ["SageError", "library_path", "load_library", "sage_buffer_sizes", "sage_quant_qk",
-           "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse", "sage_lse_correction",
+           "sage_quant_v", "sage_delta_s", "sage_attn_fwd", "sage_attn_fwd_lse",
+           "sage_lse_correction",
            "sage_qk_int32", "sageattn", "SagePlan", "BLKQ", "BLKK", "KV_TILE", "Q_GROUPS"]
 
 BLKQ, BLKK, KV_TILE = 128, 64, 128
@@ -52,7 +57,7 @@ class SageError(RuntimeError):
 class _Sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_f8", "v_scale", "o",
-        "ws_quant_qk", "ws_quant_v")]
+        "ws_quant_qk", "ws_quant_v", "q_mean", "delta_s")]
 
 
 _lib = None
@@ -76,15 +81,17 @@ def load_library():
     lib.sage_status_str.argtypes = [i]
     lib.sage_status_str.restype = ctypes.c_char_p
     lib.sage_buffer_sizes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(_Sizes)]
-    lib.sage_quant_qk.argtypes = [vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sage_quant_qk.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp,
+                                  sz, vp]
+    lib.sage_delta_s.argtypes = [vp, i, vp, vp, i, i, i, i, i, ctypes.c_float, vp, vp]
     lib.sage_quant_v.argtypes = [vp, i, i, i, i, i, vp, vp, vp, sz, vp]
-    lib.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+    lib.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                   ctypes.c_float, vp]
-    lib.sage_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i,
-                                      i, ctypes.c_float, vp]
+    lib.sage_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i,
+                                      i, i, ctypes.c_float, vp]
     lib.sage_lse_correction.argtypes = [vp, i, vp, i, i, i, i, i, ctypes.c_float, vp, vp]
     lib.sage_qk_int32.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp]
-    for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_quant_v", "sage_attn_fwd",
+    for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_delta_s", "sage_quant_v", "sage_attn_fwd",
               "sage_attn_fwd_lse", "sage_lse_correction", "sage_qk_int32"):
         getattr(lib, f).restype = i
     _lib = lib
@@ -141,15 +148,18 @@ def _q_group_of(q_scale: torch.Tensor, N: int) -> int:
                      f"ceil(N / g) for g in {Q_GROUPS} with N = {N}")
 
 
-def _alloc_qk(B, H, H_kv, N, d, device, q_group=BLKQ):
+def _alloc_qk(B, H, H_kv, N, d, device, q_group=BLKQ, smooth_q=False):
     nq, nk = -(-N // q_group), -(-N // BLKK)
-    return dict(
+    out = dict(
         q_i8=torch.empty((B, H, N, d), dtype=torch.int8, device=device),
         q_scale=torch.empty((B, H, nq), dtype=torch.float32, device=device),
         k_i8=torch.empty((B, H_kv, N, d), dtype=torch.int8, device=device),
         k_scale=torch.empty((B, H_kv, nk), dtype=torch.float32, device=device),
         k_mean=torch.empty((B, H_kv, d), dtype=torch.float32, device=device),
     )
+    if smooth_q:
+        out["q_mean"] = torch.empty((B, H, -(-N // BLKQ), d), dtype=torch.float32, device=device)
+    return out
 
 
 def _alloc_v(B, H_kv, N, d, device):
@@ -161,9 +171,10 @@ def _alloc_v(B, H_kv, N, d, device):
 
 
 def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *,
-                  q_group: int = BLKQ, out=None, workspace=None, stream=None) -> dict:
-    """Smooth K and quantize Q (q_group tokens per scale), K to INT8 (see sage.h
-    for exact semantics)."""
+                  q_group: int = BLKQ, smooth_q: bool = False, out=None, workspace=None,
+                  stream=None) -> dict:
+    """Smooth K (and, with smooth_q, Q by its 128-block means) and quantize Q
+    (q_group tokens per scale) and K to INT8 (see sage.h for exact semantics)."""
     _need_gpu(q, k)
     if q.dtype != k.dtype:
         raise TypeError("q and k must share a dtype")
@@ -173,19 +184,39 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *,
         raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     if q_group not in Q_GROUPS:
         raise ValueError(f"q_group must be one of {Q_GROUPS}")
-    out = out or _alloc_qk(B, H, H_kv, N, d, q.device, q_group)
+    out = out or _alloc_qk(B, H, H_kv, N, d, q.device, q_group, smooth_q)
     if out["q_scale"].numel() != B * H * -(-N // q_group):
         raise ValueError("out['q_scale'] does not hold ceil(N / q_group) scales per head")
+    if smooth_q and "q_mean" not in out:
+        raise ValueError("smooth_q needs out['q_mean']")
     if workspace is None and smooth_k:
         ws = sage_buffer_sizes(B, H, H_kv, N, d)["ws_quant_qk"]
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     st = load_library().sage_quant_qk(
         q.data_ptr(), k.data_ptr(), _dt(q.dtype), B, H, H_kv, N, d, q_group, int(bool(smooth_k)),
-        out["q_i8"].data_ptr(), out["q_scale"].data_ptr(), out["k_i8"].data_ptr(),
-        out["k_scale"].data_ptr(), out["k_mean"].data_ptr(), _ptr(workspace),
+        int(bool(smooth_q)), out["q_i8"].data_ptr(), out["q_scale"].data_ptr(),
+        out["k_i8"].data_ptr(), out["k_scale"].data_ptr(), out["k_mean"].data_ptr(),
+        _ptr(out.get("q_mean")) if smooth_q else None, _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream, q.device))
     _check(st, "sage_quant_qk")
+    return out
+
+
+def sage_delta_s(k: torch.Tensor, qk: dict, sm_scale: float, *, out=None,
+                 stream=None) -> torch.Tensor:
+    """The Delta S table of smooth Q: sm_scale * log2(e) * q_mean . (k - k_mean) for
+    every 128-token Q block and key, fp32 [B, H, ceil(N/128), N] (see sage.h)."""
+    _need_gpu(k, qk["k_mean"], qk["q_mean"])
+    B, H, nmb, d = qk["q_mean"].shape
+    H_kv, N = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((B, H, nmb, N), dtype=torch.float32, device=k.device)
+    _need_gpu(out)
+    st = load_library().sage_delta_s(k.data_ptr(), _dt(k.dtype), qk["k_mean"].data_ptr(),
+                                     qk["q_mean"].data_ptr(), B, H, H_kv, N, d, float(sm_scale),
+                                     out.data_ptr(), _stream(stream, k.device))
+    _check(st, "sage_delta_s")
     return out
 
 
@@ -206,8 +237,9 @@ def sage_quant_v(v: torch.Tensor, *, out=None, workspace=None, stream=None) -> d
 
 
 def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
-                  out_dtype=torch.float16, out=None, stream=None) -> torch.Tensor:
-    """Attention on quantized inputs; returns O [B, H, N, d] in out_dtype."""
+                  out_dtype=torch.float16, delta_s=None, out=None, stream=None) -> torch.Tensor:
+    """Attention on quantized inputs; returns O [B, H, N, d] in out_dtype.
+    delta_s: the sage_delta_s table when Q was smoothed."""
     q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
     _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"])
     B, H, N, d = q_i8.shape
@@ -215,17 +247,28 @@ def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
     _need_gpu(out)
+    _check_delta_s(delta_s, qk)
     st = load_library().sage_attn_fwd(
         q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
-        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
+        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), _ptr(delta_s), out.data_ptr(),
+        _dt(out.dtype),
         B, H, H_kv, N, d, _q_group_of(qk["q_scale"], N), int(bool(causal)), float(sm_scale),
         _stream(stream, q_i8.device))
     _check(st, "sage_attn_fwd")
     return out
 
 
+def _check_delta_s(delta_s, qk):
+    B, H, N, _ = qk["q_i8"].shape
+    if delta_s is None:
+        return
+    _need_gpu(delta_s)
+    if delta_s.shape != (B, H, -(-N // BLKQ), N) or delta_s.dtype != torch.float32:
+        raise ValueError("delta_s must be float32 [B, H, ceil(N/128), N]")
+
+
 def sage_attn_fwd_lse(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
-                      out_dtype=torch.float16, lse_corr=None, out=None, lse=None,
+                      out_dtype=torch.float16, lse_corr=None, delta_s=None, out=None, lse=None,
                       stream=None):
     """Attention on quantized inputs plus the row log-sum-exp; returns (o, lse).
     lse [B, H, N] fp32 is ln sum_j exp(S_ij) of the scores the softmax used,
@@ -243,9 +286,11 @@ def sage_attn_fwd_lse(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
         _need_gpu(lse_corr)
         if lse_corr.shape != (B, H, N) or lse_corr.dtype != torch.float32:
             raise ValueError("lse_corr must be float32 [B, H, N]")
+    _check_delta_s(delta_s, qk)
     st = load_library().sage_attn_fwd_lse(
         q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
-        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
+        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), _ptr(delta_s), out.data_ptr(),
+        _dt(out.dtype),
         lse.data_ptr(), _ptr(lse_corr), B, H, H_kv, N, d, _q_group_of(qk["q_scale"], N),
         int(bool(causal)), float(sm_scale), _stream(stream, q_i8.device))
     _check(st, "sage_attn_fwd_lse")
@@ -282,44 +327,53 @@ def sage_qk_int32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, *,
 
 
 def sageattn(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
-             smooth_k: bool = True, return_lse: bool = False, q_group: int = BLKQ):
+             smooth_k: bool = True, return_lse: bool = False, q_group: int = BLKQ,
+             smooth_q: bool = False):
     """The whole forward pass: quantize Q/K/V, then the attention kernel.
     With return_lse, also the row log-sum-exp of the logits sm_scale q . k
     (corrected for the smoothing of K); returns (o, lse)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
-    qk = sage_quant_qk(q, k, smooth_k, q_group=q_group)
+    qk = sage_quant_qk(q, k, smooth_k, q_group=q_group, smooth_q=smooth_q)
+    ds = sage_delta_s(k, qk, sm_scale) if smooth_q else None
     vq = sage_quant_v(v)
     if not return_lse:
-        return sage_attn_fwd(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype)
+        return sage_attn_fwd(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype,
+                             delta_s=ds)
     corr = sage_lse_correction(q, qk["k_mean"], sm_scale) if smooth_k else None
     return sage_attn_fwd_lse(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype,
-                             lse_corr=corr)
+                             lse_corr=corr, delta_s=ds)
 
 
 class SagePlan:
     """Preallocated buffers for repeated calls on fixed shapes (no allocation per call)."""
 
     def __init__(self, B, H, H_kv, N, d, dtype, causal, sm_scale=None, device="cuda",
-                 q_group=BLKQ):
+                 q_group=BLKQ, smooth_q=False):
         self.shape = (B, H, H_kv, N, d)
         self.dtype, self.causal, self.q_group = dtype, causal, q_group
+        self.smooth_q = smooth_q
         self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
         sz = sage_buffer_sizes(B, H, H_kv, N, d, q_group)
-        self.qk = _alloc_qk(B, H, H_kv, N, d, device, q_group)
+        self.qk = _alloc_qk(B, H, H_kv, N, d, device, q_group, smooth_q)
+        self.delta_s = (torch.empty((B, H, -(-N // BLKQ), N), dtype=torch.float32, device=device)
+                        if smooth_q else None)
         self.vq = _alloc_v(B, H_kv, N, d, device)
         self.ws_qk = torch.empty(max(sz["ws_quant_qk"], 16), dtype=torch.uint8, device=device)
         self.ws_v = torch.empty(max(sz["ws_quant_v"], 16), dtype=torch.uint8, device=device)
         self.o = torch.empty((B, H, N, d), dtype=dtype, device=device)
 
     def quant(self, q, k, v, stream=None):
-        sage_quant_qk(q, k, True, q_group=self.q_group, out=self.qk, workspace=self.ws_qk,
-                      stream=stream)
+        sage_quant_qk(q, k, True, q_group=self.q_group, smooth_q=self.smooth_q, out=self.qk,
+                      workspace=self.ws_qk, stream=stream)
+        if self.smooth_q:
+            sage_delta_s(k, self.qk, self.sm_scale, out=self.delta_s, stream=stream)
         sage_quant_v(v, out=self.vq, workspace=self.ws_v, stream=stream)
 
     def attn(self, stream=None):
         return sage_attn_fwd(self.qk, self.vq, causal=self.causal, sm_scale=self.sm_scale,
-                             out_dtype=self.dtype, out=self.o, stream=stream)
+                             out_dtype=self.dtype, delta_s=self.delta_s, out=self.o,
+                             stream=stream)
 
     def __call__(self, q, k, v, stream=None):
         self.quant(q, k, v, stream)

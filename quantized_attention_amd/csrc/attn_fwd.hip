@@ -25,17 +25,22 @@
 
 namespace sage {
 
-template <int D, bool CAUSAL, bool BF16>
-// d = 64 fits three workgroups per CU (168 registers); d = 128 two.
-__global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
+// SQ: Q was smoothed by its 128-block means; delta_s holds the Delta S table
+// [B][H][ceil(N/128)][N] (log2 units) that is added to every score.
+template <int D, bool CAUSAL, bool BF16, bool SQ>
+// d = 64 fits three workgroups per CU (168 registers); d = 128, and d = 64
+// with Delta S, two.
+__global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_f8, const float* __restrict__ v_scale,
-    void* __restrict__ out, float* __restrict__ lse, const float* __restrict__ lse_corr, int H,
-    int H_kv, int N, float sm_log2, int qg_shift, int nqt, int total) {
+    const float* __restrict__ delta_s, void* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ lse_corr, int H, int H_kv, int N, float sm_log2, int qg_shift,
+    int nqt, int total) {
   constexpr int NKC = D / 32;                 // 32-wide channel chunks
   constexpr int KBYTES = kKvTile * D;         // K tile bytes (== V tile bytes)
-  __shared__ __attribute__((aligned(16))) char lds[2][2 * KBYTES];
+  constexpr int DSBYTES = SQ ? kKvTile * 4 : 0;   // a tile's Delta S values
+  __shared__ __attribute__((aligned(16))) char lds[2][2 * KBYTES + DSBYTES];
 
   // ---- which (b, kv head, q tile, group member) this workgroup computes.
   // Logical order: the `group` query heads that share a kv head are
@@ -86,8 +91,18 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
 
   // this lane's byte offset inside a 32-key K fragment block (full tiles)
   const uint32_t koff = (uint32_t)((lane % 32) * D + 16 * (lane / 32));
+  // Delta S row of this workgroup's Q block; waves 0 and 1 stage a tile's
+  // 128 values (one float per lane, keys past N read key N-1)
+  const float* dsr = SQ ? delta_s + ((size_t)(b * H + h) * nqt + qt) * N : nullptr;
+  auto load_ds_tile = [&](int t, char* dst) __attribute__((always_inline)) {
+    if (SQ && wave < 2) {
+      const int key = min(t * kKvTile + wave * 64 + lane, N - 1);
+      __builtin_amdgcn_global_load_lds(dsr + key, (lds_void*)(dst + wave * 256), 4, 0, 0);
+    }
+  };
   load_k_tile<D>(kh, 0, N, lds[0], wave, lane);
   load_v_tile<D>(vh, lds[0] + KBYTES, wave, lane);
+  load_ds_tile(0, lds[0] + 2 * KBYTES);
 
   // One 128-key step of the online softmax.  MASK: the tile holds keys past
   // the diagonal (causal) or past N; only the last tile can.
@@ -115,6 +130,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
       if ((t + 2) * kKvTile <= N) load_k_tile_full<D>(kh, (t + 1) * kKvTile, koff, lds[(t + 1) & 1], wave);
       else load_k_tile<D>(kh, (t + 1) * kKvTile, N, lds[(t + 1) & 1], wave, lane);
       load_v_tile<D>(vh + (size_t)(t + 1) * KBYTES, lds[(t + 1) & 1] + KBYTES, wave, lane);
+      load_ds_tile(t + 1, lds[(t + 1) & 1] + 2 * KBYTES);
     }
     const char* kt = lds[t & 1];
     const char* vt = lds[t & 1] + KBYTES;
@@ -148,28 +164,59 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
       ck[kb] = cq * ksc[MASK ? min(kidx, nkb - 1) : kidx];
     }
 
-    if constexpr (MASK) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * kKvTile + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          if ((CAUSAL && key > qi) || key >= N) s[kb][r] = INT_MIN;
-        }
-    }
-
-    // ---- tile row max (in-lane on the int bits, then across the lane halves).
     float xm = -INFINITY;
+    if constexpr (SQ) {
+      // ---- with Delta S: s becomes the float score t = (f - kMagic) * ck +
+      // Delta S[key] in log2 units (masked: -inf), and the row max is taken
+      // on those floats.
+      const float* dt = reinterpret_cast<const float*>(lds[t & 1] + 2 * KBYTES);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      // a depth-3 tree of max3 (short dependency chain)
-      const i32x16& v = s[kb];
-      const int m0 = max(max(v[0], v[1]), v[2]), m1 = max(max(v[3], v[4]), v[5]);
-      const int m2 = max(max(v[6], v[7]), v[8]), m3 = max(max(v[9], v[10]), v[11]);
-      const int m4 = max(max(v[12], v[13]), v[14]);
-      const int fm = max(max(max(m0, m1), m2), max(max(m3, m4), v[15]));
-      const float x = (as_float(fm) - kMagic) * ck[kb];
-      xm = MASK ? (fm != INT_MIN ? fmaxf(xm, x) : xm) : fmaxf(xm, x);
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // keys kb*32 + 8j + 4*half + (0..3) are registers 4j .. 4j+3
+          const float4 d4 = *reinterpret_cast<const float4*>(dt + kb * 32 + 8 * j + 4 * half);
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            float x = fmaf(as_float(s[kb][r]) - kMagic, ck[kb], dv[i]);
+            if constexpr (MASK) {
+              const int key = t * kKvTile + kb * 32 + 8 * j + 4 * half + i;
+              if ((CAUSAL && key > qi) || key >= N) x = -INFINITY;
+            }
+            s[kb][r] = as_int(x);
+          }
+        }
+        const i32x16& v = s[kb];
+        float m = fmaxf(fmaxf(as_float(v[0]), as_float(v[1])), as_float(v[2]));
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, as_float(v[r])), as_float(v[r + 1]));
+        xm = fmaxf(xm, fmaxf(m, as_float(v[15])));
+      }
+    } else {
+      if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = t * kKvTile + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+            if ((CAUSAL && key > qi) || key >= N) s[kb][r] = INT_MIN;
+          }
+      }
+
+      // ---- tile row max (in-lane on the int bits, then across the lane halves).
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        // a depth-3 tree of max3 (short dependency chain)
+        const i32x16& v = s[kb];
+        const int m0 = max(max(v[0], v[1]), v[2]), m1 = max(max(v[3], v[4]), v[5]);
+        const int m2 = max(max(v[6], v[7]), v[8]), m3 = max(max(v[9], v[10]), v[11]);
+        const int m4 = max(max(v[12], v[13]), v[14]);
+        const int fm = max(max(max(m0, m1), m2), max(max(m3, m4), v[15]));
+        const float x = (as_float(fm) - kMagic) * ck[kb];
+        xm = MASK ? (fm != INT_MIN ? fmaxf(xm, x) : xm) : fmaxf(xm, x);
+      }
     }
     xm = max_xor32(xm);
     const float m_new = fmaxf(m_run, xm);
@@ -187,7 +234,9 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     // The score is (f - kMagic) * ck with f the biased float of the int32
     // sum.  When ck is small, f*ck - (kMagic*ck + m') in one FMA is exact up
     // to ulp(kMagic*ck)/2 <= 2^-11 (log2 units); otherwise subtract kMagic
-    // first (exact) and then apply ck.  ck is uniform over the wave.
+    // first (exact) and then apply ck.  The form is fixed per wave.  With
+    // Delta S the score is already a float: exp2(t - m').  Masked scores
+    // give exp2(-inf) = 0 there.
     const float mq = m_new - kLog2_448;
     i32x8 pf[2];
     // The first two V fragments are read before the exponentials, the rest
@@ -208,11 +257,12 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
 #pragma unroll
       for (int j = 0; j < NE; ++j) {
         const int r = r0 + j;
-        const float a = decltype(fast_tag)::value
+        const float a = SQ ? as_float(s[kb][r]) - mq
+                        : decltype(fast_tag)::value
                             ? fmaf(as_float(s[kb][r]), ck[kb], -off)
                             : fmaf(as_float(s[kb][r]) - kMagic, ck[kb], -mq);
         e[j] = __builtin_amdgcn_exp2f(a);
-        if constexpr (MASK) e[j] = (s[kb][r] == INT_MIN) ? 0.f : e[j];
+        if constexpr (MASK && !SQ) e[j] = (s[kb][r] == INT_MIN) ? 0.f : e[j];
       }
       // this part's share of l as a tree (not a chain)
       float t[NE / 2];
@@ -292,7 +342,8 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     for (int t = 0; t < nfull; ++t) step(t, std::false_type{}, fast_tag);
     if (last_masked) step(ntiles - 1, std::true_type{}, fast_tag);
   };
-  if (fast_wg) run(std::true_type{});
+  if constexpr (SQ) run(std::false_type{});   // one exact form with Delta S
+  else if (fast_wg) run(std::true_type{});
   else run(std::false_type{});
 
   // ---- O = O / l * dV (l already carries the factor 448).
@@ -384,9 +435,9 @@ __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
 
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                                void* o, int bf16_out, float* lse, const float* lse_corr, int B,
-                                int H, int H_kv, int N, int d, int q_group, int causal,
-                                float sm_scale, hipStream_t stream) {
+                                const float* delta_s, void* o, int bf16_out, float* lse,
+                                const float* lse_corr, int B, int H, int H_kv, int N, int d,
+                                int q_group, int causal, float sm_scale, hipStream_t stream) {
   using namespace sage;
   const int qg_shift = q_group == kBlkQ ? 7 : q_group == kWaveQ ? 5 : q_group == 1 ? 0 : -1;
   if (qg_shift < 0) return hipErrorInvalidValue;
@@ -395,21 +446,26 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const float sm_log2 = sm_scale * kLog2e;
   dim3 grid((unsigned)total), block(kWaves * 64);
-#define SAGE_ATTN_CASE(DD, CC, BB)                                                               \
-  if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB) {                                 \
-    hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB>), grid, block, 0, stream, q_i8, q_scale,     \
-                       k_i8, k_scale, v_f8, v_scale, o, lse, lse_corr, H, H_kv, N, sm_log2,      \
-                       qg_shift, nqt, (int)total);                                               \
+  const bool sq = delta_s != nullptr;
+#define SAGE_ATTN_CASE(DD, CC, BB, SS)                                                           \
+  if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB && sq == SS) {                     \
+    hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB, SS>), grid, block, 0, stream, q_i8, q_scale, \
+                       k_i8, k_scale, v_f8, v_scale, delta_s, o, lse, lse_corr, H, H_kv, N,      \
+                       sm_log2, qg_shift, nqt, (int)total);                                      \
     return hipGetLastError();                                                                    \
   }
-  SAGE_ATTN_CASE(64, false, false)
-  SAGE_ATTN_CASE(64, false, true)
-  SAGE_ATTN_CASE(64, true, false)
-  SAGE_ATTN_CASE(64, true, true)
-  SAGE_ATTN_CASE(128, false, false)
-  SAGE_ATTN_CASE(128, false, true)
-  SAGE_ATTN_CASE(128, true, false)
-  SAGE_ATTN_CASE(128, true, true)
+#define SAGE_ATTN_CASES(SS)          \
+  SAGE_ATTN_CASE(64, false, false, SS)  \
+  SAGE_ATTN_CASE(64, false, true, SS)   \
+  SAGE_ATTN_CASE(64, true, false, SS)   \
+  SAGE_ATTN_CASE(64, true, true, SS)    \
+  SAGE_ATTN_CASE(128, false, false, SS) \
+  SAGE_ATTN_CASE(128, false, true, SS)  \
+  SAGE_ATTN_CASE(128, true, false, SS)  \
+  SAGE_ATTN_CASE(128, true, true, SS)
+  SAGE_ATTN_CASES(false)
+  SAGE_ATTN_CASES(true)
+#undef SAGE_ATTN_CASES
 #undef SAGE_ATTN_CASE
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,109 @@
+// delta_s.hip -- the Delta S table of smooth Q for gfx950.
+//
+// Algorithm 1 of the SageAttention2 detail page subtracts each Q block's mean
+// q_bar_i before quantizing Q and adds GEMV(q_bar_i, K_j^T) back to every
+// score of the block; its pipeline figure computes that GEMV before
+// quantization, on the smoothed K.  Here, for every (b, h), 128-token Q
+// block i and key j:
+//   out[b][h][i][j] = sm_scale * log2(e) * sum_c q_mean[b][h][i][c] * Ks[j][c],
+//   Ks[j][c] = float32(K[b][h_kv][j][c]) - k_mean[b][h_kv][c]
+// (the values the K quantizer sees), already in the attention kernel's
+// log2 score units.  Products and sums are FP32 on the matrix cores
+// (v_mfma_f32_32x32x2_f32).
+//
+// Work split: a workgroup of 4 waves owns 128 keys of one (b, h).  Each wave
+// keeps its 32 keys' smoothed K rows in registers (the B operand, d/2
+// floats per lane) and walks the ceil(N/128) mean rows 32 at a time (the A
+// operand, read from L2).  Contraction index: MFMA i of a lane in half g
+// uses channel g*d/2 + i for both operands, so the sum covers every channel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sage_device.hpp"
+
+namespace sage {
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k,
+                                                      const float* __restrict__ k_mean,
+                                                      const float* __restrict__ q_mean,
+                                                      float* __restrict__ out, int H, int H_kv,
+                                                      int N, int nmb, float sm_log2) {
+  constexpr int HALF = D / 2;
+  const int bh = blockIdx.y, b = bh / H, h = bh % H, hk = h / (H / H_kv);
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int col = lane % 32, g = lane / 32;
+  const int key = blockIdx.x * 128 + wave * 32 + col;
+  // B operand: this lane's key (rows past N read row N-1 and are not stored)
+  float kb[HALF];
+  {
+    const uint16_t* kr = reinterpret_cast<const uint16_t*>(k) +
+                         ((size_t)(b * H_kv + hk) * N + min(key, N - 1)) * D + g * HALF;
+    const float* km = k_mean + (size_t)(b * H_kv + hk) * D + g * HALF;
+#pragma unroll
+    for (int j = 0; j < HALF / 8; ++j) {
+      const uint4 u = *reinterpret_cast<const uint4*>(kr + j * 8);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float lo, hi;
+        if (BF16) {
+          lo = as_float((int)(w[i] << 16));
+          hi = as_float((int)(w[i] & 0xFFFF0000u));
+        } else {
+          lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+          hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+        }
+        kb[j * 8 + 2 * i] = lo - km[j * 8 + 2 * i];
+        kb[j * 8 + 2 * i + 1] = hi - km[j * 8 + 2 * i + 1];
+      }
+    }
+  }
+  const float* qm = q_mean + (size_t)bh * nmb * D;
+  float* ob = out + (size_t)bh * nmb * N;
+  for (int r0 = 0; r0 < nmb; r0 += 32) {
+    // A operand: mean row r0 + col (rows past nmb read the last row, not stored)
+    const float* qr = qm + (size_t)min(r0 + col, nmb - 1) * D + g * HALF;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < HALF; i += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(qr + i);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, kb[i], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, kb[i + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, kb[i + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, kb[i + 3], acc, 0, 0, 0);
+    }
+    if (key < N) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + 8 * (r / 4) + 4 * g + (r % 4);
+        if (row < nmb) ob[(size_t)row * N + key] = acc[r] * sm_log2;
+      }
+    }
+  }
+}
+
+}  // namespace sage
+
+hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
+                               int B, int H, int H_kv, int N, int d, float sm_scale, float* out,
+                               hipStream_t st) {
+  using namespace sage;
+  const int nmb = (N + kBlkQ - 1) / kBlkQ;
+  const dim3 grid((N + 127) / 128, B * H), block(256);
+  const float sm_log2 = sm_scale * kLog2e;
+#define SAGE_DS(DD, BB)                                                                         \
+  if (d == DD && (bf16 != 0) == BB) {                                                           \
+    hipLaunchKernelGGL((delta_s_kernel<DD, BB>), grid, block, 0, st, k, k_mean, q_mean, out, H, \
+                       H_kv, N, nmb, sm_log2);                                                  \
+    return hipGetLastError();                                                                   \
+  }
+  SAGE_DS(64, false)
+  SAGE_DS(64, true)
+  SAGE_DS(128, false)
+  SAGE_DS(128, true)
+#undef SAGE_DS
+  return hipErrorInvalidValue;
+}

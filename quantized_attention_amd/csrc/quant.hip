@@ -11,6 +11,9 @@
 //   quant_int8_tok    : the same rules with one scale per Q token (the
 //       per-thread granularity of the SageAttention2 detail page, Figure 4,
 //       when each matrix-core lane holds one query).
+//   q_block_mean      : per-channel mean of each 128-token Q block (Smooth Q,
+//       Algorithm 1 of the SageAttention2 detail page: q_bar_i = mean(Q_i));
+//       the quantizers then subtract the mean of the token's own block.
 //   quant_v_fp8       : per-channel FP8 E4M3 quantization of V, written
 //       transposed and key-permuted in the fragment layout of sage.h.
 //
@@ -150,6 +153,42 @@ __global__ __launch_bounds__(kQuantThreads) void colstats_final(const void* __re
 }
 
 // ---------------------------------------------------------------------------
+// q_mean[bh][blk][c] = float32(sum / count) over the valid tokens of 128-token
+// block blk: float64 partial sums per thread (exact for fp16/bf16 inputs under
+// the K mean's condition), combined in a fixed order.  grid (nblk, B*H).
+template <int D, bool BF16>
+__global__ __launch_bounds__(kQuantThreads) void q_block_mean(const void* __restrict__ x,
+                                                              float* __restrict__ q_mean, int N,
+                                                              int nblk) {
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kQuantThreads / TPR;   // rows per pass
+  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int rr = tid / TPR, cg = tid % TPR;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
+  double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int p = 0; p < kBlkQ / RPP; ++p) {
+    const int row = blk * kBlkQ + p * RPP + rr;
+    if (row < N) {
+      float v[8];
+      unpack8<BF16>(*reinterpret_cast<const uint4*>(xs + (size_t)row * D + cg * 8), v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] += (double)v[i];
+    }
+  }
+  __shared__ double red[RPP][D];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rr][cg * 8 + i] = s[i];
+  __syncthreads();
+  if (tid < D) {
+    double t = red[0][tid];
+    for (int r = 1; r < RPP; ++r) t += red[r][tid];
+    const int cnt = min(kBlkQ, N - blk * kBlkQ);
+    q_mean[((size_t)bh * nblk + blk) * D + tid] = (float)(t / (double)cnt);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Block max over the workgroup (all threads get the result).
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
@@ -163,9 +202,14 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return m;
 }
 
-// Per-block INT8 quantization of one block of BLK tokens x D channels.
-// SMOOTH: subtract mean[c] (float32) first.  grid (nblk, B*heads).
-template <int D, int BLK, bool BF16, bool SMOOTH>
+// Mean subtracted before quantizing: none, the head's K mean mean[bh][c], or
+// the Q mean of the token's 128-block mean[bh][row / 128][c].
+enum { kNoMean = 0, kHeadMean = 1, kBlockMean = 2 };
+
+// Per-block INT8 quantization of one block of BLK tokens x D channels
+// (BLK <= 128, so a block lies in one 128-token mean block).
+// SMOOTH: which mean (float32) is subtracted first.  grid (nblk, B*heads).
+template <int D, int BLK, bool BF16, int SMOOTH>
 __global__ __launch_bounds__(kQuantThreads) void quant_int8(const void* __restrict__ x,
                                                             const float* __restrict__ mean,
                                                             int8_t* __restrict__ codes,
@@ -178,9 +222,13 @@ __global__ __launch_bounds__(kQuantThreads) void quant_int8(const void* __restri
   const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
   int8_t* cs = codes + (size_t)bh * N * D;
 
+  static_assert(BLK <= kBlkQ, "a block lies in one mean block");
   float mu[8];
+  const size_t mrow = SMOOTH == kBlockMean
+                          ? (size_t)bh * ((N + kBlkQ - 1) / kBlkQ) + (blk * BLK) / kBlkQ
+                          : (size_t)bh;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) mu[i] = SMOOTH ? mean[(size_t)bh * D + cg * 8 + i] : 0.f;
+  for (int i = 0; i < 8; ++i) mu[i] = SMOOTH ? mean[mrow * D + cg * 8 + i] : 0.f;
 
   float v[PER][8];
   float amax = 0.f;
@@ -192,7 +240,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_int8(const void* __restri
       unpack8<BF16>(u, v[p]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if (SMOOTH) v[p][i] = v[p][i] - mu[i];
+        if (SMOOTH != kNoMean) v[p][i] = v[p][i] - mu[i];
         amax = fmaxf(amax, fabsf(v[p][i]));
       }
     } else {
@@ -233,9 +281,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_int8(const void* __restri
 
 // Per-token INT8 quantization: one scale per token.  The D/8 consecutive
 // threads of a token each load 8 channels; the token's amax is reduced by
-// xor-shuffles among them.  grid (ceil(N / tokens per workgroup), B*heads).
-template <int D, bool BF16>
+// xor-shuffles among them.  SMOOTH: subtract the Q mean of the token's
+// 128-block first.  grid (ceil(N / tokens per workgroup), B*heads).
+template <int D, bool BF16, bool SMOOTH>
 __global__ __launch_bounds__(kQuantThreads) void quant_int8_tok(const void* __restrict__ x,
+                                                                const float* __restrict__ mean,
                                                                 int8_t* __restrict__ codes,
                                                                 float* __restrict__ scales, int N) {
   constexpr int TPR = D / 8;
@@ -248,6 +298,12 @@ __global__ __launch_bounds__(kQuantThreads) void quant_int8_tok(const void* __re
   float amax = 0.f;
   if (row < N) {
     unpack8<BF16>(*reinterpret_cast<const uint4*>(xs + (size_t)row * D + cg * 8), v);
+    if (SMOOTH) {
+      const float* mu =
+          mean + ((size_t)bh * ((N + kBlkQ - 1) / kBlkQ) + row / kBlkQ) * D + cg * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] - mu[i];
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   } else {
@@ -391,12 +447,33 @@ size_t sage_ws_quant_v_bytes(int B, int H_kv, int N, int d) {
   return (size_t)B * H_kv * nchunks(N) * d * sizeof(float);
 }
 
+template <int D, bool BF16, bool SQ>
+static void launch_quant_q(const void* q, const float* q_mean, int B, int H, int N, int q_group,
+                           int8_t* q_i8, float* q_scale, hipStream_t st) {
+  using namespace sage;
+  constexpr int QM = SQ ? kBlockMean : kNoMean;
+  if (q_group == kBlkQ) {
+    const int nbq = (N + kBlkQ - 1) / kBlkQ;
+    hipLaunchKernelGGL((quant_int8<D, kBlkQ, BF16, QM>), dim3(nbq, B * H), dim3(kQuantThreads), 0,
+                       st, q, q_mean, q_i8, q_scale, N, nbq);
+  } else if (q_group == kWaveQ) {
+    const int nbq = (N + kWaveQ - 1) / kWaveQ;
+    hipLaunchKernelGGL((quant_int8<D, kWaveQ, BF16, QM>), dim3(nbq, B * H), dim3(kQuantThreads), 0,
+                       st, q, q_mean, q_i8, q_scale, N, nbq);
+  } else {
+    constexpr int tpb = kQuantThreads / (D / 8);
+    hipLaunchKernelGGL((quant_int8_tok<D, BF16, SQ>), dim3((N + tpb - 1) / tpb, B * H),
+                       dim3(kQuantThreads), 0, st, q, q_mean, q_i8, q_scale, N);
+  }
+}
+
 template <int D, bool BF16>
 static hipError_t quant_qk_impl(const void* q, const void* k, int B, int H, int H_kv, int N,
-                                int q_group, int smooth_k, int8_t* q_i8, float* q_scale,
-                                int8_t* k_i8, float* k_scale, float* k_mean, void* ws,
-                                hipStream_t st) {
+                                int q_group, int smooth_k, int smooth_q, int8_t* q_i8,
+                                float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                                float* q_mean, void* ws, hipStream_t st) {
   using namespace sage;
+  if (q_group != kBlkQ && q_group != kWaveQ && q_group != 1) return hipErrorInvalidValue;
   const int nc = nchunks(N);
   const int nbk = (N + kBlkK - 1) / kBlkK;
   if (smooth_k) {
@@ -405,26 +482,19 @@ static hipError_t quant_qk_impl(const void* q, const void* k, int B, int H, int 
   }
   hipLaunchKernelGGL((colstats_final<D, 0>), dim3(B * H_kv), dim3(kQuantThreads), 0, st, ws, k_mean,
                      N, nc, smooth_k);
-  if (q_group == kBlkQ) {
-    const int nbq = (N + kBlkQ - 1) / kBlkQ;
-    hipLaunchKernelGGL((quant_int8<D, kBlkQ, BF16, false>), dim3(nbq, B * H), dim3(kQuantThreads),
-                       0, st, q, nullptr, q_i8, q_scale, N, nbq);
-  } else if (q_group == kWaveQ) {
-    const int nbq = (N + kWaveQ - 1) / kWaveQ;
-    hipLaunchKernelGGL((quant_int8<D, kWaveQ, BF16, false>), dim3(nbq, B * H), dim3(kQuantThreads),
-                       0, st, q, nullptr, q_i8, q_scale, N, nbq);
-  } else if (q_group == 1) {
-    constexpr int tpb = kQuantThreads / (D / 8);
-    hipLaunchKernelGGL((quant_int8_tok<D, BF16>), dim3((N + tpb - 1) / tpb, B * H),
-                       dim3(kQuantThreads), 0, st, q, q_i8, q_scale, N);
+  if (smooth_q) {
+    const int nmb = (N + kBlkQ - 1) / kBlkQ;
+    hipLaunchKernelGGL((q_block_mean<D, BF16>), dim3(nmb, B * H), dim3(kQuantThreads), 0, st, q,
+                       q_mean, N, nmb);
+    launch_quant_q<D, BF16, true>(q, q_mean, B, H, N, q_group, q_i8, q_scale, st);
   } else {
-    return hipErrorInvalidValue;
+    launch_quant_q<D, BF16, false>(q, nullptr, B, H, N, q_group, q_i8, q_scale, st);
   }
   if (smooth_k)
-    hipLaunchKernelGGL((quant_int8<D, kBlkK, BF16, true>), dim3(nbk, B * H_kv),
+    hipLaunchKernelGGL((quant_int8<D, kBlkK, BF16, kHeadMean>), dim3(nbk, B * H_kv),
                        dim3(kQuantThreads), 0, st, k, k_mean, k_i8, k_scale, N, nbk);
   else
-    hipLaunchKernelGGL((quant_int8<D, kBlkK, BF16, false>), dim3(nbk, B * H_kv),
+    hipLaunchKernelGGL((quant_int8<D, kBlkK, BF16, kNoMean>), dim3(nbk, B * H_kv),
                        dim3(kQuantThreads), 0, st, k, nullptr, k_i8, k_scale, N, nbk);
   return hipGetLastError();
 }
@@ -446,13 +516,13 @@ static hipError_t quant_v_impl(const void* v, int B, int H_kv, int N, uint8_t* v
 }
 
 hipError_t sage_launch_quant_qk(const void* q, const void* k, int bf16, int B, int H, int H_kv,
-                                int N, int d, int q_group, int smooth_k, int8_t* q_i8,
-                                float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                                void* ws, hipStream_t st) {
+                                int N, int d, int q_group, int smooth_k, int smooth_q,
+                                int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                float* k_mean, float* q_mean, void* ws, hipStream_t st) {
 #define SAGE_QQK(DD, BB)                                                                       \
   if (d == DD && (bf16 != 0) == BB)                                                            \
-    return quant_qk_impl<DD, BB>(q, k, B, H, H_kv, N, q_group, smooth_k, q_i8, q_scale, k_i8,  \
-                                 k_scale, k_mean, ws, st);
+    return quant_qk_impl<DD, BB>(q, k, B, H, H_kv, N, q_group, smooth_k, smooth_q, q_i8,       \
+                                 q_scale, k_i8, k_scale, k_mean, q_mean, ws, st);
   SAGE_QQK(64, false)
   SAGE_QQK(64, true)
   SAGE_QQK(128, false)

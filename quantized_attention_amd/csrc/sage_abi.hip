@@ -9,16 +9,19 @@
 #include "sage.h"
 
 hipError_t sage_launch_quant_qk(const void* q, const void* k, int bf16, int B, int H, int H_kv,
-                                int N, int d, int q_group, int smooth_k, int8_t* q_i8,
-                                float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                                void* ws, hipStream_t st);
+                                int N, int d, int q_group, int smooth_k, int smooth_q,
+                                int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                float* k_mean, float* q_mean, void* ws, hipStream_t st);
+hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
+                               int B, int H, int H_kv, int N, int d, float sm_scale, float* out,
+                               hipStream_t st);
 hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, int d,
                                uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st);
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                                void* o, int bf16_out, float* lse, const float* lse_corr, int B,
-                                int H, int H_kv, int N, int d, int q_group, int causal,
-                                float sm_scale, hipStream_t stream);
+                                const float* delta_s, void* o, int bf16_out, float* lse,
+                                const float* lse_corr, int B, int H, int H_kv, int N, int d,
+                                int q_group, int causal, float sm_scale, hipStream_t stream);
 hipError_t sage_launch_lse_correction(const void* q, int bf16, const float* k_mean, int B, int H,
                                       int H_kv, int N, int d, float sm_scale, float* corr,
                                       hipStream_t st);
@@ -40,6 +43,11 @@ sage_status check_shape(int B, int H, int H_kv, int N, int d) {
   const int64_t npad = ((int64_t)N + SAGE_KV_TILE - 1) / SAGE_KV_TILE * SAGE_KV_TILE;
   if ((int64_t)B * H > 65535 || (int64_t)B * H * npad * d > kMaxElems) return SAGE_ERR_SHAPE;
   return SAGE_OK;
+}
+
+// elements of the Delta S table, B*H*ceil(N/128)*N
+int64_t delta_s_elems(int B, int H, int N) {
+  return (int64_t)B * H * (((int64_t)N + SAGE_BLKQ - 1) / SAGE_BLKQ) * N;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -91,27 +99,46 @@ sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, int q_group,
   out->o = b * h * n * dd * 2;
   out->ws_quant_qk = sage_ws_quant_qk_bytes(B, H_kv, N, d);
   out->ws_quant_v = sage_ws_quant_v_bytes(B, H_kv, N, d);
+  const size_t nmb = (n + SAGE_BLKQ - 1) / SAGE_BLKQ;
+  out->q_mean = b * h * nmb * dd * sizeof(float);
+  out->delta_s = (size_t)delta_s_elems(B, H, N) * sizeof(float);
   return SAGE_OK;
 }
 
 sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype, int B, int H, int H_kv,
-                          int N, int d, int q_group, int smooth_k, int8_t* q_i8, float* q_scale,
-                          int8_t* k_i8, float* k_scale, float* k_mean, void* workspace,
-                          size_t ws_bytes, void* stream) {
+                          int N, int d, int q_group, int smooth_k, int smooth_q, int8_t* q_i8,
+                          float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                          float* q_mean, void* workspace, size_t ws_bytes, void* stream) {
   if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean) return SAGE_ERR_NULL;
+  if (smooth_q == 1 && !q_mean) return SAGE_ERR_NULL;
   sage_status st = check_shape(B, H, H_kv, N, d);
   if (st != SAGE_OK) return st;
   if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
   if (!valid_q_group(q_group)) return SAGE_ERR_ARG;
   if (smooth_k != 0 && smooth_k != 1) return SAGE_ERR_ARG;
+  if (smooth_q != 0 && smooth_q != 1) return SAGE_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8)) return SAGE_ERR_ALIGN;
   if (smooth_k) {
     if (!workspace) return SAGE_ERR_WORKSPACE;
     if (ws_bytes < sage_ws_quant_qk_bytes(B, H_kv, N, d)) return SAGE_ERR_WORKSPACE;
   }
   return from_hip(sage_launch_quant_qk(q, k, dtype == SAGE_BF16, B, H, H_kv, N, d, q_group,
-                                       smooth_k, q_i8, q_scale, k_i8, k_scale, k_mean, workspace,
-                                       (hipStream_t)stream));
+                                       smooth_k, smooth_q, q_i8, q_scale, k_i8, k_scale, k_mean,
+                                       q_mean, workspace, (hipStream_t)stream));
+}
+
+sage_status sage_delta_s(const void* k, sage_dtype dtype, const float* k_mean,
+                         const float* q_mean, int B, int H, int H_kv, int N, int d,
+                         float sm_scale, float* delta_s, void* stream) {
+  if (!k || !k_mean || !q_mean || !delta_s) return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
+  if (delta_s_elems(B, H, N) > kMaxElems) return SAGE_ERR_SHAPE;
+  if (!aligned16(k) || !aligned16(q_mean) || !aligned16(delta_s)) return SAGE_ERR_ALIGN;
+  return from_hip(sage_launch_delta_s(k, dtype == SAGE_BF16, k_mean, q_mean, B, H, H_kv, N, d,
+                                      sm_scale, delta_s, (hipStream_t)stream));
 }
 
 sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N, int d,
@@ -130,8 +157,9 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N
 
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                           const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                          void* o, sage_dtype out_dtype, int B, int H, int H_kv, int N, int d,
-                          int q_group, int causal, float sm_scale, void* stream) {
+                          const float* delta_s, void* o, sage_dtype out_dtype, int B, int H,
+                          int H_kv, int N, int d, int q_group, int causal, float sm_scale,
+                          void* stream) {
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8 || !v_scale || !o) return SAGE_ERR_NULL;
   sage_status st = check_shape(B, H, H_kv, N, d);
   if (st != SAGE_OK) return st;
@@ -141,14 +169,16 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
     return SAGE_ERR_ALIGN;
-  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, o,
+  if (delta_s && !aligned16(delta_s)) return SAGE_ERR_ALIGN;
+  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, delta_s, o,
                                        out_dtype == SAGE_BF16, nullptr, nullptr, B, H, H_kv, N,
                                        d, q_group, causal, sm_scale, (hipStream_t)stream));
 }
 
 sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                               const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                              void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
+                              const float* delta_s, void* o, sage_dtype out_dtype, float* lse,
+                              const float* lse_corr,
                               int B, int H, int H_kv, int N, int d, int q_group, int causal,
                               float sm_scale, void* stream) {
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8 || !v_scale || !o || !lse)
@@ -161,7 +191,8 @@ sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const in
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
     return SAGE_ERR_ALIGN;
-  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, o,
+  if (delta_s && !aligned16(delta_s)) return SAGE_ERR_ALIGN;
+  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, delta_s, o,
                                        out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d,
                                        q_group, causal, sm_scale, (hipStream_t)stream));
 }

@@ -26,10 +26,11 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse",
             "sage_lse_correction", "sage_buffer_sizes", "sage_qk_int32", "sage_status_str",
+            "sage_delta_s",
             "sage_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sage_abi_version() == 3
+    assert lib.sage_abi_version() == 4
 
 
 def test_status_strings():
@@ -53,6 +54,8 @@ def test_buffer_sizes(B, H, H_kv, N, d, q_group):
     assert s["o"] == 2 * B * H * N * d
     assert s["ws_quant_qk"] == 8 * B * H_kv * math.ceil(N / 256) * d
     assert s["ws_quant_v"] == 4 * B * H_kv * math.ceil(N / 256) * d
+    assert s["q_mean"] == 4 * B * H * math.ceil(N / 128) * d
+    assert s["delta_s"] == 4 * B * H * math.ceil(N / 128) * N
 
 
 @pytest.mark.parametrize("args,code", [
@@ -68,9 +71,9 @@ def test_buffer_sizes_rejects(args, code):
 
 
 def _qk(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, dt=0, B=1, H=2, H_kv=2, N=256, d=64, qg=128, smooth=1, q_i8=FAKE,
-             q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, ws=FAKE, ws_bytes=1 << 20,
-             stream=None)
+    a = dict(q=FAKE, k=FAKE, dt=0, B=1, H=2, H_kv=2, N=256, d=64, qg=128, smooth=1, sq=0,
+             q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, q_mean=None, ws=FAKE,
+             ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return lib.sage_quant_qk(*a.values())
 
@@ -83,15 +86,16 @@ def _v(lib, **kw):
 
 
 def _attn(lib, **kw):
-    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, o=FAKE,
-             dt=0, B=1, H=2, H_kv=2, N=256, d=64, qg=128, causal=0, sm_scale=0.125, stream=None)
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, ds=None,
+             o=FAKE, dt=0, B=1, H=2, H_kv=2, N=256, d=64, qg=128, causal=0, sm_scale=0.125,
+             stream=None)
     a.update(kw)
     return lib.sage_attn_fwd(*a.values())
 
 
 def _attn_lse(lib, **kw):
-    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, o=FAKE,
-             dt=0, lse=FAKE, corr=None, B=1, H=2, H_kv=2, N=256, d=64, qg=128, causal=0,
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, ds=None,
+             o=FAKE, dt=0, lse=FAKE, corr=None, B=1, H=2, H_kv=2, N=256, d=64, qg=128, causal=0,
              sm_scale=0.125, stream=None)
     a.update(kw)
     return lib.sage_attn_fwd_lse(*a.values())
@@ -104,6 +108,13 @@ def _lse_corr(lib, **kw):
     return lib.sage_lse_correction(*a.values())
 
 
+def _ds(lib, **kw):
+    a = dict(k=FAKE, dt=0, k_mean=FAKE, q_mean=FAKE, B=1, H=2, H_kv=2, N=256, d=64,
+             sm_scale=0.125, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.sage_delta_s(*a.values())
+
+
 def _qk32(lib, **kw):
     a = dict(q_i8=FAKE, k_i8=FAKE, B=1, H=2, H_kv=2, N=256, d=64, b=0, h=0, s=FAKE, stream=None)
     a.update(kw)
@@ -114,7 +125,8 @@ def _qk32(lib, **kw):
     (dict(q=None), 1), (dict(k_mean=None), 1), (dict(B=0), 2), (dict(N=-5), 2),
     (dict(d=32), 3), (dict(H=3), 4), (dict(dt=2), 5), (dict(smooth=2), 6),
     (dict(q=FAKE + 8), 9), (dict(k_i8=FAKE + 4), 9), (dict(ws=None), 7), (dict(ws_bytes=1023), 7),
-    (dict(qg=64), 6), (dict(qg=0), 6), (dict(qg=2), 6),
+    (dict(qg=64), 6), (dict(qg=0), 6), (dict(qg=2), 6), (dict(sq=2), 6), (dict(sq=1), 1),
+    (dict(sq=-1), 6),
 ])
 def test_quant_qk_rejects(kw, code):
     assert _qk(qa.load_library(), **kw) == code
@@ -137,7 +149,7 @@ def test_quant_v_rejects(kw, code):
     (dict(o=None), 1), (dict(v_scale=None), 1), (dict(H_kv=0), 2), (dict(d=16), 3),
     (dict(H=4, H_kv=3), 4), (dict(dt=7), 5), (dict(causal=3), 6), (dict(sm_scale=0.0), 6),
     (dict(sm_scale=-1.0), 6), (dict(sm_scale=float("inf")), 6), (dict(sm_scale=float("nan")), 6),
-    (dict(o=FAKE + 2), 9), (dict(qg=16), 6), (dict(qg=-1), 6),
+    (dict(o=FAKE + 2), 9), (dict(qg=16), 6), (dict(qg=-1), 6), (dict(ds=FAKE + 4), 9),
 ])
 def test_attn_fwd_rejects(kw, code):
     assert _attn(qa.load_library(), **kw) == code
@@ -159,6 +171,16 @@ def test_attn_fwd_lse_rejects(kw, code):
 ])
 def test_lse_correction_rejects(kw, code):
     assert _lse_corr(qa.load_library(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), 1), (dict(k_mean=None), 1), (dict(q_mean=None), 1), (dict(out=None), 1),
+    (dict(B=0), 2), (dict(d=96), 3), (dict(H=3), 4), (dict(dt=4), 5), (dict(sm_scale=0.0), 6),
+    (dict(sm_scale=float("inf")), 6), (dict(q_mean=FAKE + 8), 9), (dict(out=FAKE + 4), 9),
+    (dict(B=8, H=512, H_kv=512, N=1 << 20), 2),
+])
+def test_delta_s_rejects(kw, code):
+    assert _ds(qa.load_library(), **kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -233,14 +233,132 @@ def test_deterministic(gpu_lib):
     assert all(torch.equal(outs[0], o) for o in outs[1:])
 
 
+# ------------------------------------------------------------------ smooth Q + Delta S
+
+LOG2E = 1.4426950408889634
+
+
+def _check_delta_s_table(ds_gpu, ds_ref, q_mean, k, k_mean, sm):
+    """One head's table: GPU = sm * log2(e) * q_bar . K_s in FP32 against the oracle's exact
+    q_bar . K_s, within the FP32 dot-product bound (d + 4) * 2^-24 * sum |q_bar_c K_s,c|."""
+    d = q_mean.shape[-1]
+    ks = (np.asarray(k, dtype=np.float32) - np.asarray(k_mean, dtype=np.float32)).astype(np.float32)
+    absb = np.abs(np.asarray(q_mean, dtype=np.float64)) @ np.abs(ks.astype(np.float64)).T
+    l2 = sm * LOG2E
+    err = np.abs(ds_gpu.astype(np.float64) - ds_ref * l2)
+    assert np.all(err <= (d + 4) * 2.0 ** -24 * l2 * absb + 1e-30), err.max()
+
+
+def _biased_q_inputs(B, H, H_kv, N, d, dtype, seed, qbias=1.5):
+    """Inputs whose Q carries a per-(head, channel) bias shared by its tokens (what
+    smoothing Q removes)."""
+    q, k, v = _rand_inputs(B, H, H_kv, N, d, dtype, seed)
+    g = np.random.default_rng(seed + 1)
+    bias = torch.from_numpy((g.standard_normal((B, H, 1, d)) * qbias).astype(np.float32))
+    return (q.float() + bias).to(dtype), k, v
+
+
+def _check_smooth_q(qa, q, k, v, sm, q_group=128, smooth_k=True):
+    qk = qa.sage_quant_qk(q.to(DEV), k.to(DEV), smooth_k, q_group=q_group, smooth_q=True)
+    ds = qa.sage_delta_s(k.to(DEV), qk, sm)
+    vq = qa.sage_quant_v(v.to(DEV))
+    torch.cuda.synchronize()
+    ref = O.quantize_qk(q, k, smooth_k=smooth_k, q_group=q_group, smooth_q=True)
+    refv = O.quantize_v(v)
+    for n in ("q_mean", "k_mean", "q_scale", "q_i8", "k_scale", "k_i8"):
+        assert np.array_equal(to_np(qk[n]), ref[n]), n
+    ds_ref = O.delta_s(ref["q_mean"], k, ref["k_mean"])
+    B, H = q.shape[:2]
+    grp = H // k.shape[1]
+    k32 = k.float().numpy()
+    ds_g = to_np(ds)
+    for b in range(B):
+        for h in range(H):
+            _check_delta_s_table(ds_g[b, h], ds_ref[b, h], ref["q_mean"][b, h], k32[b, h // grp],
+                                 ref["k_mean"][b, h // grp], sm)
+    return qk, vq, ds, ref, refv, ds_ref
+
+
+SQ_CASES = [SMALL[i] for i in (1, 2, 3, 5, 9, 10)]
+
+
+@pytest.mark.parametrize("q_group", [128, 1])
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", SQ_CASES)
+def test_smooth_q_parity(gpu_lib, B, H, H_kv, N, d, dtype, causal, q_group):
+    """Smooth Q: block means, codes and scales bit-exact, the Delta S table within the FP32
+    bound, and the output against the oracle with its exact Delta S."""
+    print(f"smooth_q q_group {q_group} case B{B} H{H}/{H_kv} N{N} d{d} {dtype} causal={causal}",
+          flush=True)
+    q, k, v = _biased_q_inputs(B, H, H_kv, N, d, dtype, seed=N * 11 + d + q_group)
+    sm = 1 / math.sqrt(d)
+    qk, vq, ds, ref, refv, ds_ref = _check_smooth_q(gpu_lib, q, k, v, sm, q_group)
+    o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=sm, out_dtype=dtype, delta_s=ds)
+    torch.cuda.synchronize()
+    o_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"], refv["v_f8"],
+                         refv["v_scale"], causal=causal, sm_scale=sm, blkq=q_group,
+                         delta_s=ds_ref)
+    compare_output(o, o_ref)
+
+
+def test_smooth_q_without_smooth_k(gpu_lib):
+    q, k, v = _biased_q_inputs(1, 2, 2, 300, 64, torch.float16, seed=51)
+    qk, vq, ds, ref, refv, ds_ref = _check_smooth_q(gpu_lib, q, k, v, 0.125, smooth_k=False)
+    assert (to_np(qk["k_mean"]) == 0).all()
+    o = gpu_lib.sage_attn_fwd(qk, vq, causal=False, sm_scale=0.125, out_dtype=torch.float16,
+                              delta_s=ds)
+    torch.cuda.synchronize()
+    compare_output(o, O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
+                                   refv["v_f8"], refv["v_scale"], causal=False, sm_scale=0.125,
+                                   delta_s=ds_ref))
+
+
+def test_smooth_q_lse(gpu_lib):
+    q, k, v = _biased_q_inputs(1, 4, 2, 300, 128, torch.bfloat16, seed=52)
+    sm = 1 / math.sqrt(128)
+    qk, vq, ds, ref, refv, ds_ref = _check_smooth_q(gpu_lib, q, k, v, sm)
+    o0 = gpu_lib.sage_attn_fwd(qk, vq, causal=True, sm_scale=sm, out_dtype=torch.bfloat16,
+                               delta_s=ds)
+    o1, lse = gpu_lib.sage_attn_fwd_lse(qk, vq, causal=True, sm_scale=sm,
+                                        out_dtype=torch.bfloat16, delta_s=ds)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1)
+    _, l_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
+                            refv["v_f8"], refv["v_scale"], causal=True, sm_scale=sm,
+                            return_lse=True, delta_s=ds_ref)
+    # exact exponent form; plus the FP32 Delta S error (log2 units -> natural log)
+    ks = (k.float().numpy() - ref["k_mean"][:, :, None, :]).astype(np.float32)
+    absb = np.einsum("bhic,bhjc->bhij", np.abs(ref["q_mean"]).astype(np.float64),
+                     np.repeat(np.abs(ks).astype(np.float64), 2, axis=1))
+    ds_err = (128 + 4) * 2.0 ** -24 * sm * absb.max(axis=(2, 3))[..., None]
+    err = np.abs(to_np(lse).astype(np.float64) - l_ref)
+    assert np.all(err <= _lse_tol(300, 0.0) + ds_err), err.max()
+
+
+def test_smooth_q_tracks_exact_attention(gpu_lib):
+    """End to end (sageattn): on Q with a shared channel bias, smoothing Q brings the
+    quantized result closer to exact FP64 attention than quantizing Q directly."""
+    q, k, v = _biased_q_inputs(1, 4, 2, 512, 128, torch.float16, seed=53, qbias=3.0)
+    sm = 1 / math.sqrt(128)
+    ex = O.attn_exact(q, k, v, causal=True, sm_scale=sm)
+    rl1 = {}
+    for sq in (False, True):
+        o = gpu_lib.sageattn(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=True, sm_scale=sm,
+                             smooth_q=sq)
+        torch.cuda.synchronize()
+        m = O.metrics(to_np(o).astype(np.float64), ex)
+        rl1[sq] = m["rel_l1"]
+        assert m["cos"] >= 0.998, (sq, m)
+    assert rl1[True] < rl1[False], rl1
+
+
 # ------------------------------------------------------------------ the workloads
 
-def _workload_check(gpu_lib, name, heads, nrows, seed=0, q_group=128):
+def _workload_check(gpu_lib, name, heads, nrows, seed=0, q_group=128, smooth_q=False):
     w = W.get(name)
-    print(f"workload {name} q_group {q_group}: generating", flush=True)
+    print(f"workload {name} q_group {q_group} smooth_q {smooth_q}: generating", flush=True)
     t = W.generate(w)
     plan = gpu_lib.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal,
-                            q_group=q_group)
+                            q_group=q_group, smooth_q=smooth_q)
     qd, kd, vd = t["q"].to(DEV), t["k"].to(DEV), t["v"].to(DEV)
     o = plan(qd, kd, vd)
     torch.cuda.synchronize()
@@ -251,8 +369,10 @@ def _workload_check(gpu_lib, name, heads, nrows, seed=0, q_group=128):
     qsel = torch.stack([t["q"][b, h] for b, h in heads])[None]
     ksel = torch.stack([t["k"][b, h] for b, h in hk_set])[None]
     vsel = torch.stack([t["v"][b, h] for b, h in hk_set])[None]
-    ref = O.quantize_qk(qsel, ksel, q_group=q_group)
+    ref = O.quantize_qk(qsel, ksel, q_group=q_group, smooth_q=smooth_q)
     refv = O.quantize_v(vsel)
+    if smooth_q:
+        assert np.array_equal(sub(to_np(plan.qk["q_mean"]), heads), ref["q_mean"][0])
     assert np.array_equal(sub(to_np(plan.qk["k_mean"]), hk_set), ref["k_mean"][0])
     assert np.array_equal(sub(to_np(plan.qk["q_i8"]), heads), ref["q_i8"][0])
     assert np.array_equal(sub(to_np(plan.qk["q_scale"]), heads), ref["q_scale"][0])
@@ -271,10 +391,17 @@ def _workload_check(gpu_lib, name, heads, nrows, seed=0, q_group=128):
     o_ref = np.zeros((len(heads), len(rows), w.d))
     for j, (b, h) in enumerate(heads):
         kvj = kv_index[j]
+        ds = None
+        if smooth_q:
+            ds = O.delta_s(ref["q_mean"][:, j:j + 1], ksel[:, kvj:kvj + 1],
+                           ref["k_mean"][:, kvj:kvj + 1])
+            _check_delta_s_table(to_np(plan.delta_s[b, h]), ds[0, 0], ref["q_mean"][0, j],
+                                 ksel[0, kvj].float().numpy(), ref["k_mean"][0, kvj], w.sm_scale)
         o1 = O.attn_quant(qsel_i8[:, j:j + 1], ref["q_scale"][:, j:j + 1],
                           ref["k_i8"][:, kvj:kvj + 1], ref["k_scale"][:, kvj:kvj + 1],
                           refv["v_f8"][:, kvj:kvj + 1], refv["v_scale"][:, kvj:kvj + 1],
-                          causal=w.causal, sm_scale=w.sm_scale, rows=rows, blkq=q_group)
+                          causal=w.causal, sm_scale=w.sm_scale, rows=rows, blkq=q_group,
+                          delta_s=ds)
         o_ref[j] = o1[0, 0]
     o_gpu = torch.stack([o[b, h, torch.from_numpy(rows).to(DEV)] for b, h in heads])
     m = compare_output(o_gpu, o_ref)
@@ -302,6 +429,15 @@ def test_workload_parity(gpu_lib, name, heads, nrows):
 ])
 def test_workload_parity_q_group(gpu_lib, name, heads, nrows, q_group):
     _workload_check(gpu_lib, name, heads, nrows, q_group=q_group)
+
+
+@pytest.mark.parametrize("name,heads,nrows,q_group", [
+    ("llm_prefill", [(0, 3)], 128, 128),
+    ("video_dit", [(0, 11)], 64, 1),
+    ("sweep@N4096", [(3, 2)], 96, 128),
+])
+def test_workload_parity_smooth_q(gpu_lib, name, heads, nrows, q_group):
+    _workload_check(gpu_lib, name, heads, nrows, q_group=q_group, smooth_q=True)
 
 
 # ------------------------------------------------------------------ log-sum-exp (LSE)
