@@ -43,17 +43,32 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   __shared__ __attribute__((aligned(16))) char lds[2][2 * KBYTES + DSBYTES];
 
   // ---- which (b, kv head, q tile, group member) this workgroup computes.
-  // Logical order: the `group` query heads that share a kv head are
-  // adjacent and walk the q tiles together (they read the same K/V tiles);
-  // causal runs the heaviest q tiles first.
-  const int lid = xcd_remap(blockIdx.x, total);
+  // Non-causal (equal work per workgroup): each XCD takes a contiguous range
+  // of logical ids, in which the `group` query heads that share a kv head are
+  // adjacent and walk the q tiles together (they read the same K/V tiles).
+  // Causal (q tile qt does qt+1 key tiles): the grid runs the q tiles
+  // heaviest first, across all heads, with the (b, kv head) index varying
+  // fastest.  The hardware deals consecutive ids round-robin to the 8 XCDs,
+  // so every XCD gets the same mix of tile counts, each in heaviest-first
+  // order, and when B*H_kv is a multiple of 8 each (b, kv head) stays on one
+  // XCD (its K/V tiles stay in that XCD's L2).
   const int group = H / H_kv;
-  int rest = lid;
-  const int gm = rest % group; rest /= group;
-  int qt = rest % nqt; rest /= nqt;
-  const int hk = rest % H_kv;
-  const int b = rest / H_kv;
-  if (CAUSAL) qt = nqt - 1 - qt;
+  int gm, qt, hk, b;
+  if (CAUSAL) {
+    const int nbk = total / (nqt * group);   // B * H_kv
+    int rest = blockIdx.x;
+    const int bk = rest % nbk; rest /= nbk;
+    gm = rest % group;
+    qt = nqt - 1 - rest / group;
+    b = bk / H_kv;
+    hk = bk % H_kv;
+  } else {
+    int rest = xcd_remap(blockIdx.x, total);
+    gm = rest % group; rest /= group;
+    qt = rest % nqt; rest /= nqt;
+    hk = rest % H_kv;
+    b = rest / H_kv;
+  }
   const int h = hk * group + gm;
 
   const int tid = threadIdx.x, lane = tid % 64;
