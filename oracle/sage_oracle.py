@@ -25,6 +25,7 @@ import math
 import numpy as np
 
 from . import fp8_e4m3
+from . import mxfp4
 
 BLKQ = 128        # Q tokens per INT8 scale (Algorithm 1's b_q, detail page sec. 3)
 BLKK = 64         # K tokens per INT8 scale (Algorithm 1's b_kv)
@@ -198,6 +199,24 @@ def quantize_v(v):
     return dict(v_f8=codes, v_scale=s)
 
 
+# MXFP4 V (the SageAttention3 synthesis page names MXFP4 as the FP4 format
+# of MI350-class GPUs; the format is the OCP microscaling standard, see
+# ``mxfp4``).  Reading: V's blocks are 32 consecutive keys of one channel,
+# the contraction axis of P V; keys past N are zero (a zero block decodes to
+# 0 whatever its scale).
+
+def quantize_v_mxfp4(v):
+    """v: [B, H_kv, N, d] -> dict(v_f4 E2M1 codes uint8 [B,H_kv,Np,d],
+    v_e8 int64 exponents [B,H_kv,Np/32,d]), Np = N rounded up to 32."""
+    v32 = _f32(v)
+    B, Hk, n, d = v32.shape
+    npad = -(-n // mxfp4.MX_BLOCK) * mxfp4.MX_BLOCK
+    vp = np.zeros((B, Hk, npad, d))
+    vp[:, :, :n] = v32
+    codes, e = mxfp4.quantize_blocks(vp, axis=-2)
+    return dict(v_f4=codes, v_e8=e)
+
+
 # ---------------------------------------------------------------------------
 # (i) Exact attention: the plain definition, float64.
 
@@ -267,7 +286,7 @@ def softmax_rows(q, k, *, causal: bool, sm_scale: float, b=0, h=0, hk=None):
 def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
                kv_tile: int = KV_TILE, rows=None, heads=None,
                quantize_p: bool = True, blkq: int = BLKQ, blkk: int = BLKK,
-               return_lse: bool = False, delta_s=None):
+               return_lse: bool = False, delta_s=None, pv: str = "fp8"):
     """Quantized attention, float64 result [B,H,len(rows),d].
 
     qc int8 [B,H,N,d], qs f32 [B,H,nq]; kc int8 [B,H_kv,N,d], ks f32
@@ -279,6 +298,9 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
     K - mean(K); ``lse_correction`` restores the unsmoothed value.
     ``delta_s`` ([B,H,ceil(N/128),N], from ``delta_s``): with smoothed-Q codes,
     sm_scale * Delta S[query's 128-block, key] is added to every score.
+    ``pv="mxfp4"``: vc, vs are ``quantize_v_mxfp4``'s codes and exponents, and
+    P~ of each 32-key block of a row is MX-quantized (no factor 448) before
+    the product (the reading stated at ``quantize_v_mxfp4``).
     """
     B, H, N, d = qc.shape
     grp = H // kc.shape[1]
@@ -289,9 +311,14 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
     out = np.zeros((B, H, len(rows), d))
     lse = np.zeros((B, H, len(rows)))
     chunk = max(1, (1 << 24) // npad)               # bound the [rows, keys] temporaries
+    mx = pv == "mxfp4"
+    assert pv in ("fp8", "mxfp4") and (not mx or kv_tile % mxfp4.MX_BLOCK == 0)
     for b, h in (heads or [(b, h) for b in range(B) for h in range(H)]):
         hk = h // grp
-        vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
+        if mx:
+            vdq = mxfp4.dequantize_blocks(vc[b, hk], vs[b, hk], axis=0)[:N]
+        else:
+            vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
         kf = kc[b, hk].astype(np.float64).T
         ksc = ks[b, hk, key_blk].astype(np.float64)[None, :]
         for r0 in range(0, len(rows), chunk):
@@ -310,7 +337,13 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
             m_run = np.maximum.accumulate(st.max(axis=2), axis=1)        # [R, nt]
             m_fin = m_run[:, -1:]
             pt = np.exp(st - m_run[:, :, None])                          # P tilde in [0, 1]
-            pq = fp8_e4m3.round_to_e4m3(P_SCALE * pt) if quantize_p else P_SCALE * pt
+            if mx:
+                # P~ in MX blocks of 32 consecutive keys; scaled back to P~ * 448
+                # so the rest of the recursion is shared with the FP8 form
+                codes, e = mxfp4.quantize_blocks(pt.reshape(len(rr), npad), axis=-1)
+                pq = (P_SCALE * mxfp4.dequantize_blocks(codes, e)).reshape(pt.shape)
+            else:
+                pq = fp8_e4m3.round_to_e4m3(P_SCALE * pt) if quantize_p else P_SCALE * pt
             carry = np.exp(m_run - m_fin)                                # exp(m_t - m_T)
             l = np.sum(pt.sum(axis=2) * carry, axis=1)
             w = (pq * carry[:, :, None]).reshape(len(rr), npad)[:, :N]
@@ -334,7 +367,7 @@ def lse_correction(q, k_mean, *, sm_scale: float):
 
 def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
                          b=0, h=0, hk=None, blkq=BLKQ, blkk=BLKK, return_lse=False,
-                         delta_s=None):
+                         delta_s=None, pv="fp8"):
     """Literal online recursion of Algorithm 1 in pure Python loops (tiny sizes).
 
     Used to pin ``attn_quant``'s closed form: the same steps, one key tile at
@@ -343,7 +376,11 @@ def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
     """
     n, d = qc.shape[2], qc.shape[3]
     hk = h if hk is None else hk
-    vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
+    mx = pv == "mxfp4"
+    if mx:
+        vdq = mxfp4.dequantize_blocks(vc[b, hk], vs[b, hk], axis=0)
+    else:
+        vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
     out = np.zeros((n, d))
     lse = np.zeros(n)
     for i in range(n):
@@ -365,10 +402,17 @@ def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
             alpha = math.exp(m - m_new) if m != -math.inf else 0.0
             l = alpha * l
             o = [alpha * x for x in o]
-            for j, sv in srow.items():
-                pt = math.exp(sv - m_new)
+            pts = {j: math.exp(sv - m_new) for j, sv in srow.items()}
+            for j, pt in pts.items():
                 l += pt
-                pq = float(fp8_e4m3.round_to_e4m3(P_SCALE * pt))
+                if mx:
+                    # the shared exponent of j's block of 32 keys (masked keys: 0)
+                    j0 = j - j % mxfp4.MX_BLOCK
+                    amax = max(pts.get(jj, 0.0) for jj in range(j0, j0 + mxfp4.MX_BLOCK))
+                    sc = 2.0 ** int(mxfp4.scale_exponent(amax))
+                    pq = P_SCALE * float(mxfp4.decode(mxfp4.encode(pt / sc))) * sc
+                else:
+                    pq = float(fp8_e4m3.round_to_e4m3(P_SCALE * pt))
                 for c in range(d):
                     o[c] += pq * vdq[j, c]
             m = m_new

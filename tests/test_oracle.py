@@ -12,6 +12,7 @@ import torch
 
 import workloads as W
 from oracle import fp8_e4m3 as F8
+from oracle import mxfp4 as MX
 from oracle import sage_oracle as O
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -533,6 +534,108 @@ def test_smooth_q_quantized_tracks_exact_attention():
         rl1[sq] = O.metrics(o, ex)["rel_l1"]
     assert O.metrics(o, ex)["cos"] >= 0.998
     assert rl1[True] < rl1[False], rl1
+
+
+# ------------------------------------------------------------------ MXFP4 PV
+
+_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_golden_table():
+    rows = [l.split() for l in open(os.path.join(GOLD, "e2m1_codes.txt"))
+            if l.strip() and not l.startswith("#")]
+    for c, v in rows:
+        got = MX.decode(int(c))
+        assert got == float(v) and math.copysign(1, got) == math.copysign(1, float(v)), (c, v)
+    # every code but -0 survives encode(decode(.))
+    codes = np.arange(16)
+    back = MX.encode(MX.decode(codes))
+    assert (back[codes != 8] == codes[codes != 8]).all() and back[8] == 0
+
+
+def test_e2m1_encode_is_nearest_with_ties_to_even():
+    g = np.random.default_rng(61)
+    grid = np.array(sorted(set([-v for v in _E2M1] + _E2M1)))
+    x = np.concatenate([g.uniform(-7, 7, 20000),
+                        (np.array(_E2M1[1:]) + np.array(_E2M1[:-1])) / 2,       # midpoints
+                        -(np.array(_E2M1[1:]) + np.array(_E2M1[:-1])) / 2])
+    v = MX.decode(MX.encode(x))
+    xc = np.clip(x, -6, 6)
+    d = np.abs(grid[None, :] - xc[:, None])
+    best = d.min(axis=1)
+    assert np.allclose(np.abs(v - xc), best)                       # nearest (after saturation)
+    # ties: the chosen code is even (mantissa bit 0)
+    tie = (np.sort(d, axis=1)[:, 1] - best) < 1e-12
+    assert tie.sum() >= 14
+    assert (MX.encode(x[tie]) & 1 == 0).all()
+    assert (MX.encode(np.array([7.0, 100.0, -9.0])) == [7, 7, 15]).all()   # saturation
+
+
+def test_mx_scale_rule():
+    g = np.random.default_rng(62)
+    x = g.standard_normal((50, 64)) * np.exp(g.uniform(-30, 30, (50, 1)))
+    codes, e = MX.quantize_blocks(x, axis=-1)
+    assert e.shape == (50, 2)
+    amax = np.abs(x.reshape(50, 2, 32)).max(axis=-1)
+    r = amax / np.exp2(e.astype(np.float64))
+    assert ((r >= 4) & (r < 8)).all()                  # amax lands in E2M1's top binade
+    dq = MX.dequantize_blocks(codes, e, axis=-1)
+    # within half a grid step of x / 2^e (saturation only above 6)
+    step = np.where(np.abs(x / np.exp2(np.repeat(e, 32, axis=-1))) <= 2, 0.25,
+                    np.where(np.abs(x / np.exp2(np.repeat(e, 32, axis=-1))) <= 4, 0.5, 1.0))
+    err = np.abs(dq - x) / np.exp2(np.repeat(e, 32, axis=-1))
+    sat = np.abs(x / np.exp2(np.repeat(e, 32, axis=-1))) > 6
+    assert (err[~sat] <= step[~sat] + 1e-12).all()
+    z, ez = MX.quantize_blocks(np.zeros((1, 32)))
+    assert (z == 0).all() and ez[0, 0] == -127
+    assert MX.scale_exponent(1.0) == -2 and MX.scale_exponent(6.0) == 0
+    assert MX.scale_exponent(3.999) == -1 and MX.scale_exponent(2.0 ** -140) == -127
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mxfp4_pv_closed_form_matches_recursion(causal):
+    g = np.random.default_rng(63)
+    n, d = 100, 8
+    q = torch.from_numpy(g.standard_normal((1, 2, n, d)).astype(np.float32) * 2).half()
+    k = torch.from_numpy((g.standard_normal((1, 1, n, d)) + 1).astype(np.float32)).half()
+    v = torch.from_numpy(g.standard_normal((1, 1, n, d)).astype(np.float32)).half()
+    z = O.quantize_qk(q, k)
+    v4 = O.quantize_v_mxfp4(v)
+    assert v4["v_f4"].shape == (1, 1, 128, d) and v4["v_e8"].shape == (1, 1, 4, d)
+    kw = dict(causal=causal, sm_scale=0.35, kv_tile=64, pv="mxfp4")
+    args = (z["q_i8"], z["q_scale"], z["k_i8"], z["k_scale"], v4["v_f4"], v4["v_e8"])
+    a, la = O.attn_quant(*args, return_lse=True, **kw)
+    for h in range(2):
+        r, lr = O.attn_quant_recursive(*args, h=h, hk=0, return_lse=True, **kw)
+        assert np.abs(a[0, h] - r).max() < 1e-12
+        assert np.abs(la[0, h] - lr).max() < 1e-12
+
+
+def test_mxfp4_pv_constant_v_and_accuracy():
+    # constant V is represented exactly by MX blocks, so O = v * sum(Pq) / l
+    # with l the unquantized sum; on random data MXFP4 PV is close to exact
+    # attention but less accurate than FP8 PV (the pages rank MXFP4 below
+    # finer formats)
+    w = W.get("tiny")
+    t = W.generate(w)
+    qz = O.quantize_qk(t["q"], t["k"])
+    ex = O.attn_exact(t["q"], t["k"], t["v"], causal=False, sm_scale=w.sm_scale)
+    v4 = O.quantize_v_mxfp4(t["v"])
+    vz = O.quantize_v(t["v"])
+    args = (qz["q_i8"], qz["q_scale"], qz["k_i8"], qz["k_scale"])
+    o4 = O.attn_quant(*args, v4["v_f4"], v4["v_e8"], causal=False, sm_scale=w.sm_scale,
+                      pv="mxfp4")
+    o8 = O.attn_quant(*args, vz["v_f8"], vz["v_scale"], causal=False, sm_scale=w.sm_scale)
+    m4, m8 = O.metrics(o4, ex), O.metrics(o8, ex)
+    # the SageAttention3 synthesis page quotes CosSim 98.37 % for MXFP4
+    assert m4["cos"] >= 0.975 and m8["rel_l1"] < m4["rel_l1"], (m4, m8)
+    vc = torch.full_like(t["v"], 1.5)
+    vc4 = O.quantize_v_mxfp4(vc)
+    oc = O.attn_quant(*args, vc4["v_f4"], vc4["v_e8"], causal=True, sm_scale=w.sm_scale,
+                      pv="mxfp4")
+    # O = 1.5 * sum(Pq) / sum(P~): each E2M1 rounding (and the saturation of
+    # the [6, 8) top of a block) moves an element by at most 1/4 of itself
+    assert np.abs(oc - 1.5).max() <= 0.25 * 1.5
 
 
 def test_quantized_vs_exact_tiny_full():
