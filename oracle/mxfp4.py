@@ -18,7 +18,8 @@ it; what follows is that standard's definition:
   - an element is x / scale rounded to nearest, ties to the even code, and
     saturated to +-6.
 Readings: an all-zero block gets the smallest scale code 0 (2^-127) and zero
-codes; exponents are clamped to E8M0's range [-127, 127].
+codes (of the values' signs); exponents are clamped to E8M0's range
+[-127, 127].
 """
 from __future__ import annotations
 
@@ -39,7 +40,8 @@ def decode(codes) -> np.ndarray:
 
 def encode(x) -> np.ndarray:
     """float -> E2M1 code (uint8 0..15): nearest magnitude, ties to the even
-    code, saturated to 6."""
+    code, saturated to 6; the sign bit is copied, so a negative value that
+    rounds to zero gives -0 (code 8), as in IEEE rounding."""
     x = np.asarray(x, dtype=np.float64)
     a = np.minimum(np.abs(x), E2M1_MAX)
     # the grid is 0.5-spaced below 2 (codes 0..4), 1-spaced to 4 (codes
@@ -48,7 +50,7 @@ def encode(x) -> np.ndarray:
     mid = 4.0 + np.rint(a - 2.0)                         # codes 4..6 where 2 <= a <= 4
     hi = 6.0 + np.rint((a - 4.0) / 2.0)                  # codes 6..7 where 4 <= a <= 6
     code = np.where(a <= 2.0, lo, np.where(a <= 4.0, mid, hi)).astype(np.int64)
-    return (code | np.where((x < 0) & (code > 0), 8, 0)).astype(np.uint8)
+    return (code | np.where(np.signbit(x), 8, 0)).astype(np.uint8)
 
 
 def scale_exponent(amax) -> np.ndarray:

@@ -547,10 +547,10 @@ def test_e2m1_golden_table():
     for c, v in rows:
         got = MX.decode(int(c))
         assert got == float(v) and math.copysign(1, got) == math.copysign(1, float(v)), (c, v)
-    # every code but -0 survives encode(decode(.))
+    # every code survives encode(decode(.)), -0 included (the sign is copied)
     codes = np.arange(16)
-    back = MX.encode(MX.decode(codes))
-    assert (back[codes != 8] == codes[codes != 8]).all() and back[8] == 0
+    assert (MX.encode(MX.decode(codes)) == codes).all()
+    assert (MX.encode(np.array([-0.1, -0.0, 0.0, 0.2])) == [8, 8, 0, 0]).all()
 
 
 def test_e2m1_encode_is_nearest_with_ties_to_even():
