@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--smooth-q", action="store_true",
                     help="smooth Q by its 128-block means and add the Delta S table back "
                          "(sage_delta_s, timed separately)")
+    ap.add_argument("--pv", default="fp8", choices=("fp8", "mxfp4"),
+                    help="P V format: FP8 E4M3 (the method's) or MXFP4 on the FP4 matrix cores")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB (3 times), "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -149,11 +151,11 @@ def main():
         names.append("gqa_long")
         for name in names:
             r = run_config(W.get(name), max(args.steps, 5), args.warmup, q_group=args.q_group,
-                           smooth_q=args.smooth_q)
+                           smooth_q=args.smooth_q, pv=args.pv)
             print(json.dumps(r), flush=True)
         return
     res = run_config(W.get(args.config), args.steps, args.warmup, full=True,
-                     q_group=args.q_group, smooth_q=args.smooth_q)
+                     q_group=args.q_group, smooth_q=args.smooth_q, pv=args.pv)
     if args.lse:
         res["lse"] = run_lse(W.get(args.config), args.steps, args.warmup)
     if not args.no_cpu:
@@ -206,7 +208,7 @@ def run_lse(w, steps: int, warmup: int) -> dict:
 
 
 def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 128,
-               smooth_q: bool = False) -> dict:
+               smooth_q: bool = False, pv: str = "fp8") -> dict:
     """Time `steps` whole steps of workload `w` (inputs resident on the GPU)."""
     import torch
     import quantized_attention_amd as qa
@@ -216,7 +218,7 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
     q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
     del t
     plan = qa.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal, device=dev,
-                       q_group=q_group, smooth_q=smooth_q)
+                       q_group=q_group, smooth_q=smooth_q, pv=pv)
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(warmup):
@@ -235,7 +237,7 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
         if smooth_q:
             qa.sage_delta_s(k, plan.qk, plan.sm_scale, out=plan.delta_s)
         e[2].record(stream)
-        qa.sage_quant_v(v, out=plan.vq, workspace=plan.ws_v)
+        plan.quant_v(v)
         e[3].record(stream)
         plan.attn()
         e[4].record(stream)
@@ -252,7 +254,8 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
     # algorithmic bytes of the quantizers: read 2 B + write 1 B per element of Q, K and V
     quant_bytes = 3 * (w.B * w.H * w.N * w.d + 2 * w.B * w.H_kv * w.N * w.d)
     # the committed counters were taken with the default 128-token Q groups
-    traffic = traffic_from_profile(w.name) if q_group == 128 and not smooth_q else None
+    traffic = (traffic_from_profile(w.name) if q_group == 128 and not smooth_q and pv == "fp8"
+               else None)
 
     res = {
         "metric": "quantized attn fwd TOPS at N=32K hd128 (4BHN^2d/t); % of MFMA INT8/FP8 peak",
@@ -269,7 +272,7 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
         "data": "synthetic (seeded normals, shared K channel bias)",
         "config": {"workload": w.description, "name": w.name, "B": w.B, "H": w.H,
                    "H_kv": w.H_kv, "N": w.N, "d": w.d, "causal": w.causal,
-                   "in_dtype": w.dtype, "q_group": q_group, "smooth_q": smooth_q},
+                   "in_dtype": w.dtype, "q_group": q_group, "smooth_q": smooth_q, "pv": pv},
         "attn_tops": round(attn_tops, 2),
         "attn_ms": round(t_attn, 4),
         "quant_qk_ms": round(t_qk, 4),

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 4
+#define SAGE_ABI_VERSION 5
 
 /* Q tokens per INT8 scale (default), K tokens per INT8 scale. */
 #define SAGE_BLKQ 128
@@ -106,6 +106,8 @@ typedef struct {
   size_t ws_quant_v;  /* workspace bytes sage_quant_v needs                     */
   size_t q_mean;    /* float [B][H][ceil(N/128)][d]   (smooth Q only)           */
   size_t delta_s;   /* float [B][H][ceil(N/128)][N]   (smooth Q only)           */
+  size_t v_f4;      /* uint8 [B][H_kv][ceil(N/128)*64*d]  (MXFP4 V codes)       */
+  size_t v_e8;      /* uint8 [B][H_kv][ceil(N/128)*512]   (MXFP4 V scales)      */
 } sage_sizes;
 
 /*
@@ -237,6 +239,40 @@ sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const in
 sage_status sage_lse_correction(const void* q, sage_dtype dtype, const float* k_mean, int B, int H,
                                 int H_kv, int N, int d, float sm_scale, float* corr,
                                 void* stream);
+
+/*
+ * MXFP4 P V (the SageAttention3 synthesis page names MXFP4, the OCP
+ * microscaling format, as the FP4 format of MI350-class GPUs): V and P~ in
+ * E2M1 with one E8M0 scale 2^e per 32 consecutive keys, on the FP4 matrix
+ * cores at twice the FP8 rate.  The format: e = floor(log2 amax) - 2
+ * (clamped to [-127, 127]; an all-zero block takes -127), code =
+ * RNE(x / 2^e) saturated to +-6.
+ *
+ * Step 3 in MXFP4: v [B][H_kv][N][d] in `dtype`.
+ *   v_f4: per (b, kv head), 128-key tiles of 64*d bytes: 2 key halves (h:
+ *     keys h*64 ..) x d/32 channel blocks (cb) x 64 lanes (L) x 16 bytes;
+ *       offset = tile*64*d + ((h*(d/32) + cb)*64 + L)*16 + p/2
+ *     holds in nibble p%2 (low first) the code of V[key][chan], chan = cb*32
+ *     + L%32, key = tile*128 + h*64 + (L/32)*32 + 8*((p%16)/4) + 4*(p/16) +
+ *     p%4 (the key order of P in the kernel's registers); keys >= N are 0.
+ *   v_e8: per (b, kv head), 512 bytes per tile: byte (h*64 + L)*4 + cb is
+ *     e + 127 for the 32 keys of chunk (tile, h, cb, L) (bytes cb >= d/32
+ *     unused).  Deterministic, bit-exact.
+ */
+sage_status sage_quant_v_mxfp4(const void* v, sage_dtype dtype, int B, int H_kv, int N, int d,
+                               uint8_t* v_f4, uint8_t* v_e8, void* stream);
+
+/*
+ * Step 4 with MXFP4 P V: as sage_attn_fwd_lse (lse may be NULL here), with V
+ * from sage_quant_v_mxfp4 and, per tile and row, P~ quantized in blocks of
+ * 32 consecutive keys: e = floor(log2 max P~) - 2, codes RNE(P~ / 2^e); l
+ * sums the unquantized P~.  No Delta S (smoothed Q is not taken here).
+ */
+sage_status sage_attn_fwd_mxfp4(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                const float* k_scale, const uint8_t* v_f4, const uint8_t* v_e8,
+                                void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
+                                int B, int H, int H_kv, int N, int d, int q_group, int causal,
+                                float sm_scale, void* stream);
 
 /*
  * Diagnostic: the exact int32 dot products sum_c q_i8[b][h][i][c] *

@@ -16,9 +16,11 @@ Entry points (same names as the C ABI):
         -> dict(q_i8, q_scale, k_i8, k_scale, k_mean[, q_mean])
     sage_delta_s(k, qk, sm_scale) -> fp32 [B, H, ceil(N/128), N] (smooth Q)
     sage_quant_v(v) -> dict(v_f8, v_scale)
+    sage_quant_v_mxfp4(v) -> dict(v_f4, v_e8) (MXFP4 V)
     sage_attn_fwd(qk, vq, causal=..., sm_scale=..., out_dtype=..., delta_s=None) -> o
     sage_attn_fwd_lse(qk, vq, causal=..., sm_scale=..., lse_corr=None, delta_s=None)
         -> (o, lse)
+    sage_attn_fwd_mxfp4(qk, vq4, causal=..., sm_scale=..., return_lse=False) -> o or (o, lse)
     sage_lse_correction(q, k_mean, sm_scale) -> fp32 [B, H, N]
     sage_qk_int32(q_i8, k_i8, b, h) -> int32 [N, N] (diagnostic)
 and the composition ``sageattn(q, k, v, is_causal=False, sm_scale=None,
@@ -27,7 +29,9 @@ consecutive Q tokens per scale: 128 (per block), 32 (per wave, the per-warp
 granularity) or 1 (per query, the per-thread granularity); the attention
 entry points read it from the length of ``q_scale``.  ``smooth_q`` subtracts each
 128-token Q block's mean before quantizing and adds the Delta S table back to
-the scores (Algorithm 1's GEMV compensation).
+the scores (Algorithm 1's GEMV compensation).  ``pv="mxfp4"`` runs P V in MXFP4
+(E2M1 with E8M0 scales per 32 keys, the OCP format the pages name for MI350-class
+GPUs) on the FP4 matrix cores.
 """
 from __future__ import annotations
 
@@ -38,7 +42,8 @@ import os
 import torch
 
 __all__ = ["SageError", "library_path", "load_library", "sage_buffer_sizes", "sage_quant_qk",
-           "sage_quant_v", "sage_delta_s", "sage_attn_fwd", "sage_attn_fwd_lse",
+           "sage_quant_v", "sage_quant_v_mxfp4", "sage_delta_s", "sage_attn_fwd",
+           "sage_attn_fwd_lse", "sage_attn_fwd_mxfp4",
            "sage_lse_correction",
            "sage_qk_int32", "sageattn", "SagePlan", "BLKQ", "BLKK", "KV_TILE", "Q_GROUPS"]
 
@@ -57,7 +62,7 @@ class SageError(RuntimeError):
 class _Sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_f8", "v_scale", "o",
-        "ws_quant_qk", "ws_quant_v", "q_mean", "delta_s")]
+        "ws_quant_qk", "ws_quant_v", "q_mean", "delta_s", "v_f4", "v_e8")]
 
 
 _lib = None
@@ -90,9 +95,13 @@ def load_library():
     lib.sage_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i,
                                       i, i, ctypes.c_float, vp]
     lib.sage_lse_correction.argtypes = [vp, i, vp, i, i, i, i, i, ctypes.c_float, vp, vp]
+    lib.sage_quant_v_mxfp4.argtypes = [vp, i, i, i, i, i, vp, vp, vp]
+    lib.sage_attn_fwd_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i,
+                                        i, ctypes.c_float, vp]
     lib.sage_qk_int32.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp]
     for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_delta_s", "sage_quant_v", "sage_attn_fwd",
-              "sage_attn_fwd_lse", "sage_lse_correction", "sage_qk_int32"):
+              "sage_attn_fwd_lse", "sage_lse_correction", "sage_qk_int32", "sage_quant_v_mxfp4",
+              "sage_attn_fwd_mxfp4"):
         getattr(lib, f).restype = i
     _lib = lib
     return lib
@@ -201,6 +210,54 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *,
         _stream(stream, q.device))
     _check(st, "sage_quant_qk")
     return out
+
+
+def _alloc_v4(B, H_kv, N, d, device):
+    nt = -(-N // KV_TILE)
+    return dict(
+        v_f4=torch.empty((B, H_kv, nt * KV_TILE * d // 2), dtype=torch.uint8, device=device),
+        v_e8=torch.empty((B, H_kv, nt * 512), dtype=torch.uint8, device=device),
+    )
+
+
+def sage_quant_v_mxfp4(v: torch.Tensor, *, out=None, stream=None) -> dict:
+    """MXFP4 quantization of V (E2M1 codes, E8M0 scale per 32 keys of a channel) into
+    the FP4 fragment layout of sage.h."""
+    _need_gpu(v)
+    B, H_kv, N, d = v.shape
+    out = out or _alloc_v4(B, H_kv, N, d, v.device)
+    st = load_library().sage_quant_v_mxfp4(v.data_ptr(), _dt(v.dtype), B, H_kv, N, d,
+                                           out["v_f4"].data_ptr(), out["v_e8"].data_ptr(),
+                                           _stream(stream, v.device))
+    _check(st, "sage_quant_v_mxfp4")
+    return out
+
+
+def sage_attn_fwd_mxfp4(qk: dict, vq4: dict, *, causal: bool, sm_scale: float,
+                        out_dtype=torch.float16, return_lse: bool = False, lse_corr=None,
+                        out=None, lse=None, stream=None):
+    """Attention with MXFP4 P V; returns O, or (O, lse) with return_lse."""
+    q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
+    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq4["v_f4"], vq4["v_e8"])
+    B, H, N, d = q_i8.shape
+    H_kv = k_i8.shape[1]
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q_i8.device)
+    _need_gpu(out)
+    if lse_corr is not None:
+        _need_gpu(lse_corr)
+        if lse_corr.shape != (B, H, N) or lse_corr.dtype != torch.float32:
+            raise ValueError("lse_corr must be float32 [B, H, N]")
+    st = load_library().sage_attn_fwd_mxfp4(
+        q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
+        vq4["v_f4"].data_ptr(), vq4["v_e8"].data_ptr(), out.data_ptr(), _dt(out.dtype),
+        _ptr(lse) if return_lse else None, _ptr(lse_corr) if return_lse else None, B, H, H_kv, N,
+        d, _q_group_of(qk["q_scale"], N), int(bool(causal)), float(sm_scale),
+        _stream(stream, q_i8.device))
+    _check(st, "sage_attn_fwd_mxfp4")
+    return (out, lse) if return_lse else out
 
 
 def sage_delta_s(k: torch.Tensor, qk: dict, sm_scale: float, *, out=None,
@@ -328,12 +385,22 @@ def sage_qk_int32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, *,
 
 def sageattn(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
              smooth_k: bool = True, return_lse: bool = False, q_group: int = BLKQ,
-             smooth_q: bool = False):
+             smooth_q: bool = False, pv: str = "fp8"):
     """The whole forward pass: quantize Q/K/V, then the attention kernel.
     With return_lse, also the row log-sum-exp of the logits sm_scale q . k
     (corrected for the smoothing of K); returns (o, lse)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    if pv not in ("fp8", "mxfp4"):
+        raise ValueError("pv must be 'fp8' or 'mxfp4'")
+    if pv == "mxfp4":
+        if smooth_q:
+            raise ValueError("smooth_q is not combined with MXFP4 P V")
+        qk = sage_quant_qk(q, k, smooth_k, q_group=q_group)
+        vq4 = sage_quant_v_mxfp4(v)
+        corr = sage_lse_correction(q, qk["k_mean"], sm_scale) if return_lse and smooth_k else None
+        return sage_attn_fwd_mxfp4(qk, vq4, causal=is_causal, sm_scale=sm_scale,
+                                   out_dtype=q.dtype, return_lse=return_lse, lse_corr=corr)
     qk = sage_quant_qk(q, k, smooth_k, q_group=q_group, smooth_q=smooth_q)
     ds = sage_delta_s(k, qk, sm_scale) if smooth_q else None
     vq = sage_quant_v(v)
@@ -349,16 +416,18 @@ class SagePlan:
     """Preallocated buffers for repeated calls on fixed shapes (no allocation per call)."""
 
     def __init__(self, B, H, H_kv, N, d, dtype, causal, sm_scale=None, device="cuda",
-                 q_group=BLKQ, smooth_q=False):
+                 q_group=BLKQ, smooth_q=False, pv="fp8"):
+        if pv not in ("fp8", "mxfp4") or (pv == "mxfp4" and smooth_q):
+            raise ValueError("pv must be 'fp8' or 'mxfp4' (and mxfp4 without smooth_q)")
         self.shape = (B, H, H_kv, N, d)
         self.dtype, self.causal, self.q_group = dtype, causal, q_group
-        self.smooth_q = smooth_q
+        self.smooth_q, self.pv = smooth_q, pv
         self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
         sz = sage_buffer_sizes(B, H, H_kv, N, d, q_group)
         self.qk = _alloc_qk(B, H, H_kv, N, d, device, q_group, smooth_q)
         self.delta_s = (torch.empty((B, H, -(-N // BLKQ), N), dtype=torch.float32, device=device)
                         if smooth_q else None)
-        self.vq = _alloc_v(B, H_kv, N, d, device)
+        self.vq = _alloc_v4(B, H_kv, N, d, device) if pv == "mxfp4" else _alloc_v(B, H_kv, N, d, device)
         self.ws_qk = torch.empty(max(sz["ws_quant_qk"], 16), dtype=torch.uint8, device=device)
         self.ws_v = torch.empty(max(sz["ws_quant_v"], 16), dtype=torch.uint8, device=device)
         self.o = torch.empty((B, H, N, d), dtype=dtype, device=device)
@@ -368,9 +437,19 @@ class SagePlan:
                       workspace=self.ws_qk, stream=stream)
         if self.smooth_q:
             sage_delta_s(k, self.qk, self.sm_scale, out=self.delta_s, stream=stream)
-        sage_quant_v(v, out=self.vq, workspace=self.ws_v, stream=stream)
+        self.quant_v(v, stream)
+
+    def quant_v(self, v, stream=None):
+        if self.pv == "mxfp4":
+            sage_quant_v_mxfp4(v, out=self.vq, stream=stream)
+        else:
+            sage_quant_v(v, out=self.vq, workspace=self.ws_v, stream=stream)
 
     def attn(self, stream=None):
+        if self.pv == "mxfp4":
+            return sage_attn_fwd_mxfp4(self.qk, self.vq, causal=self.causal,
+                                       sm_scale=self.sm_scale, out_dtype=self.dtype, out=self.o,
+                                       stream=stream)
         return sage_attn_fwd(self.qk, self.vq, causal=self.causal, sm_scale=self.sm_scale,
                              out_dtype=self.dtype, delta_s=self.delta_s, out=self.o,
                              stream=stream)

@@ -27,20 +27,27 @@ namespace sage {
 
 // SQ: Q was smoothed by its 128-block means; delta_s holds the Delta S table
 // [B][H][ceil(N/128)][N] (log2 units) that is added to every score.
-template <int D, bool CAUSAL, bool BF16, bool SQ>
+// PV4: P V on the FP4 matrix cores in MXFP4 (v_f8 holds E2M1 codes, v_e8 the
+// E8M0 scale bytes, see quant_v_mxfp4); P~ is quantized per 32 keys of a row.
+template <int D, bool CAUSAL, bool BF16, bool SQ, bool PV4>
 // d = 64 fits three workgroups per CU (168 registers); d = 128, and d = 64
 // with Delta S, two.
 __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_f8, const float* __restrict__ v_scale,
-    const float* __restrict__ delta_s, void* __restrict__ out, float* __restrict__ lse,
+    const uint8_t* __restrict__ v_e8, const float* __restrict__ delta_s,
+    void* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ lse_corr, int H, int H_kv, int N, float sm_log2, int qg_shift,
     int nqt, int total) {
   constexpr int NKC = D / 32;                 // 32-wide channel chunks
-  constexpr int KBYTES = kKvTile * D;         // K tile bytes (== V tile bytes)
-  constexpr int DSBYTES = SQ ? kKvTile * 4 : 0;   // a tile's Delta S values
-  __shared__ __attribute__((aligned(16))) char lds[2][2 * KBYTES + DSBYTES];
+  constexpr int KBYTES = kKvTile * D;         // K tile bytes
+  constexpr int VBYTES = PV4 ? KBYTES / 2 : KBYTES;   // V tile bytes (FP8 or FP4 codes)
+  constexpr int VSBYTES = PV4 ? kMxScaleBytes : 0;    // a tile's MXFP4 V scale bytes
+  constexpr int DSOFF = KBYTES + VBYTES + VSBYTES;    // a tile's Delta S values
+  constexpr int DSBYTES = SQ ? kKvTile * 4 : 0;
+  static_assert(!(SQ && PV4), "Delta S and MXFP4 P V are separate variants");
+  __shared__ __attribute__((aligned(16))) char lds[2][DSOFF + DSBYTES];
 
   // ---- which (b, kv head, q tile, group member) this workgroup computes.
   // Non-causal (equal work per workgroup): each XCD takes a contiguous range
@@ -80,7 +87,8 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   const int8_t* qh = q_i8 + (size_t)(b * H + h) * N * D;
   const int8_t* kh = k_i8 + (size_t)(b * H_kv + hk) * N * D;
   const int ntk = (N + kKvTile - 1) / kKvTile;
-  const uint8_t* vh = v_f8 + (size_t)(b * H_kv + hk) * ntk * KBYTES;
+  const uint8_t* vh = v_f8 + (size_t)(b * H_kv + hk) * ntk * VBYTES;
+  const uint8_t* vsh = PV4 ? v_e8 + (size_t)(b * H_kv + hk) * ntk * VSBYTES : nullptr;
   const int nkb = (N + kBlkK - 1) / kBlkK;
   const float* ksc = k_scale + (size_t)(b * H_kv + hk) * nkb;
   const int ntiles = CAUSAL ? qt + 1 : ntk;
@@ -102,7 +110,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[c][r] = 0.f;
   float m_run = -INFINITY;   // running max of the log2-domain scores
-  float l_part = 0.f;        // this lane's share of sum 448*P~
+  float l_part = 0.f;        // this lane's share of sum 448*P~ (MXFP4: of sum P~)
 
   // this lane's byte offset inside a 32-key K fragment block (full tiles)
   const uint32_t koff = (uint32_t)((lane % 32) * D + 16 * (lane / 32));
@@ -115,9 +123,17 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
       __builtin_amdgcn_global_load_lds(dsr + key, (lds_void*)(dst + wave * 256), 4, 0, 0);
     }
   };
+  // V codes (and, for MXFP4, the tile's 512 scale bytes: waves 0 and 1, one
+  // dword per lane) of tile t into a stage
+  auto load_v = [&](int t, char* stage) __attribute__((always_inline)) {
+    load_v_tile<VBYTES>(vh + (size_t)t * VBYTES, stage + KBYTES, wave, lane);
+    if (PV4 && wave < 2)
+      __builtin_amdgcn_global_load_lds(vsh + (size_t)t * VSBYTES + wave * 256 + lane * 4,
+                                       (lds_void*)(stage + KBYTES + VBYTES + wave * 256), 4, 0, 0);
+  };
   load_k_tile<D>(kh, 0, N, lds[0], wave, lane);
-  load_v_tile<D>(vh, lds[0] + KBYTES, wave, lane);
-  load_ds_tile(0, lds[0] + 2 * KBYTES);
+  load_v(0, lds[0]);
+  load_ds_tile(0, lds[0] + DSOFF);
 
   // One 128-key step of the online softmax.  MASK: the tile holds keys past
   // the diagonal (causal) or past N; only the last tile can.
@@ -144,8 +160,8 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
     if (t + 1 < ntiles) {
       if ((t + 2) * kKvTile <= N) load_k_tile_full<D>(kh, (t + 1) * kKvTile, koff, lds[(t + 1) & 1], wave);
       else load_k_tile<D>(kh, (t + 1) * kKvTile, N, lds[(t + 1) & 1], wave, lane);
-      load_v_tile<D>(vh + (size_t)(t + 1) * KBYTES, lds[(t + 1) & 1] + KBYTES, wave, lane);
-      load_ds_tile(t + 1, lds[(t + 1) & 1] + 2 * KBYTES);
+      load_v(t + 1, lds[(t + 1) & 1]);
+      load_ds_tile(t + 1, lds[(t + 1) & 1] + DSOFF);
     }
     const char* kt = lds[t & 1];
     const char* vt = lds[t & 1] + KBYTES;
@@ -180,11 +196,12 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
     }
 
     float xm = -INFINITY;
+    float xk[4];   // MXFP4: each 32-key block's max over the whole row block
     if constexpr (SQ) {
       // ---- with Delta S: s becomes the float score t = (f - kMagic) * ck +
       // Delta S[key] in log2 units (masked: -inf), and the row max is taken
       // on those floats.
-      const float* dt = reinterpret_cast<const float*>(lds[t & 1] + 2 * KBYTES);
+      const float* dt = reinterpret_cast<const float*>(lds[t & 1] + DSOFF);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -230,10 +247,21 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         const int m4 = max(max(v[12], v[13]), v[14]);
         const int fm = max(max(max(m0, m1), m2), max(max(m3, m4), v[15]));
         const float x = (as_float(fm) - kMagic) * ck[kb];
-        xm = MASK ? (fm != INT_MIN ? fmaxf(xm, x) : xm) : fmaxf(xm, x);
+        if constexpr (PV4) {
+          xk[kb] = MASK ? (fm != INT_MIN ? x : -INFINITY) : x;
+        } else {
+          xm = MASK ? (fm != INT_MIN ? fmaxf(xm, x) : xm) : fmaxf(xm, x);
+        }
       }
     }
-    xm = max_xor32(xm);
+    if constexpr (PV4) {
+      // a block's 32 keys sit in both lane halves
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) xk[kb] = max_xor32(xk[kb]);
+      xm = fmaxf(fmaxf(xk[0], xk[1]), fmaxf(xk[2], xk[3]));
+    } else {
+      xm = max_xor32(xm);
+    }
     const float m_new = fmaxf(m_run, xm);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -334,6 +362,68 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         }
       }
     };
+    if constexpr (PV4) {
+      // ---- MXFP4: block kb's shared exponent e = floor(log2 max P~) - 2 =
+      // floor(xk - m) - 2 (>= -127); exp2(s - m - e) = P~ / 2^e lands in
+      // [0, 8) and is cast to E2M1 (nearest, ties even, saturated to 6); l
+      // sums P~ itself.
+      int ex[4];
+      uint32_t pk4[4][2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        ex[kb] = (int)fmaxf(floorf(xk[kb] - m_new), -125.0f) - 2;
+        const float mqk = m_new + (float)ex[kb];
+        const float off = fmaf(kMagic, ck[kb], mqk);
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float a = decltype(fast_tag)::value
+                              ? fmaf(as_float(s[kb][r]), ck[kb], -off)
+                              : fmaf(as_float(s[kb][r]) - kMagic, ck[kb], -mqk);
+          e[r] = __builtin_amdgcn_exp2f(a);
+          if constexpr (MASK) e[r] = (s[kb][r] == INT_MIN) ? 0.f : e[r];
+        }
+        float u[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = e[2 * j] + e[2 * j + 1];
+#pragma unroll
+        for (int w = 4; w >= 1; w /= 2)
+#pragma unroll
+          for (int j = 0; j < w; ++j) u[j] = u[2 * j] + u[2 * j + 1];
+        l_part += ldexpf(u[0], ex[kb]);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          uint32_t pk = 0u;
+          static_for<4>([&](auto ji) {
+            constexpr int j = decltype(ji)::value;
+            pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, e[8 * w + 2 * j],
+                                                          e[8 * w + 2 * j + 1], 1.0f, j);
+          });
+          pk4[kb][w] = pk;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- O^T += V^T P^T on the FP4 matrix cores, 64 keys per MFMA: after
+      // exchanging lane halves, half g holds all 32 keys of block 2h + g
+      // (nibble p = key mx_slot_key(p)), as V's chunks do.
+      const char* vsc = vt + VBYTES;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const auto r0 = __builtin_amdgcn_permlane32_swap(pk4[2 * hh][0], pk4[2 * hh + 1][0], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(pk4[2 * hh][1], pk4[2 * hh + 1][1], false, false);
+        const i32x8 bop = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1], 0, 0, 0, 0};
+        const int sb = (half ? ex[2 * hh + 1] : ex[2 * hh]) + 127;
+        const int sa = *reinterpret_cast<const int*>(vsc + (hh * 64 + lane) * 4);
+        static_for<NKC>([&](auto ci) {
+          constexpr int c = decltype(ci)::value;
+          const i32x4 a4 = *reinterpret_cast<const i32x4*>(vt + ((hh * NKC + c) * 64 + lane) * 16);
+          const i32x8 aop = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
+          // A and B are FP4 (format 4); A's scale is byte c of sa
+          acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc_o[c], 4, 4, c,
+                                                                       sa, 0, sb);
+        });
+      }
+    } else {
     exp_pv(fast_tag);
     if constexpr (D != 64) {
       __builtin_amdgcn_sched_barrier(0);
@@ -349,6 +439,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         vb = vn;
       }
     }
+    }
   };
 
   const bool last_masked = CAUSAL || (N % kKvTile) != 0;
@@ -361,7 +452,8 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   else if (fast_wg) run(std::true_type{});
   else run(std::false_type{});
 
-  // ---- O = O / l * dV (l already carries the factor 448).
+  // ---- O = O / l * dV (l already carries the factor 448; MXFP4: no 448,
+  // and V's scales were applied by the matrix cores).
 #pragma unroll
   for (int c = 0; c < NKC; ++c) pin(acc_o[c]);
   const float l_tot = l_part + __shfl_xor(l_part, 32);
@@ -372,7 +464,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   // correction for smoothed K (sm_scale * q . mean K) when given.
   if (lse != nullptr && half == 0 && qi < N) {
     const size_t row = (size_t)(b * H + h) * N + qi;
-    float v = 0.69314718055994531f * (m_run + log2f(l_tot) - kLog2_448);
+    float v = 0.69314718055994531f * (m_run + log2f(l_tot) - (PV4 ? 0.f : kLog2_448));
     if (lse_corr != nullptr) v += lse_corr[row];
     lse[row] = v;
   }
@@ -386,7 +478,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         const int ch = c * 32 + 8 * r4 + 4 * half;
         float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = acc_o[c][r4 * 4 + j] * inv * vs[ch + j];
+        for (int j = 0; j < 4; ++j) v[j] = acc_o[c][r4 * 4 + j] * inv * (PV4 ? 1.0f : vs[ch + j]);
         uint2 pk;
         if (BF16) {
           __hip_bfloat16 x0 = __float2bfloat16(v[0]), x1 = __float2bfloat16(v[1]);
@@ -450,9 +542,10 @@ __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
 
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                                const float* delta_s, void* o, int bf16_out, float* lse,
-                                const float* lse_corr, int B, int H, int H_kv, int N, int d,
-                                int q_group, int causal, float sm_scale, hipStream_t stream) {
+                                const uint8_t* v_e8, const float* delta_s, void* o, int bf16_out,
+                                float* lse, const float* lse_corr, int B, int H, int H_kv, int N,
+                                int d, int q_group, int causal, float sm_scale,
+                                hipStream_t stream) {
   using namespace sage;
   const int qg_shift = q_group == kBlkQ ? 7 : q_group == kWaveQ ? 5 : q_group == 1 ? 0 : -1;
   if (qg_shift < 0) return hipErrorInvalidValue;
@@ -461,25 +554,27 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const float sm_log2 = sm_scale * kLog2e;
   dim3 grid((unsigned)total), block(kWaves * 64);
-  const bool sq = delta_s != nullptr;
-#define SAGE_ATTN_CASE(DD, CC, BB, SS)                                                           \
-  if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB && sq == SS) {                     \
-    hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB, SS>), grid, block, 0, stream, q_i8, q_scale, \
-                       k_i8, k_scale, v_f8, v_scale, delta_s, o, lse, lse_corr, H, H_kv, N,      \
-                       sm_log2, qg_shift, nqt, (int)total);                                      \
-    return hipGetLastError();                                                                    \
+  const bool sq = delta_s != nullptr, pv4 = v_e8 != nullptr;
+  if (sq && pv4) return hipErrorInvalidValue;
+#define SAGE_ATTN_CASE(DD, CC, BB, SS, PP)                                                        \
+  if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB && sq == SS && pv4 == PP) {          \
+    hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB, SS, PP>), grid, block, 0, stream, q_i8,       \
+                       q_scale, k_i8, k_scale, v_f8, v_scale, v_e8, delta_s, o, lse, lse_corr, H, \
+                       H_kv, N, sm_log2, qg_shift, nqt, (int)total);                              \
+    return hipGetLastError();                                                                     \
   }
-#define SAGE_ATTN_CASES(SS)          \
-  SAGE_ATTN_CASE(64, false, false, SS)  \
-  SAGE_ATTN_CASE(64, false, true, SS)   \
-  SAGE_ATTN_CASE(64, true, false, SS)   \
-  SAGE_ATTN_CASE(64, true, true, SS)    \
-  SAGE_ATTN_CASE(128, false, false, SS) \
-  SAGE_ATTN_CASE(128, false, true, SS)  \
-  SAGE_ATTN_CASE(128, true, false, SS)  \
-  SAGE_ATTN_CASE(128, true, true, SS)
-  SAGE_ATTN_CASES(false)
-  SAGE_ATTN_CASES(true)
+#define SAGE_ATTN_CASES(SS, PP)              \
+  SAGE_ATTN_CASE(64, false, false, SS, PP)  \
+  SAGE_ATTN_CASE(64, false, true, SS, PP)   \
+  SAGE_ATTN_CASE(64, true, false, SS, PP)   \
+  SAGE_ATTN_CASE(64, true, true, SS, PP)    \
+  SAGE_ATTN_CASE(128, false, false, SS, PP) \
+  SAGE_ATTN_CASE(128, false, true, SS, PP)  \
+  SAGE_ATTN_CASE(128, true, false, SS, PP)  \
+  SAGE_ATTN_CASE(128, true, true, SS, PP)
+  SAGE_ATTN_CASES(false, false)
+  SAGE_ATTN_CASES(true, false)
+  SAGE_ATTN_CASES(false, true)
 #undef SAGE_ATTN_CASES
 #undef SAGE_ATTN_CASE
   return hipErrorInvalidValue;

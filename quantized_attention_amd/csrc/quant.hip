@@ -16,6 +16,9 @@
 //       the quantizers then subtract the mean of the token's own block.
 //   quant_v_fp8       : per-channel FP8 E4M3 quantization of V, written
 //       transposed and key-permuted in the fragment layout of sage.h.
+//   quant_v_mxfp4     : MXFP4 V (E2M1 codes, one E8M0 scale per 32
+//       consecutive keys of a channel: the OCP microscaling format the
+//       SageAttention3 synthesis page names), in the FP4 fragment layout.
 //
 // Every read of the fp16/bf16 inputs is a 16-byte vector load of 8 channels
 // of one token; consecutive threads read consecutive 16-byte chunks.
@@ -402,6 +405,63 @@ __global__ __launch_bounds__(kQuantThreads) void quant_v_fp8(const void* __restr
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 V.  One wave per (128-key tile, 32-channel block): lane L holds
+// channel cb*32 + L%32 and, for each 64-key half h of the tile, the 32 keys
+// of block 2h + L/32.  The block's shared exponent is e = floor(log2 amax) - 2
+// (clamped to E8M0's [-127, 127]; an all-zero block takes -127), its codes
+// are RNE(v * 2^-e) saturated to +-6 (the scaling by a power of two is exact).
+// The 16-byte chunk (tile, h, cb, L) holds nibble p = key mx_slot_key(p) of
+// the block; the scale byte e + 127 sits at (tile, h, L, cb) of the scale
+// array (4 bytes per (h, lane), one per channel block).  Keys >= N are 0.
+// grid (ceil(ntile * D/32 / 4), B*Hkv), 4 waves per workgroup.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kQuantThreads) void quant_v_mxfp4(const void* __restrict__ x,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales,
+                                                               int N, int ntile) {
+  constexpr int NCB = D / 32;
+  const int bh = blockIdx.y, lane = threadIdx.x % 64;
+  const int pair = blockIdx.x * (kQuantThreads / 64) + threadIdx.x / 64;
+  if (pair >= ntile * NCB) return;
+  const int tile = pair / NCB, cb = pair % NCB;
+  const int chan = cb * 32 + (lane % 32), g = lane / 32;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D + chan;
+  uint8_t* ct = codes + ((size_t)bh * ntile + tile) * (kKvTile / 2) * D;
+  uint8_t* st = scales + ((size_t)bh * ntile + tile) * kMxScaleBytes;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float y[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int p = 0; p < 32; ++p) {
+      const int n = tile * kKvTile + h * 64 + g * 32 + mx_slot_key(p);
+      float v = 0.f;
+      if (n < N) {
+        const uint16_t u = xs[(size_t)n * D];
+        v = BF16 ? as_float((int)((uint32_t)u << 16)) : (float)__builtin_bit_cast(_Float16, u);
+      }
+      y[p] = v;
+      amax = fmaxf(amax, fabsf(v));
+    }
+    int e = -127;
+    if (amax > 0.f) {
+      int ex;
+      frexpf(amax, &ex);                 // amax = f * 2^ex, f in [0.5, 1)
+      e = min(max(ex - 3, -127), 127);   // floor(log2 amax) - 2
+    }
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    static_for<16>([&](auto ji) {
+      constexpr int j = decltype(ji)::value;
+      w[j / 4] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[j / 4], ldexpf(y[2 * j], -e),
+                                                         ldexpf(y[2 * j + 1], -e), 1.0f, j % 4);
+    });
+    *reinterpret_cast<uint4*>(ct + (size_t)((h * NCB + cb) * 64 + lane) * 16) =
+        uint4{w[0], w[1], w[2], w[3]};
+    st[(h * 64 + lane) * 4 + cb] = (uint8_t)(e + 127);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // corr[bh][n] = sm_scale * sum_c q[bh][n][c] * mean[bh_kv][c]: the part of
 // every logit of row n that smoothing K removed (source-analysis page,
 // smooth_k and LSE correction).  D/8 threads per row, 16-byte loads, fixed
@@ -539,6 +599,26 @@ hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, 
   if (d == 128)
     return bf16 ? quant_v_impl<128, true>(v, B, H_kv, N, v_f8, v_scale, ws, st)
                 : quant_v_impl<128, false>(v, B, H_kv, N, v_f8, v_scale, ws, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t sage_launch_quant_v_mxfp4(const void* v, int bf16, int B, int H_kv, int N, int d,
+                                     uint8_t* v_f4, uint8_t* v_e8, hipStream_t st) {
+  using namespace sage;
+  const int nt = (N + kKvTile - 1) / kKvTile;
+  const int wpg = kQuantThreads / 64;
+#define SAGE_QV4(DD, BB)                                                                       \
+  if (d == DD && (bf16 != 0) == BB) {                                                          \
+    const int pairs = nt * (DD / 32);                                                          \
+    hipLaunchKernelGGL((quant_v_mxfp4<DD, BB>), dim3((pairs + wpg - 1) / wpg, B * H_kv),       \
+                       dim3(kQuantThreads), 0, st, v, v_f4, v_e8, N, nt);                      \
+    return hipGetLastError();                                                                  \
+  }
+  SAGE_QV4(64, false)
+  SAGE_QV4(64, true)
+  SAGE_QV4(128, false)
+  SAGE_QV4(128, true)
+#undef SAGE_QV4
   return hipErrorInvalidValue;
 }
 

@@ -19,9 +19,12 @@ hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, 
                                uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st);
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                                const float* delta_s, void* o, int bf16_out, float* lse,
-                                const float* lse_corr, int B, int H, int H_kv, int N, int d,
-                                int q_group, int causal, float sm_scale, hipStream_t stream);
+                                const uint8_t* v_e8, const float* delta_s, void* o, int bf16_out,
+                                float* lse, const float* lse_corr, int B, int H, int H_kv, int N,
+                                int d, int q_group, int causal, float sm_scale,
+                                hipStream_t stream);
+hipError_t sage_launch_quant_v_mxfp4(const void* v, int bf16, int B, int H_kv, int N, int d,
+                                     uint8_t* v_f4, uint8_t* v_e8, hipStream_t st);
 hipError_t sage_launch_lse_correction(const void* q, int bf16, const float* k_mean, int B, int H,
                                       int H_kv, int N, int d, float sm_scale, float* corr,
                                       hipStream_t st);
@@ -102,6 +105,8 @@ sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, int q_group,
   const size_t nmb = (n + SAGE_BLKQ - 1) / SAGE_BLKQ;
   out->q_mean = b * h * nmb * dd * sizeof(float);
   out->delta_s = (size_t)delta_s_elems(B, H, N) * sizeof(float);
+  out->v_f4 = b * hk * npad * dd / 2;
+  out->v_e8 = b * hk * (npad / SAGE_KV_TILE) * 512;
   return SAGE_OK;
 }
 
@@ -170,8 +175,9 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
     return SAGE_ERR_ALIGN;
   if (delta_s && !aligned16(delta_s)) return SAGE_ERR_ALIGN;
-  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, delta_s, o,
-                                       out_dtype == SAGE_BF16, nullptr, nullptr, B, H, H_kv, N,
+  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr,
+                                       delta_s, o, out_dtype == SAGE_BF16, nullptr, nullptr, B, H,
+                                       H_kv, N,
                                        d, q_group, causal, sm_scale, (hipStream_t)stream));
 }
 
@@ -192,8 +198,40 @@ sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const in
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
     return SAGE_ERR_ALIGN;
   if (delta_s && !aligned16(delta_s)) return SAGE_ERR_ALIGN;
-  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, delta_s, o,
-                                       out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d,
+  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr,
+                                       delta_s, o, out_dtype == SAGE_BF16, lse, lse_corr, B, H,
+                                       H_kv, N, d,
+                                       q_group, causal, sm_scale, (hipStream_t)stream));
+}
+
+sage_status sage_quant_v_mxfp4(const void* v, sage_dtype dtype, int B, int H_kv, int N, int d,
+                               uint8_t* v_f4, uint8_t* v_e8, void* stream) {
+  if (!v || !v_f4 || !v_e8) return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H_kv, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!aligned16(v) || !aligned16(v_f4) || !aligned16(v_e8)) return SAGE_ERR_ALIGN;
+  return from_hip(sage_launch_quant_v_mxfp4(v, dtype == SAGE_BF16, B, H_kv, N, d, v_f4, v_e8,
+                                            (hipStream_t)stream));
+}
+
+sage_status sage_attn_fwd_mxfp4(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                const float* k_scale, const uint8_t* v_f4, const uint8_t* v_e8,
+                                void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
+                                int B, int H, int H_kv, int N, int d, int q_group, int causal,
+                                float sm_scale, void* stream) {
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f4 || !v_e8 || !o) return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!valid_q_group(q_group)) return SAGE_ERR_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_ARG;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
+  if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f4) || !aligned16(v_e8) ||
+      !aligned16(o))
+    return SAGE_ERR_ALIGN;
+  return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f4, nullptr, v_e8, nullptr,
+                                       o, out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d,
                                        q_group, causal, sm_scale, (hipStream_t)stream));
 }
 

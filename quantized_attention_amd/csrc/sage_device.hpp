@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sage {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -22,6 +24,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kBlkQ = 128;     // Q tokens per INT8 scale (the default Q granularity)
 constexpr int kBlkK = 64;      // K tokens per INT8 scale
 constexpr int kKvTile = 128;   // keys per online-softmax step / V tile
+constexpr int kMxScaleBytes = 512;   // MXFP4 V scale bytes per tile: 2 halves x 64 lanes x 4
 constexpr int kWaveQ = 32;     // queries per wave (one 32-wide MFMA column block)
 constexpr int kWaves = 4;      // waves per workgroup
 constexpr int kBlockQ = kWaveQ * kWaves;   // queries per workgroup (== kBlkQ)
@@ -71,6 +74,24 @@ __device__ __forceinline__ float max_xor32(float x) {
   asm volatile("" : "+v"(b));
   const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
   return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, each I a constant
+// expression (for builtin arguments that must be immediates).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Key (0..31 inside a 32-key block) of nibble p (0..31) of a lane's 16-byte
+// FP4 operand (32 keys of one block): nibbles 0..15 are the block's keys that
+// lane half 0 holds in the C/D layout (8*(r/4) + r%4), nibbles 16..31 those of
+// half 1 (8*(r/4) + 4 + r%4) -- the order of P after the lane-half exchange.
+__host__ __device__ constexpr int mx_slot_key(int p) {
+  return 8 * ((p % 16) / 4) + 4 * (p / 16) + (p % 4);
 }
 
 // Map a linear workgroup id to a logical work id so that each XCD (ids are
@@ -152,11 +173,12 @@ __device__ __forceinline__ void load_k_tile_full(const int8_t* kh, int key0, uin
   }
 }
 
-// V tile (already fragment-ordered in HBM, kKvTile*D bytes) -> LDS, a
-// straight copy with direct global->LDS loads.
-template <int D>
+// V tile (already fragment-ordered in HBM, BYTES bytes: kKvTile*D FP8 or
+// half that of FP4 codes) -> LDS, a straight copy with direct global->LDS
+// loads.
+template <int BYTES>
 __device__ __forceinline__ void load_v_tile(const uint8_t* vtile, char* lds_v, int wave, int lane) {
-  constexpr int NB = kKvTile * D / 1024;
+  constexpr int NB = BYTES / 1024;
   static_assert(NB % kWaves == 0, "whole blocks per wave");
   const uint32_t voff = (uint32_t)lane * 16;
 #pragma unroll

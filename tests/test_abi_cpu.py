@@ -26,11 +26,11 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse",
             "sage_lse_correction", "sage_buffer_sizes", "sage_qk_int32", "sage_status_str",
-            "sage_delta_s",
+            "sage_delta_s", "sage_quant_v_mxfp4", "sage_attn_fwd_mxfp4",
             "sage_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sage_abi_version() == 4
+    assert lib.sage_abi_version() == 5
 
 
 def test_status_strings():
@@ -56,6 +56,8 @@ def test_buffer_sizes(B, H, H_kv, N, d, q_group):
     assert s["ws_quant_v"] == 4 * B * H_kv * math.ceil(N / 256) * d
     assert s["q_mean"] == 4 * B * H * math.ceil(N / 128) * d
     assert s["delta_s"] == 4 * B * H * math.ceil(N / 128) * N
+    assert s["v_f4"] == B * H_kv * math.ceil(N / 128) * 64 * d
+    assert s["v_e8"] == B * H_kv * math.ceil(N / 128) * 512
 
 
 @pytest.mark.parametrize("args,code", [
@@ -113,6 +115,37 @@ def _ds(lib, **kw):
              sm_scale=0.125, out=FAKE, stream=None)
     a.update(kw)
     return lib.sage_delta_s(*a.values())
+
+
+def _qv4(lib, **kw):
+    a = dict(v=FAKE, dt=0, B=1, H_kv=2, N=256, d=64, v_f4=FAKE, v_e8=FAKE, stream=None)
+    a.update(kw)
+    return lib.sage_quant_v_mxfp4(*a.values())
+
+
+def _attn4(lib, **kw):
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f4=FAKE, v_e8=FAKE, o=FAKE,
+             dt=0, lse=None, corr=None, B=1, H=2, H_kv=2, N=256, d=64, qg=128, causal=0,
+             sm_scale=0.125, stream=None)
+    a.update(kw)
+    return lib.sage_attn_fwd_mxfp4(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), 1), (dict(v_e8=None), 1), (dict(N=0), 2), (dict(d=32), 3), (dict(dt=5), 5),
+    (dict(v_f4=FAKE + 4), 9), (dict(v_e8=FAKE + 1), 9),
+])
+def test_quant_v_mxfp4_rejects(kw, code):
+    assert _qv4(qa.load_library(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v_f4=None), 1), (dict(o=None), 1), (dict(B=0), 2), (dict(d=96), 3),
+    (dict(H=4, H_kv=3), 4), (dict(dt=3), 5), (dict(qg=8), 6), (dict(causal=2), 6),
+    (dict(sm_scale=-1.0), 6), (dict(v_e8=FAKE + 2), 9),
+])
+def test_attn_fwd_mxfp4_rejects(kw, code):
+    assert _attn4(qa.load_library(), **kw) == code
 
 
 def _qk32(lib, **kw):

@@ -13,7 +13,7 @@ import torch
 import workloads as W
 from oracle import fp8_e4m3 as F8
 from oracle import sage_oracle as O
-from tests.sage_testlib import compare_output, to_np, v_natural
+from tests.sage_testlib import compare_output, compare_output_mx, to_np, v4_natural, v_natural
 
 pytestmark = pytest.mark.gpu
 
@@ -349,6 +349,93 @@ def test_smooth_q_tracks_exact_attention(gpu_lib):
         rl1[sq] = m["rel_l1"]
         assert m["cos"] >= 0.998, (sq, m)
     assert rl1[True] < rl1[False], rl1
+
+
+# ------------------------------------------------------------------ MXFP4 P V
+
+def _check_quant_v4(qa, v):
+    vq4 = qa.sage_quant_v_mxfp4(v.to(DEV))
+    torch.cuda.synchronize()
+    ref4 = O.quantize_v_mxfp4(v)
+    N, d = v.shape[2], v.shape[3]
+    codes, e = v4_natural(to_np(vq4["v_f4"]), to_np(vq4["v_e8"]), N, d)
+    np_ = ref4["v_f4"].shape[2]
+    assert np.array_equal(codes[:, :, :np_], ref4["v_f4"]), "MXFP4 V codes differ"
+    assert (codes[:, :, np_:] == 0).all(), "MXFP4 V padding must be zero codes"
+    nb = ref4["v_e8"].shape[2]
+    assert np.array_equal(e[:, :, :nb], ref4["v_e8"]), "MXFP4 V exponents differ"
+    return vq4, ref4
+
+
+MX_CASES = [SMALL[i] for i in (0, 1, 3, 5, 9, 10)]
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", MX_CASES)
+def test_mxfp4_parity(gpu_lib, B, H, H_kv, N, d, dtype, causal):
+    """MXFP4 P V: V codes and E8M0 exponents bit-exact; the output against the oracle's
+    MXFP4 recursion (the bulk to 2e-2, rare P rounding flips bounded)."""
+    print(f"mxfp4 case B{B} H{H}/{H_kv} N{N} d{d} {dtype} causal={causal}", flush=True)
+    q, k, v = _rand_inputs(B, H, H_kv, N, d, dtype, seed=N * 13 + d)
+    qk = gpu_lib.sage_quant_qk(q.to(DEV), k.to(DEV))
+    ref = O.quantize_qk(q, k)
+    vq4, ref4 = _check_quant_v4(gpu_lib, v)
+    sm = 1 / math.sqrt(d)
+    o = gpu_lib.sage_attn_fwd_mxfp4(qk, vq4, causal=causal, sm_scale=sm, out_dtype=dtype)
+    torch.cuda.synchronize()
+    o_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"], ref4["v_f4"],
+                         ref4["v_e8"], causal=causal, sm_scale=sm, pv="mxfp4")
+    print(compare_output_mx(o, o_ref), flush=True)
+
+
+def test_mxfp4_lse_and_exact(gpu_lib):
+    """The MXFP4 LSE (no factor 448 in l) against the oracle's, and the output close to
+    exact attention (the pages quote CosSim 98.37 % for MXFP4)."""
+    q, k, v = _rand_inputs(1, 4, 2, 700, 128, torch.bfloat16, seed=71)
+    sm = 1 / math.sqrt(128)
+    o, lse = gpu_lib.sageattn(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=True, sm_scale=sm,
+                              return_lse=True, pv="mxfp4")
+    torch.cuda.synchronize()
+    ref = O.quantize_qk(q, k)
+    ref4 = O.quantize_v_mxfp4(v)
+    _, l_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
+                            ref4["v_f4"], ref4["v_e8"], causal=True, sm_scale=sm, pv="mxfp4",
+                            return_lse=True)
+    c_ref = O.lse_correction(q, ref["k_mean"], sm_scale=sm)
+    c_abs = O.lse_correction(q.float().abs(), np.abs(ref["k_mean"]), sm_scale=sm)
+    err = np.abs(to_np(lse).astype(np.float64) - (l_ref + c_ref))
+    assert np.all(err <= _lse_tol(700, c_abs)), err.max()
+    ex = O.attn_exact(q, k, v, causal=True, sm_scale=sm)
+    m = O.metrics(to_np(o.float()).astype(np.float64), ex)
+    assert m["cos"] >= 0.975, m
+
+
+@pytest.mark.parametrize("name,heads,nrows", [
+    ("llm_prefill", [(0, 9)], 96),
+    ("video_dit", [(0, 20)], 64),
+])
+def test_workload_parity_mxfp4(gpu_lib, name, heads, nrows):
+    w = W.get(name)
+    print(f"workload {name} mxfp4: generating", flush=True)
+    t = W.generate(w)
+    plan = gpu_lib.SagePlan(w.B, w.H, w.H_kv, w.N, w.d, w.torch_dtype, w.causal, pv="mxfp4")
+    o = plan(t["q"].to(DEV), t["k"].to(DEV), t["v"].to(DEV))
+    torch.cuda.synchronize()
+    grp = w.H // w.H_kv
+    for b, h in heads:
+        hk = h // grp
+        ref = O.quantize_qk(t["q"][b:b + 1, h:h + 1], t["k"][b:b + 1, hk:hk + 1])
+        ref4 = O.quantize_v_mxfp4(t["v"][b:b + 1, hk:hk + 1])
+        codes, e = v4_natural(to_np(plan.vq["v_f4"][b:b + 1, hk:hk + 1]),
+                              to_np(plan.vq["v_e8"][b:b + 1, hk:hk + 1]), w.N, w.d)
+        assert np.array_equal(codes[:, :, :ref4["v_f4"].shape[2]], ref4["v_f4"])
+        assert np.array_equal(e[:, :, :ref4["v_e8"].shape[2]], ref4["v_e8"])
+        g = np.random.default_rng(b * 100 + h)
+        rows = np.unique(np.concatenate([g.choice(w.N, size=nrows, replace=False), [0, w.N - 1]]))
+        o_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
+                             ref4["v_f4"], ref4["v_e8"], causal=w.causal, sm_scale=w.sm_scale,
+                             rows=rows, pv="mxfp4")
+        m = compare_output_mx(o[b, h, torch.from_numpy(rows).to(DEV)], o_ref[0, 0])
+        print(f"workload {name} mxfp4 head {(b, h)}: {m}", flush=True)
 
 
 # ------------------------------------------------------------------ the workloads
