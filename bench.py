@@ -8,7 +8,9 @@ Default workload: the sequence-sweep configuration at N = 32768
 
 Prints ONE JSON line.  ``value`` is whole-step TOPS, 4*B*H*N^2*d / t_step
 (halved when causal); ``attn_tops`` is the attention kernel alone (the pages'
-convention: quantization time excluded).  ``roofline`` is the attention
+convention: quantization time excluded), from the mean of the per-step
+launch times; ``attn_tops_median`` takes their median (20 steps by default).
+``roofline`` is the attention
 kernel's algorithmic TOPS against the dense INT8/FP8 MFMA peak, with the
 kernel time measured by HIP events on the launch stream.  ``cpu_baseline``
 times the float64 CPU oracle on a bounded sample of the same workload.
@@ -20,6 +22,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -95,7 +98,7 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="sweep@N32768",
                     help="workload name: tiny, llm_prefill, video_dit, sweep@N<n>, gqa_long")
@@ -150,7 +153,7 @@ def main():
                                                         (1024, 2048, 4096, 8192, 16384, 32768)]
         names.append("gqa_long")
         for name in names:
-            r = run_config(W.get(name), max(args.steps, 5), args.warmup, q_group=args.q_group,
+            r = run_config(W.get(name), max(args.steps, 20), args.warmup, q_group=args.q_group,
                            smooth_q=args.smooth_q, pv=args.pv)
             print(json.dumps(r), flush=True)
         return
@@ -248,6 +251,7 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
     t_ds = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     t_v = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
     t_attn = sum(e[3].elapsed_time(e[4]) for e in ev) / steps
+    t_attn_med = statistics.median(e[3].elapsed_time(e[4]) for e in ev)
     ms_step = wall * 1e3 / steps
     ops = w.ops()
     attn_tops = ops / (t_attn * 1e-3) / 1e12
@@ -275,6 +279,8 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
                    "in_dtype": w.dtype, "q_group": q_group, "smooth_q": smooth_q, "pv": pv},
         "attn_tops": round(attn_tops, 2),
         "attn_ms": round(t_attn, 4),
+        "attn_ms_median": round(t_attn_med, 4),
+        "attn_tops_median": round(ops / (t_attn_med * 1e-3) / 1e12, 2),
         "quant_qk_ms": round(t_qk, 4),
         "quant_v_ms": round(t_v, 4),
         "quant_gbs": round(quant_bytes / ((t_qk + t_v) * 1e-3) / 1e9, 1),
@@ -290,7 +296,8 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
         },
     }
     if not full:
-        keep = ("value", "ms_per_step", "config", "attn_tops", "attn_ms", "quant_qk_ms", "quant_v_ms",
+        keep = ("value", "ms_per_step", "config", "attn_tops", "attn_ms", "attn_ms_median",
+                "attn_tops_median", "quant_qk_ms", "quant_v_ms",
                 "quant_gbs", "delta_s_ms")
         res = {k: res[k] for k in keep}
         res["attn_frac_of_peak"] = round(res["attn_tops"] / PEAK_TOPS, 4)
