@@ -2,18 +2,18 @@
  * sage.h -- C ABI of the MI355X (gfx950) quantized attention forward pass.
  *
  * The method (SageAttention2 detail page, Algorithm 1, with INT8 Q/K as the
- * source-analysis page's "Q/K 统一走 INT8" and without smoothing Q):
+ * source-analysis page's "Q/K 统一走 INT8"; smoothing Q is optional):
  *   1. Smooth K: subtract the per-channel mean of K over tokens
  *      (SageAttention synthesis page, Smooth K; Algorithm 1 preprocessing).
  *   2. Optionally smooth Q by the per-channel mean of each 128-token block
  *      (Algorithm 1's q_bar_i); the Delta S table q_bar_i . K_j, computed
  *      once by sage_delta_s, adds the removed part back to the scores.
- *      Quantize Q (or Q - q_bar) per group of 128, 32 or 1 tokens and smoothed K per block
- *      of 64 tokens to INT8 with one FP32 scale per group: scale = amax /
- *      127, code = round-half-even(x / scale) (deployment-guide page,
- *      quantization formula; block sizes b_q = 128, b_kv = 64 from the
- *      detail page's "Optimization Techniques" table; the finer Q groups are
- *      the per-warp / per-thread granularities, below).
+ *      Quantize Q (or Q - q_bar) per group of 128, 32 or 1 tokens and
+ *      smoothed K per block of 64 tokens to INT8 with one FP32 scale per
+ *      group: scale = amax / 127, code = round-half-even(x / scale)
+ *      (deployment-guide page, quantization formula; block sizes b_q = 128,
+ *      b_kv = 64 from the detail page's "Optimization Techniques" table; the
+ *      finer Q groups are the per-warp / per-thread granularities, below).
  *   3. Quantize V per channel to FP8 E4M3 with one FP32 scale per channel:
  *      scale = amax / 448 (Algorithm 1's psi_V; source-analysis page: V is
  *      transposed, padded and permuted before the per-channel FP8 cast).
