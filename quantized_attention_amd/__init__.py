@@ -139,6 +139,25 @@ def _need_gpu(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_sizes(where: str, sizes: dict, **bufs):
+    """Each given buffer must hold at least the bytes sage_buffer_sizes names for
+    the shapes (a shorter one would be read or written past its end)."""
+    for name, t in bufs.items():
+        if t is not None and _nbytes(t) < sizes[name]:
+            raise ValueError(f"{where}: {name} holds {_nbytes(t)} bytes; the shapes need "
+                             f"{sizes[name]}")
+
+
+def _check_tensor(where: str, name: str, t, shape, dtype):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{where}: {name} must be {dtype} {list(shape)}, got {t.dtype} "
+                         f"{list(t.shape)}")
+
+
 def sage_buffer_sizes(B: int, H: int, H_kv: int, N: int, d: int, q_group: int = BLKQ) -> dict:
     s = _Sizes()
     _check(load_library().sage_buffer_sizes(B, H, H_kv, N, d, q_group, ctypes.byref(s)),
@@ -184,7 +203,6 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *,
                   stream=None) -> dict:
     """Smooth K (and, with smooth_q, Q by its 128-block means) and quantize Q
     (q_group tokens per scale) and K to INT8 (see sage.h for exact semantics)."""
-    _need_gpu(q, k)
     if q.dtype != k.dtype:
         raise TypeError("q and k must share a dtype")
     B, H, N, d = q.shape
@@ -198,9 +216,13 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *,
         raise ValueError("out['q_scale'] does not hold ceil(N / q_group) scales per head")
     if smooth_q and "q_mean" not in out:
         raise ValueError("smooth_q needs out['q_mean']")
+    sizes = sage_buffer_sizes(B, H, H_kv, N, d, q_group)
+    _check_sizes("sage_quant_qk", sizes, q_i8=out["q_i8"], q_scale=out["q_scale"],
+                 k_i8=out["k_i8"], k_scale=out["k_scale"], k_mean=out["k_mean"],
+                 q_mean=out.get("q_mean") if smooth_q else None)
+    _need_gpu(q, k, *(t for n, t in out.items() if n != "q_mean" or smooth_q))
     if workspace is None and smooth_k:
-        ws = sage_buffer_sizes(B, H, H_kv, N, d)["ws_quant_qk"]
-        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(sizes["ws_quant_qk"], dtype=torch.uint8, device=q.device)
     st = load_library().sage_quant_qk(
         q.data_ptr(), k.data_ptr(), _dt(q.dtype), B, H, H_kv, N, d, q_group, int(bool(smooth_k)),
         int(bool(smooth_q)), out["q_i8"].data_ptr(), out["q_scale"].data_ptr(),
@@ -223,9 +245,11 @@ def _alloc_v4(B, H_kv, N, d, device):
 def sage_quant_v_mxfp4(v: torch.Tensor, *, out=None, stream=None) -> dict:
     """MXFP4 quantization of V (E2M1 codes, E8M0 scale per 32 keys of a channel) into
     the FP4 fragment layout of sage.h."""
-    _need_gpu(v)
     B, H_kv, N, d = v.shape
     out = out or _alloc_v4(B, H_kv, N, d, v.device)
+    _check_sizes("sage_quant_v_mxfp4", sage_buffer_sizes(B, H_kv, H_kv, N, d), v_f4=out["v_f4"],
+                 v_e8=out["v_e8"])
+    _need_gpu(v, out["v_f4"], out["v_e8"])
     st = load_library().sage_quant_v_mxfp4(v.data_ptr(), _dt(v.dtype), B, H_kv, N, d,
                                            out["v_f4"].data_ptr(), out["v_e8"].data_ptr(),
                                            _stream(stream, v.device))
@@ -238,14 +262,17 @@ def sage_attn_fwd_mxfp4(qk: dict, vq4: dict, *, causal: bool, sm_scale: float,
                         out=None, lse=None, stream=None):
     """Attention with MXFP4 P V; returns O, or (O, lse) with return_lse."""
     q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
-    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq4["v_f4"], vq4["v_e8"])
     B, H, N, d = q_i8.shape
     H_kv = k_i8.shape[1]
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q_i8.device)
-    _need_gpu(out)
+    _check_attn_inputs("sage_attn_fwd_mxfp4", qk, out, v_f4=vq4["v_f4"], v_e8=vq4["v_e8"])
+    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq4["v_f4"], vq4["v_e8"], out)
+    if return_lse:
+        _need_gpu(lse)
+        _check_tensor("sage_attn_fwd_mxfp4", "lse", lse, (B, H, N), torch.float32)
     if lse_corr is not None:
         _need_gpu(lse_corr)
         if lse_corr.shape != (B, H, N) or lse_corr.dtype != torch.float32:
@@ -267,8 +294,13 @@ def sage_delta_s(k: torch.Tensor, qk: dict, sm_scale: float, *, out=None,
     _need_gpu(k, qk["k_mean"], qk["q_mean"])
     B, H, nmb, d = qk["q_mean"].shape
     H_kv, N = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, H_kv, N, d) or nmb != -(-N // BLKQ):
+        raise ValueError(f"sage_delta_s: k {list(k.shape)} does not match q_mean "
+                         f"{list(qk['q_mean'].shape)}")
     if out is None:
         out = torch.empty((B, H, nmb, N), dtype=torch.float32, device=k.device)
+    _check_tensor("sage_delta_s", "k_mean", qk["k_mean"], (B, H_kv, d), torch.float32)
+    _check_tensor("sage_delta_s", "out", out, (B, H, nmb, N), torch.float32)
     _need_gpu(out)
     st = load_library().sage_delta_s(k.data_ptr(), _dt(k.dtype), qk["k_mean"].data_ptr(),
                                      qk["q_mean"].data_ptr(), B, H, H_kv, N, d, float(sm_scale),
@@ -279,12 +311,13 @@ def sage_delta_s(k: torch.Tensor, qk: dict, sm_scale: float, *, out=None,
 
 def sage_quant_v(v: torch.Tensor, *, out=None, workspace=None, stream=None) -> dict:
     """Per-channel FP8 E4M3 quantization of V into the fragment layout of sage.h."""
-    _need_gpu(v)
     B, H_kv, N, d = v.shape
     out = out or _alloc_v(B, H_kv, N, d, v.device)
+    sizes = sage_buffer_sizes(B, H_kv, H_kv, N, d)
+    _check_sizes("sage_quant_v", sizes, v_f8=out["v_f8"], v_scale=out["v_scale"])
+    _need_gpu(v, out["v_f8"], out["v_scale"])
     if workspace is None:
-        ws = sage_buffer_sizes(B, H_kv, H_kv, N, d)["ws_quant_v"]
-        workspace = torch.empty(ws, dtype=torch.uint8, device=v.device)
+        workspace = torch.empty(sizes["ws_quant_v"], dtype=torch.uint8, device=v.device)
     st = load_library().sage_quant_v(
         v.data_ptr(), _dt(v.dtype), B, H_kv, N, d, out["v_f8"].data_ptr(),
         out["v_scale"].data_ptr(), workspace.data_ptr(),
@@ -298,12 +331,12 @@ def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
     """Attention on quantized inputs; returns O [B, H, N, d] in out_dtype.
     delta_s: the sage_delta_s table when Q was smoothed."""
     q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
-    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"])
     B, H, N, d = q_i8.shape
     H_kv = k_i8.shape[1]
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
-    _need_gpu(out)
+    _check_attn_inputs("sage_attn_fwd", qk, out, v_f8=vq["v_f8"], v_scale=vq["v_scale"])
+    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"], out)
     _check_delta_s(delta_s, qk)
     st = load_library().sage_attn_fwd(
         q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
@@ -313,6 +346,21 @@ def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
         _stream(stream, q_i8.device))
     _check(st, "sage_attn_fwd")
     return out
+
+
+def _check_attn_inputs(where: str, qk: dict, out, **vbufs):
+    """Shapes of the quantized inputs and the output against q_i8's [B, H, N, d]."""
+    B, H, N, d = qk["q_i8"].shape
+    k_i8 = qk["k_i8"]
+    if k_i8.dim() != 4 or (k_i8.shape[0], k_i8.shape[2], k_i8.shape[3]) != (B, N, d):
+        raise ValueError(f"{where}: k_i8 {list(k_i8.shape)} does not match q_i8 "
+                         f"{list(qk['q_i8'].shape)}")
+    H_kv = k_i8.shape[1]
+    sizes = sage_buffer_sizes(B, H, H_kv, N, d, _q_group_of(qk["q_scale"], N))
+    _check_sizes(where, sizes, q_scale=qk["q_scale"], k_scale=qk["k_scale"], **vbufs)
+    if tuple(out.shape) != (B, H, N, d):
+        raise ValueError(f"{where}: out must be [B, H, N, d] = {[B, H, N, d]}, got "
+                         f"{list(out.shape)}")
 
 
 def _check_delta_s(delta_s, qk):
@@ -331,14 +379,15 @@ def sage_attn_fwd_lse(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
     lse [B, H, N] fp32 is ln sum_j exp(S_ij) of the scores the softmax used,
     plus lse_corr (the output of sage_lse_correction) when given."""
     q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
-    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"])
     B, H, N, d = q_i8.shape
     H_kv = k_i8.shape[1]
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q_i8.device)
-    _need_gpu(out, lse)
+    _check_attn_inputs("sage_attn_fwd_lse", qk, out, v_f8=vq["v_f8"], v_scale=vq["v_scale"])
+    _check_tensor("sage_attn_fwd_lse", "lse", lse, (B, H, N), torch.float32)
+    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"], out, lse)
     if lse_corr is not None:
         _need_gpu(lse_corr)
         if lse_corr.shape != (B, H, N) or lse_corr.dtype != torch.float32:
@@ -360,8 +409,10 @@ def sage_lse_correction(q: torch.Tensor, k_mean: torch.Tensor, sm_scale: float, 
     _need_gpu(q, k_mean)
     B, H, N, d = q.shape
     H_kv = k_mean.shape[1]
+    _check_tensor("sage_lse_correction", "k_mean", k_mean, (B, H_kv, d), torch.float32)
     if out is None:
         out = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_tensor("sage_lse_correction", "out", out, (B, H, N), torch.float32)
     _need_gpu(out)
     st = load_library().sage_lse_correction(q.data_ptr(), _dt(q.dtype), k_mean.data_ptr(), B, H,
                                             H_kv, N, d, float(sm_scale), out.data_ptr(),
@@ -376,6 +427,9 @@ def sage_qk_int32(q_i8: torch.Tensor, k_i8: torch.Tensor, b: int, h: int, *,
     _need_gpu(q_i8, k_i8)
     B, H, N, d = q_i8.shape
     H_kv = k_i8.shape[1]
+    if tuple(k_i8.shape) != (B, H_kv, N, d):
+        raise ValueError(f"sage_qk_int32: k_i8 {list(k_i8.shape)} does not match q_i8 "
+                         f"{list(q_i8.shape)}")
     s = torch.empty((N, N), dtype=torch.int32, device=q_i8.device)
     st = load_library().sage_qk_int32(q_i8.data_ptr(), k_i8.data_ptr(), B, H, H_kv, N, d, b, h,
                                       s.data_ptr(), _stream(stream, q_i8.device))

@@ -243,3 +243,52 @@ def test_q_group_inferred_from_scale_length():
             assert all(i // got == i // g for i in range(min(N, 300)))
     with pytest.raises(ValueError):
         qa._q_group_of(torch.zeros(1, 2, 5), 300)
+
+
+def _cpu_qk_vq(B=1, H=4, H_kv=2, N=200, d=64, q_group=128):
+    import torch
+    qk = qa._alloc_qk(B, H, H_kv, N, d, "cpu", q_group)
+    vq = qa._alloc_v(B, H_kv, N, d, "cpu")
+    return qk, vq
+
+
+def test_binding_rejects_short_or_mismatched_buffers_before_any_launch():
+    """A buffer shorter than the shapes need would be read or written past its
+    end by the kernels; the binding refuses it (on the host, before the device
+    check, so this runs without a GPU)."""
+    import torch
+    qk, vq = _cpu_qk_vq()
+    short = dict(vq, v_f8=vq["v_f8"][..., :-1])
+    with pytest.raises(ValueError, match="v_f8"):
+        qa.sage_attn_fwd(qk, short, causal=False, sm_scale=0.125)
+    with pytest.raises(ValueError, match="v_scale"):
+        qa.sage_attn_fwd(qk, dict(vq, v_scale=vq["v_scale"][..., :-1]), causal=False,
+                         sm_scale=0.125)
+    with pytest.raises(ValueError, match="k_scale"):
+        qa.sage_attn_fwd_lse(dict(qk, k_scale=qk["k_scale"][..., :-1]), vq, causal=False,
+                             sm_scale=0.125)
+    # K for another sequence length
+    other, _ = _cpu_qk_vq(N=100)
+    with pytest.raises(ValueError, match="k_i8"):
+        qa.sage_attn_fwd(dict(qk, k_i8=other["k_i8"]), vq, causal=False, sm_scale=0.125)
+    with pytest.raises(ValueError, match="out"):
+        qa.sage_attn_fwd(qk, vq, causal=False, sm_scale=0.125,
+                         out=torch.empty(1, 4, 199, 64, dtype=torch.float16))
+    with pytest.raises(ValueError, match="lse"):
+        qa.sage_attn_fwd_lse(qk, vq, causal=False, sm_scale=0.125,
+                             lse=torch.empty(1, 4, 199))
+    v4 = qa._alloc_v4(1, 2, 200, 64, "cpu")
+    with pytest.raises(ValueError, match="v_e8"):
+        qa.sage_attn_fwd_mxfp4(qk, dict(v4, v_e8=v4["v_e8"][..., :-1]), causal=False,
+                               sm_scale=0.125)
+    v = torch.zeros(1, 2, 200, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="v_f8"):
+        qa.sage_quant_v(v, out=short)
+    with pytest.raises(ValueError, match="v_f4"):
+        qa.sage_quant_v_mxfp4(v, out=dict(v4, v_f4=v4["v_f4"][..., :-1]))
+    q = torch.zeros(1, 4, 200, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="k_i8"):
+        qa.sage_quant_qk(q, v, out=dict(qk, k_i8=qk["k_i8"][..., :-1]))
+    # well-formed buffers get as far as the device check
+    with pytest.raises(ValueError, match="CUDA"):
+        qa.sage_attn_fwd(qk, vq, causal=False, sm_scale=0.125)
