@@ -500,7 +500,10 @@ def _workload_check(gpu_lib, name, heads, nrows, seed=0, q_group=128, smooth_q=F
     ("llm_prefill", [(0, 0), (0, 17), (0, 31)], 192),
     ("video_dit", [(0, 0), (0, 47)], 128),
     ("sweep@N1024", [(0, 0), (3, 31)], 192),
+    ("sweep@N2048", [(2, 5)], 128),
     ("sweep@N4096", [(1, 7)], 128),
+    ("sweep@N8192", [(0, 19)], 96),
+    ("sweep@N16384", [(3, 2)], 64),
     ("sweep@N32768", [(3, 30)], 64),
     ("gqa_long", [(0, 0), (0, 3), (0, 29)], 48),
 ])
