@@ -167,7 +167,11 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   // sum when every dequant factor ck = cq * k_scale of the tiles this
   // wave visits is <= kFastCk; otherwise kMagic is subtracted first.
   // Decided once per wave, so each path is a loop of its own (both paths
-  // pass the same barriers).
+  // pass the same barriers).  Rows that see at most 2 tiles of keys (causal
+  // q tiles 0 and 1, or N <= 256) always take the exact form: with few keys
+  // one P~ code that lands on the other side of an FP8 rounding midpoint
+  // moves the row's output by up to |v| / 12, and the one-FMA form's 2^-11
+  // argument error makes that about 100x likelier than fp32 rounding does.
   float kmax = 0.f;
   for (int i = lane; i < min(nkb, ntiles * (kKvTile / kBlkK)); i += 64) kmax = fmaxf(kmax, ksc[i]);
 #pragma unroll
@@ -175,7 +179,8 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   float cmax = cq;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, o));
-  const bool fast_wg = cmax * kmax <= kFastCk;
+  const bool few_keys = CAUSAL ? qt < 2 : N <= 2 * kKvTile;
+  const bool fast_wg = cmax * kmax <= kFastCk && !few_keys;
 
   auto step = [&](int t, auto mask_tag, auto fast_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
