@@ -5,7 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import it; the product never calls it and it shares no code with the
 HIP path.  Plain NumPy in float64 (float32 only where the method's own
 arithmetic is float32: the K mean cast, the smoothing subtraction, the scales
-and the x/scale divisions that decide integer codes).
+and the x/scale divisions that decide integer codes, and the FP8 rounding of
+448 * P~, decided on Algorithm 1's float32 softmax values).
 
 Two results are computed:
 
@@ -32,6 +33,8 @@ BLKK = 64         # K tokens per INT8 scale (Algorithm 1's b_kv)
 INT8_MAX = 127.0
 P_SCALE = 448.0   # static scale of P before the FP8 cast (Algorithm 1)
 KV_TILE = 128     # keys per online-softmax step of the GPU kernel
+LOG2E_F32 = np.float32(1.0 / math.log(2.0))        # log2 e in float32
+LOG2_P_SCALE_F32 = np.float32(math.log2(P_SCALE))  # log2 448 in float32
 
 
 # ---------------------------------------------------------------------------
@@ -283,6 +286,45 @@ def softmax_rows(q, k, *, causal: bool, sm_scale: float, b=0, h=0, hk=None):
 # update of the source-analysis page) accumulate to, followed by the final
 # rescale O = diag(l)^-1 O / 448 * delta_V.
 
+def sm_log2_f32(sm_scale: float) -> np.float32:
+    """sm_scale * log2 e in float32: the softmax runs in base 2 with the scale
+    folded into the exponent (source-analysis page, "attention kernel 前向")."""
+    return np.float32(np.float32(sm_scale) * LOG2E_F32)
+
+
+def _p448_decided_f32(sint, ck32, dsl32, valid, kv_tile):
+    """448 * P~ rounded to E4M3, the rounding decided in float32.
+
+    Algorithm 1 of the SageAttention2 detail page keeps S, the row max m and
+    P~ on chip in FP32 before P~ is cast to FP8, so the code of each P~ is
+    taken from float32 values (reading c25): x = fp32(S * ck) with S the exact
+    int32 dot and ck = fp32(fp32(sQ * sm_log2) * sK) (plus, with smoothed Q,
+    fp32(S * ck + fp32(Delta S * sm_log2))); m = the running max of x over
+    the tiles seen; the argument fp32(S * ck - fp32(m - log2 448)) (with Delta
+    S: fp32(x - fp32(m - log2 448))); e = fp32(2^argument); the code is
+    E4M3(e).  sint, ck32 (and dsl32) are [R, N]; valid masks keys; returns
+    float64 [R, N] (0 where not valid).
+    """
+    R, N = sint.shape
+    nt = -(-N // kv_tile)
+    x = sint * ck32.astype(np.float64)                     # exact: |S| < 2^22, ck 24 bits
+    x32 = (x + dsl32).astype(np.float32) if dsl32 is not None else x.astype(np.float32)
+    x32 = np.where(valid, x32, np.float32(-np.inf))
+    xp = np.full((R, nt * kv_tile), -np.inf, dtype=np.float32)
+    xp[:, :N] = x32
+    m32 = np.maximum.accumulate(xp.reshape(R, nt, kv_tile).max(axis=2), axis=1)
+    mq32 = (m32 - LOG2_P_SCALE_F32).astype(np.float32)    # [R, nt]
+    mq = np.repeat(mq32, kv_tile, axis=1)[:, :N]
+    with np.errstate(invalid="ignore"):
+        if dsl32 is not None:
+            a32 = (x32 - mq).astype(np.float32)
+        else:
+            a32 = (x - mq.astype(np.float64)).astype(np.float32)
+    a32 = np.where(valid, a32, np.float32(-np.inf))
+    e32 = np.exp2(a32.astype(np.float64)).astype(np.float32)
+    return fp8_e4m3.round_to_e4m3(e32.astype(np.float64))
+
+
 def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
                kv_tile: int = KV_TILE, rows=None, heads=None,
                quantize_p: bool = True, blkq: int = BLKQ, blkk: int = BLKK,
@@ -321,11 +363,12 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
             vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
         kf = kc[b, hk].astype(np.float64).T
         ksc = ks[b, hk, key_blk].astype(np.float64)[None, :]
+        sml32 = sm_log2_f32(sm_scale)
         for r0 in range(0, len(rows), chunk):
             rr = rows[r0:r0 + chunk]
             # exact integer dot products (|partial sums| <= 127^2 d < 2^53)
-            s = qc[b, h, rr].astype(np.float64) @ kf
-            s = s * qs[b, h, rr // blkq].astype(np.float64)[:, None]
+            sint = qc[b, h, rr].astype(np.float64) @ kf
+            s = sint * qs[b, h, rr // blkq].astype(np.float64)[:, None]
             s = s * ksc * sm_scale
             if delta_s is not None:
                 s = s + np.asarray(delta_s[b, h], dtype=np.float64)[rr // BLKQ] * sm_scale
@@ -342,8 +385,22 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
                 # so the rest of the recursion is shared with the FP8 form
                 codes, e = mxfp4.quantize_blocks(pt.reshape(len(rr), npad), axis=-1)
                 pq = (P_SCALE * mxfp4.dequantize_blocks(codes, e)).reshape(pt.shape)
+            elif quantize_p:
+                cq32 = (qs[b, h, rr // blkq].astype(np.float32) * sml32).astype(np.float32)
+                ck32 = (cq32[:, None] * ks[b, hk, key_blk].astype(np.float32)[None, :]).astype(
+                    np.float32)
+                dsl32 = None
+                if delta_s is not None:
+                    dsl32 = (np.asarray(delta_s[b, h], dtype=np.float64)[rr // BLKQ] *
+                             np.float64(sml32)).astype(np.float32)
+                valid = np.ones((len(rr), N), dtype=bool)
+                if causal:
+                    valid = np.arange(N)[None, :] <= rr[:, None]
+                pq = np.zeros((len(rr), npad))
+                pq[:, :N] = _p448_decided_f32(sint, ck32, dsl32, valid, kv_tile)
+                pq = pq.reshape(pt.shape)
             else:
-                pq = fp8_e4m3.round_to_e4m3(P_SCALE * pt) if quantize_p else P_SCALE * pt
+                pq = P_SCALE * pt
             carry = np.exp(m_run - m_fin)                                # exp(m_t - m_T)
             l = np.sum(pt.sum(axis=2) * carry, axis=1)
             w = (pq * carry[:, :, None]).reshape(len(rr), npad)[:, :N]
@@ -383,21 +440,33 @@ def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
         vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
     out = np.zeros((n, d))
     lse = np.zeros(n)
+    sml32 = sm_log2_f32(sm_scale)
     for i in range(n):
         m, l = -math.inf, 0.0
+        m32 = np.float32(-np.inf)           # the float32 running max of the P~ decisions
+        cq32 = np.float32(np.float32(qs[b, h, i // blkq]) * sml32)
         o = [0.0] * d
         for t0 in range(0, n, kv_tile):
             keys = range(t0, min(t0 + kv_tile, n))
             srow = {}
+            xs = {}                         # float64 S * ck and float32 x of each key
             for j in keys:
                 if causal and j > i:
                     continue
                 acc = sum(int(qc[b, h, i, c]) * int(kc[b, hk, j, c]) for c in range(d))
                 srow[j] = acc * float(qs[b, h, i // blkq]) * float(ks[b, hk, j // blkk]) * sm_scale
+                ck32 = np.float32(cq32 * np.float32(ks[b, hk, j // blkk]))
+                x = acc * float(ck32)
                 if delta_s is not None:
                     srow[j] += float(delta_s[b, h, i // BLKQ, j]) * sm_scale
+                    dsl = np.float32(float(delta_s[b, h, i // BLKQ, j]) * float(sml32))
+                    xs[j] = (x, np.float32(x + float(dsl)))
+                else:
+                    xs[j] = (x, np.float32(x))
             if not srow:
                 continue
+            m32 = max(m32, max(x32 for _, x32 in xs.values()))
+            mq32 = np.float32(m32 - LOG2_P_SCALE_F32)
             m_new = max(m, max(srow.values()))
             alpha = math.exp(m - m_new) if m != -math.inf else 0.0
             l = alpha * l
@@ -412,7 +481,12 @@ def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
                     sc = 2.0 ** int(mxfp4.scale_exponent(amax))
                     pq = P_SCALE * float(mxfp4.decode(mxfp4.encode(pt / sc))) * sc
                 else:
-                    pq = float(fp8_e4m3.round_to_e4m3(P_SCALE * pt))
+                    # the E4M3 code decided in float32 (see _p448_decided_f32)
+                    x, x32 = xs[j]
+                    a32 = np.float32(x32 - mq32) if delta_s is not None else np.float32(
+                        x - float(mq32))
+                    e32 = np.float32(np.exp2(np.float64(a32)))
+                    pq = float(fp8_e4m3.round_to_e4m3(float(e32)))
                 for c in range(d):
                     o[c] += pq * vdq[j, c]
             m = m_new

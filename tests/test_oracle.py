@@ -728,3 +728,50 @@ def test_lse_correction_restores_unsmoothed_lse(causal):
     corr = O.lse_correction(q, z["k_mean"], sm_scale=0.125)
     assert np.abs(ls + corr - lx).max() < 0.05
     assert np.abs(ls - lx).max() > 1.0
+
+
+@pytest.mark.parametrize("with_ds,causal", [(False, False), (False, True), (True, True)])
+def test_p_codes_decided_in_float32_differ_only_at_midpoints(with_ds, causal):
+    """The E4M3 code of 448 * P~ is taken on float32 values (Algorithm 1's on-chip
+    softmax).  Against the same step in float64 (scores S sQ sK sm log2 e, the running
+    max per 128-key tile, 448 * 2^(x - m)), a code may differ only where the float64 value
+    lies within a few float32 ulps of an E4M3 rounding midpoint, and only rarely.  A wrong
+    factor, max, tile or Delta S term would move codes far from any midpoint."""
+    g = np.random.default_rng(31)
+    n, d = 300, 64
+    q = torch.from_numpy(g.standard_normal((1, 1, n, d)).astype(np.float32) * 1.5).half()
+    k = torch.from_numpy(g.standard_normal((1, 1, n, d)).astype(np.float32) + 2).half()
+    qz = O.quantize_qk(q, k, smooth_q=with_ds)
+    sm = 0.125
+    ds = O.delta_s(qz["q_mean"], k, qz["k_mean"]) if with_ds else None
+    rows = np.arange(n)
+    sint = qz["q_i8"][0, 0].astype(np.float64) @ qz["k_i8"][0, 0].astype(np.float64).T
+    qs = qz["q_scale"][0, 0][rows // O.BLKQ]
+    ks = qz["k_scale"][0, 0][np.arange(n) // O.BLKK]
+    valid = (np.arange(n)[None, :] <= rows[:, None]) if causal else np.ones((n, n), bool)
+    sml = O.sm_log2_f32(sm)
+    ck32 = ((qs.astype(np.float32) * sml).astype(np.float32)[:, None] *
+            ks.astype(np.float32)[None, :]).astype(np.float32)
+    dsl32 = (ds[0, 0][rows // O.BLKQ] * np.float64(sml)).astype(np.float32) if with_ds else None
+    got = O._p448_decided_f32(sint, ck32, dsl32, valid, O.KV_TILE)
+    # float64: the same scores and running max without any float32 rounding
+    x = sint * qs.astype(np.float64)[:, None] * ks.astype(np.float64)[None, :] * sm / math.log(2)
+    if with_ds:
+        x = x + ds[0, 0][rows // O.BLKQ] * sm / math.log(2)
+    x = np.where(valid, x, -np.inf)
+    nt = -(-n // O.KV_TILE)
+    xp = np.full((n, nt * O.KV_TILE), -np.inf)
+    xp[:, :n] = x
+    m = np.maximum.accumulate(xp.reshape(n, nt, O.KV_TILE).max(axis=2), axis=1)
+    p64 = np.where(valid, O.P_SCALE * np.exp2(x - np.repeat(m, O.KV_TILE, axis=1)[:, :n]), 0.0)
+    want = F8.round_to_e4m3(p64)
+    diff = np.argwhere(got != want)
+    assert len(diff) <= 1e-3 * valid.sum(), len(diff)
+    for i, j in diff:
+        mid = 0.5 * (got[i, j] + want[i, j])
+        # both codes are neighbours, and p64 sits next to the midpoint between them
+        assert abs(got[i, j] - want[i, j]) <= 0.13 * max(got[i, j], want[i, j])
+        assert abs(p64[i, j] - mid) <= 2.0 ** -19 * (1 + abs(x[i, j])) * p64[i, j], (i, j)
+    # the decisions are not trivially equal to the float64 ones by construction:
+    # the float32 x carries rounding (else this test would not exercise anything)
+    assert np.any(ck32.astype(np.float64) != qs[:, None] * ks[None, :] * sm / math.log(2))
