@@ -5,17 +5,22 @@
 // score of the block; its pipeline figure computes that GEMV before
 // quantization, on the smoothed K.  Here, for every (b, h), 128-token Q
 // block i and key j:
-//   out[b][h][i][j] = sm_scale * log2(e) * sum_c q_mean[b][h][i][c] * Ks[j][c],
+//   out[b][h][i][j] = fp32(sum_c q_mean[b][h][i][c] * Ks[j][c] * sm_log2),
 //   Ks[j][c] = float32(K[b][h_kv][j][c]) - k_mean[b][h_kv][c]
 // (the values the K quantizer sees), already in the attention kernel's
-// log2 score units.  Products and sums are FP32 on the matrix cores
-// (v_mfma_f32_32x32x2_f32).
+// log2 score units.  The products of the float32 operands are exact in
+// FP64 and the sums are taken in FP64 on the matrix cores
+// (v_mfma_f64_16x16x4_f64), so the stored value is the float32 rounding of
+// an almost exact sum: it does not depend on a summation order.  Each table
+// entry decides scores that the FP8 rounding of P~ turns into codes, so its
+// value must not move with the order of an FP32 sum.
 //
-// Work split: a workgroup of 4 waves owns 128 keys of one (b, h).  Each wave
-// keeps its 32 keys' smoothed K rows in registers (the B operand, d/2
-// floats per lane) and walks the ceil(N/128) mean rows 32 at a time (the A
-// operand, read from L2).  Contraction index: MFMA i of a lane in half g
-// uses channel g*d/2 + i for both operands, so the sum covers every channel.
+// Work split: a workgroup of 4 waves owns 64 keys of one (b, h).  Each wave
+// keeps its 16 keys' smoothed K rows in registers as FP64 (the B operand,
+// d/4 doubles per lane) and walks the ceil(N/128) mean rows 16 at a time
+// (the A operand, read from L2).  Contraction index: MFMA s of a lane in
+// group g = L/16 uses channel g*d/4 + s for both operands, so the d/4 MFMAs
+// cover every channel, and each lane's channels are contiguous.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,25 +28,28 @@
 
 namespace sage {
 
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k,
                                                       const float* __restrict__ k_mean,
                                                       const float* __restrict__ q_mean,
                                                       float* __restrict__ out, int H, int H_kv,
                                                       int N, int nmb, float sm_log2) {
-  constexpr int HALF = D / 2;
+  constexpr int QD = D / 4;   // channels per lane group
   const int bh = blockIdx.y, b = bh / H, h = bh % H, hk = h / (H / H_kv);
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  const int col = lane % 32, g = lane / 32;
-  const int key = blockIdx.x * 128 + wave * 32 + col;
-  // B operand: this lane's key (rows past N read row N-1 and are not stored)
-  float kb[HALF];
+  const int col = lane % 16, g = lane / 16;
+  const int key = blockIdx.x * 64 + wave * 16 + col;
+  // B operand: this lane's key, channels g*QD .. g*QD + QD - 1 (rows past N
+  // read row N-1 and are not stored)
+  double kb[QD];
   {
     const uint16_t* kr = reinterpret_cast<const uint16_t*>(k) +
-                         ((size_t)(b * H_kv + hk) * N + min(key, N - 1)) * D + g * HALF;
-    const float* km = k_mean + (size_t)(b * H_kv + hk) * D + g * HALF;
+                         ((size_t)(b * H_kv + hk) * N + min(key, N - 1)) * D + g * QD;
+    const float* km = k_mean + (size_t)(b * H_kv + hk) * D + g * QD;
 #pragma unroll
-    for (int j = 0; j < HALF / 8; ++j) {
+    for (int j = 0; j < QD / 8; ++j) {
       const uint4 u = *reinterpret_cast<const uint4*>(kr + j * 8);
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -54,32 +62,32 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
           lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
           hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
         }
-        kb[j * 8 + 2 * i] = lo - km[j * 8 + 2 * i];
-        kb[j * 8 + 2 * i + 1] = hi - km[j * 8 + 2 * i + 1];
+        kb[j * 8 + 2 * i] = (double)(lo - km[j * 8 + 2 * i]);
+        kb[j * 8 + 2 * i + 1] = (double)(hi - km[j * 8 + 2 * i + 1]);
       }
     }
   }
   const float* qm = q_mean + (size_t)bh * nmb * D;
   float* ob = out + (size_t)bh * nmb * N;
-  for (int r0 = 0; r0 < nmb; r0 += 32) {
+  const double scale = (double)sm_log2;
+  for (int r0 = 0; r0 < nmb; r0 += 16) {
     // A operand: mean row r0 + col (rows past nmb read the last row, not stored)
-    const float* qr = qm + (size_t)min(r0 + col, nmb - 1) * D + g * HALF;
-    f32x16 acc;
+    const float* qr = qm + (size_t)min(r0 + col, nmb - 1) * D + g * QD;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int i = 0; i < HALF; i += 4) {
+    for (int i = 0; i < QD; i += 4) {
       const float4 a = *reinterpret_cast<const float4*>(qr + i);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, kb[i], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, kb[i + 1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, kb[i + 2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, kb[i + 3], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.x, kb[i], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.y, kb[i + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.z, kb[i + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.w, kb[i + 3], acc, 0, 0, 0);
     }
+    // lane L holds rows 4r + L/16 of the 16x16 result, column L%16 (its key)
     if (key < N) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = r0 + 8 * (r / 4) + 4 * g + (r % 4);
-        if (row < nmb) ob[(size_t)row * N + key] = acc[r] * sm_log2;
+      for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 4 * r + g;
+        if (row < nmb) ob[(size_t)row * N + key] = (float)(acc[r] * scale);
       }
     }
   }
@@ -92,7 +100,7 @@ hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, con
                                hipStream_t st) {
   using namespace sage;
   const int nmb = (N + kBlkQ - 1) / kBlkQ;
-  const dim3 grid((N + 127) / 128, B * H), block(256);
+  const dim3 grid((N + 63) / 64, B * H), block(256);
   const float sm_log2 = sm_scale * kLog2e;
 #define SAGE_DS(DD, BB)                                                                         \
   if (d == DD && (bf16 != 0) == BB) {                                                           \

@@ -260,14 +260,15 @@ LOG2E = 1.4426950408889634
 
 
 def _check_delta_s_table(ds_gpu, ds_ref, q_mean, k, k_mean, sm):
-    """One head's table: GPU = sm * log2(e) * q_bar . K_s in FP32 against the oracle's exact
-    q_bar . K_s, within the FP32 dot-product bound (d + 4) * 2^-24 * sum |q_bar_c K_s,c|."""
-    d = q_mean.shape[-1]
-    ks = (np.asarray(k, dtype=np.float32) - np.asarray(k_mean, dtype=np.float32)).astype(np.float32)
-    absb = np.abs(np.asarray(q_mean, dtype=np.float64)) @ np.abs(ks.astype(np.float64)).T
-    l2 = sm * LOG2E
-    err = np.abs(ds_gpu.astype(np.float64) - ds_ref * l2)
-    assert np.all(err <= (d + 4) * 2.0 ** -24 * l2 * absb + 1e-30), err.max()
+    """One head's table against the oracle's q_bar . K_s (float64): the GPU sums the exact
+    products in FP64 and rounds once, so each entry is fp32(q_bar . K_s * sm_log2) with
+    sm_log2 = fp32(sm * log2 e).  FP64 sums in another order can only move an entry
+    that sits on a float32 rounding boundary, by one float32 step."""
+    want = (np.asarray(ds_ref, dtype=np.float64) * np.float64(O.sm_log2_f32(sm))).astype(np.float32)
+    got = np.asarray(ds_gpu, dtype=np.float32)
+    steps = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert np.all((steps <= 1) | (got == want)), steps.max()
+    assert np.count_nonzero(got != want) <= 1e-4 * got.size + 1, np.count_nonzero(got != want)
 
 
 def _biased_q_inputs(B, H, H_kv, N, d, dtype, seed, qbias=1.5):
