@@ -162,10 +162,13 @@ sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype,
  * The Delta S table of smooth Q (SageAttention2 detail page, Algorithm 1:
  * S_ij = dequant(Q^_i K^_j^T) + GEMV(q_bar_i, K_j^T); its pipeline figure
  * computes the GEMV before quantization, on the smoothed K):
- *   delta_s[b][h][i][j] = sm_scale * log2(e) * sum_c q_mean[b][h][i][c] *
+ *   delta_s[b][h][i][j] = float32( sum_c q_mean[b][h][i][c] *
  *                         (float32(k[b][h/(H/H_kv)][j][c]) - k_mean[b][h/(H/H_kv)][c])
+ *                         * float32(sm_scale * log2(e)) )
  * for every 128-token Q block i and key j < N, in the attention kernel's
- * log2 score units, FP32 products and sums (FP32 matrix cores).
+ * log2 score units.  The products are exact and the sums are FP64 (FP64
+ * matrix cores), rounded once: each entry is the float32 rounding of the
+ * exact value up to the FP64 sum's rounding, whatever the summation order.
  *   k: the original K in `dtype`; k_mean, q_mean: from sage_quant_qk
  *   (k_mean is zeros when K was not smoothed).  sm_scale must be the one
  *   passed to sage_attn_fwd.  delta_s: float, sizes.delta_s bytes.
