@@ -86,11 +86,12 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   // by one, both waves reach their exponentials together, and the SIMD
   // alternates between MFMA-only and VALU-only stretches.  The workgroup in
   // an odd slot of its CU (HW_ID.TG_ID) takes priority 3 for its MFMA phase
-  // (P V of tile t, the barrier, QK^T of tile t+1), the other 2, and both
-  // drop to 0 for the exponentials.  One wave then finishes its MFMA phase
-  // first, and the other's follows while it computes exponentials: +3 % at
-  // N = 32K, +7 % at N = 4K, +8 % on a causal 4K prefill.  d = 64 (three
-  // workgroups, MFMAs already interleaved with the exponentials) gains nothing.
+  // (P V of tile t with the exponentials interleaved into it, the barrier,
+  // QK^T of tile t+1), the other 2, and both drop to 0 after QK^T for the
+  // row max and the first exponentials.  One wave then finishes its MFMA
+  // phase first, and the other's follows while it computes exponentials:
+  // +3 % at N = 32K, +7 % at N = 4K, +8 % on a causal 4K prefill.  d = 64
+  // (three workgroups per CU) gains nothing.
   const bool mfma_first = (__builtin_amdgcn_s_getreg((3 << 11) | (16 << 6) | 4) & 1) != 0;
   auto prio_mfma = [&]() __attribute__((always_inline)) {
     if constexpr (D != 64) {
@@ -357,21 +358,20 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         pf[kb / 2][(kb % 2) * 4 + r0 / 4 + w] = pk;
       }
     };
-    // ---- P, then O^T += V^T P^T on the FP8 matrix cores.  With d = 64 the
-    // registers allow overlapping: the MFMAs of keys 0..63 go one at a time
-    // beside 1/NKC of the exponentials of keys 64..127 (a wave's MFMAs only
-    // overlap well with its own VALU work), then those of keys 64..127.
-    // With d = 128 there is no room for that (it spills); all of P first.
+    // ---- P, then O^T += V^T P^T on the FP8 matrix cores, overlapped: the
+    // MFMAs of keys 0..63 go one at a time beside 1/NKC of the exponentials
+    // of keys 64..127 (a wave's MFMAs overlap well with its own VALU work),
+    // then those of keys 64..127.  With d = 128 the matrix-core precedence
+    // starts with the first of them.
     auto exp_pv = [&](auto fast_tag) __attribute__((always_inline)) {
       using E16 = std::integral_constant<int, 16>;
       using EC = std::integral_constant<int, 32 / NKC>;
-      if constexpr (D != 64) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) exp_part(kb, 0, E16{}, fast_tag);
-      } else {
+      {
         exp_part(0, 0, E16{}, fast_tag);
         exp_part(1, 0, E16{}, fast_tag);
         __builtin_amdgcn_sched_barrier(0);
+        prio_mfma();
+
 #pragma unroll
         for (int c = 0; c < NKC; ++c) {
           const i32x8 vn = vfrag(c + 2);
@@ -457,20 +457,6 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
       }
     } else {
     exp_pv(fast_tag);
-    if constexpr (D != 64) {
-      prio_mfma();
-#pragma unroll
-      for (int idx = 0; idx < 2 * NKC; ++idx) {
-        const int kb = idx / NKC, c = idx % NKC;
-        const i32x8 vn = (idx + 2 < 2 * NKC) ? vfrag(idx + 2) : i32x8{};
-        __builtin_amdgcn_sched_barrier(0);
-        acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[kb], acc_o[c], 0, 0, 0,
-                                                                     127, 0, 127);
-        __builtin_amdgcn_sched_barrier(0);
-        va = vb;
-        vb = vn;
-      }
-    }
     }
   };
 
