@@ -1,4 +1,5 @@
-"""Host-side contract of bench.py: one GPU only, no CPU fallback, known workloads."""
+"""Host-side contracts: bench.py measures one GPU only and has no CPU fallback, its
+workloads exist, and the binding and smoke() refuse to run without a GPU."""
 import os
 import subprocess
 import sys
@@ -41,3 +42,18 @@ def test_every_workload_the_benchmark_names_exists():
         w = W.get(name)
         assert w.N > 0 and w.d in (64, 128) and w.H % w.H_kv == 0, name
     assert W.get("sweep@N32768").N == 32768
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_binding_refuses_host_tensors():
+    import quantized_attention_amd as qa
+    q = torch.randn(1, 2, 64, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="CUDA"):
+        qa.sageattn(q, q, q)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_smoke_refuses_a_host_without_a_gpu():
+    import __graft_entry__ as g
+    with pytest.raises(AssertionError, match="needs a GPU"):
+        g.smoke()
