@@ -22,6 +22,7 @@ Where the pages leave a step open the reading taken is stated at the step.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -34,7 +35,6 @@ INT8_MAX = 127.0
 P_SCALE = 448.0   # static scale of P before the FP8 cast (Algorithm 1)
 KV_TILE = 128     # keys per online-softmax step of the GPU kernel
 LOG2E_F32 = np.float32(1.0 / math.log(2.0))        # log2 e in float32
-LOG2_P_SCALE_F32 = np.float32(math.log2(P_SCALE))  # log2 448 in float32
 
 
 # ---------------------------------------------------------------------------
@@ -274,55 +274,99 @@ def softmax_rows(q, k, *, causal: bool, sm_scale: float, b=0, h=0, hk=None):
 # (ii) The quantized attention of Algorithm 1 (SageAttention2 detail page),
 # INT8 QK^T and FP8 PV, written as the sums the online recursion produces.
 #
-# Per query row i and key tile t (tiles of ``kv_tile`` keys, ascending):
-#   S_ij   = (sum_c qcode_ic kcode_jc) * dQ(i) * dK(j) * sm_scale, masked to -inf
-#   m_t    = max(m_{t-1}, rowmax_t S)                      (running max)
-#   Pt_ij  = exp(S_ij - m_t)                               (P tilde)
-#   Pq_ij  = E4M3(448 * Pt_ij)                             (static P scale)
-#   l      = sum_t exp(m_t - m_T) rowsum(Pt_t)             (unquantized P tilde)
-#   O_i    = [sum_t exp(m_t - m_T) sum_{j in t} Pq_ij Vdq_j] / (448 l)
+# Per query row i and key tile t (tiles of ``kv_tile`` keys, ascending), in
+# base 2 (the source-analysis page, "attention kernel 前向": the kernel
+# multiplies sm_scale by log2 e, so scores are in log2 units):
+#   x_ij  = S^_ij * c_ij   (+ Delta S term with smoothed Q), masked to -inf,
+#           S^ the exact int32 dot of the codes, c = dQ dK sm_scale log2 e
+#   m_t   = max(m_{t-1}, rowmax_t x)                      (running max)
+#   Pt_ij = 2^(x_ij - m_t)                                (P tilde)
+#   Pq_ij = E4M3(448 * Pt_ij)                             (static P scale)
+#   l     = sum_t 2^(m_t - m_T) rowsum(Pt_t)              (unquantized P tilde)
+#   O_i   = [sum_t 2^(m_t - m_T) sum_{j in t} Pq_ij Vdq_j] / (448 l)
 # which is what "l = exp(m_old - m_new) l + rowsum(Pt)" and
 # "O = diag(exp(m_old - m_new)) O + Pq V" (Algorithm 1 and the online-softmax
 # update of the source-analysis page) accumulate to, followed by the final
 # rescale O = diag(l)^-1 O / 448 * delta_V.
+#
+# Precision (reading c25).  The FP8 code of 448 * Pt is a rounding decision,
+# so it is taken in the precision the method computes Pt in: float32, the
+# precision of the scales, of Algorithm 1's level-2 accumulator and of the
+# kernel's softmax registers.  The steps, each a value the pages name and each
+# rounded once to float32 (round to nearest even):
+#   lam = sm_scale * log2 e                      (the softmax constant)
+#   c   = (dQ * dK) * lam                         (psi^-1's scale product, then lam)
+#   x   = S^ * c            (with smoothed Q: S^ * c + g, g = Delta S * lam)
+#   m   = the running max of x                    (a max: no rounding)
+#   a   = x - m                                   (exp's argument; 0 at the max)
+#   Pt  = 2^a
+#   y   = Pt * 448, then E4M3 round-to-nearest-even of y.
+# x is Algorithm 1's S_ij in log2 units, one float32 rounding of its exact
+# terms (the scaled integer dot, plus the Delta S term with smoothed Q).
+# l, the tile carries 2^(m_t - m_T) and O stay float64 (no decision rides on
+# them).  ``quantize_p=False`` keeps the whole path in float64 instead (P is
+# not rounded at all): the pin against exact attention on dequantized inputs.
 
 def sm_log2_f32(sm_scale: float) -> np.float32:
-    """sm_scale * log2 e in float32: the softmax runs in base 2 with the scale
-    folded into the exponent (source-analysis page, "attention kernel 前向")."""
+    """lam = float32(sm_scale * log2 e), both factors float32 (sm_scale is the
+    float the C ABI takes)."""
     return np.float32(np.float32(sm_scale) * LOG2E_F32)
 
 
-def _p448_decided_f32(sint, ck32, dsl32, valid, kv_tile):
-    """448 * P~ rounded to E4M3, the rounding decided in float32.
+def rn32(x) -> np.ndarray:
+    """float64 -> the nearest float32 (ties to even)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
 
-    Algorithm 1 of the SageAttention2 detail page keeps S, the row max m and
-    P~ on chip in FP32 before P~ is cast to FP8, so the code of each P~ is
-    taken from float32 values (reading c25): x = fp32(S * ck) with S the exact
-    int32 dot and ck = fp32(fp32(sQ * sm_log2) * sK) (plus, with smoothed Q,
-    fp32(S * ck + fp32(Delta S * sm_log2))); m = the running max of x over
-    the tiles seen; the argument fp32(S * ck - fp32(m - log2 448)) (with Delta
-    S: fp32(x - fp32(m - log2 448))); e = fp32(2^argument); the code is
-    E4M3(e).  sint, ck32 (and dsl32) are [R, N]; valid masks keys; returns
-    float64 [R, N] (0 where not valid).
+
+def rn32_sum(a, b) -> np.ndarray:
+    """The float32 nearest (ties to even) to the EXACT sum a + b of two finite
+    float64 arrays.  s = a + b is rounded once to float64 first; that can only
+    mislead the float32 rounding when s is itself halfway between two float32
+    values and the float64 sum was inexact, where the exact residual (Knuth's
+    TwoSum) says on which side the true sum lies."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    s = a + b
+    bb = s - a
+    err = (a - (s - bb)) + (b - bb)                 # a + b = s + err exactly
+    r = s.astype(np.float32)
+    r64 = r.astype(np.float64)
+    up = np.nextafter(r, np.float32(np.inf))
+    dn = np.nextafter(r, np.float32(-np.inf))
+    other = np.where(s > r64, up, dn)
+    tie = (s != r64) & (2.0 * s == r64 + other.astype(np.float64))
+    go = tie & (((err > 0) & (other > r)) | ((err < 0) & (other < r)))
+    return np.where(go, other, r).astype(np.float32)
+
+
+def softmax_f32(sint, c32, g32, valid, kv_tile):
+    """Algorithm 1's online softmax on float32 values, for rows of scores.
+
+    sint: exact integer dots (float64) [R, N]; c32: float32 factors c [R, N];
+    g32: float32 Delta S terms [R, N] or None; valid: bool [R, N].
+    Returns (pt32 float32 [R, N], 0 where not valid; m32 float32 [R, nt], the
+    running max after each tile of kv_tile keys).
     """
     R, N = sint.shape
     nt = -(-N // kv_tile)
-    x = sint * ck32.astype(np.float64)                     # exact: |S| < 2^22, ck 24 bits
-    x32 = (x + dsl32).astype(np.float32) if dsl32 is not None else x.astype(np.float32)
-    x32 = np.where(valid, x32, np.float32(-np.inf))
+    prod = np.where(valid, sint, 0.0) * c32.astype(np.float64)  # exact: |S^| < 2^22, c 24 bits
+    g = None if g32 is None else np.where(valid, g32, 0).astype(np.float64)
+    x32 = rn32(prod) if g is None else rn32_sum(prod, g)
     xp = np.full((R, nt * kv_tile), -np.inf, dtype=np.float32)
-    xp[:, :N] = x32
+    xp[:, :N] = np.where(valid, x32, np.float32(-np.inf))
     m32 = np.maximum.accumulate(xp.reshape(R, nt, kv_tile).max(axis=2), axis=1)
-    mq32 = (m32 - LOG2_P_SCALE_F32).astype(np.float32)    # [R, nt]
-    mq = np.repeat(mq32, kv_tile, axis=1)[:, :N]
-    with np.errstate(invalid="ignore"):
-        if dsl32 is not None:
-            a32 = (x32 - mq).astype(np.float32)
-        else:
-            a32 = (x - mq.astype(np.float64)).astype(np.float32)
-    a32 = np.where(valid, a32, np.float32(-np.inf))
-    e32 = np.exp2(a32.astype(np.float64)).astype(np.float32)
-    return fp8_e4m3.round_to_e4m3(e32.astype(np.float64))
+    mk = np.repeat(m32, kv_tile, axis=1)[:, :N].astype(np.float64)
+    mk = np.where(valid, mk, 0.0)
+    a32 = rn32_sum(np.where(valid, x32, np.float32(0)), -mk)
+    pt32 = rn32(np.exp2(a32.astype(np.float64)))
+    return np.where(valid, pt32, np.float32(0)), m32
+
+
+def p_fp8(pt32) -> np.ndarray:
+    """(P~ * 448).to(FP8 E4M3): the float32 product, rounded to nearest even
+    onto the E4M3 grid; float64 values of the codes."""
+    y32 = rn32(np.asarray(pt32, dtype=np.float64) * P_SCALE)   # exact product, one rounding
+    return fp8_e4m3.round_to_e4m3(y32.astype(np.float64))
 
 
 def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
@@ -333,16 +377,16 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
 
     qc int8 [B,H,N,d], qs f32 [B,H,nq]; kc int8 [B,H_kv,N,d], ks f32
     [B,H_kv,nk]; vc uint8 E4M3 codes [B,H_kv,N,d] (natural layout), vs f32
-    [B,H_kv,d].  ``quantize_p=False`` skips the FP8 rounding of 448*Pt (the
-    result is then exact attention on the dequantized inputs).  With
-    ``return_lse`` also L'_i = m_T + ln l (natural log) of the dequantized
-    scores S the recursion used -- of the smoothed K when the codes are of
-    K - mean(K); ``lse_correction`` restores the unsmoothed value.
-    ``delta_s`` ([B,H,ceil(N/128),N], from ``delta_s``): with smoothed-Q codes,
-    sm_scale * Delta S[query's 128-block, key] is added to every score.
-    ``pv="mxfp4"``: vc, vs are ``quantize_v_mxfp4``'s codes and exponents, and
-    P~ of each 32-key block of a row is MX-quantized (no factor 448) before
-    the product (the reading stated at ``quantize_v_mxfp4``).
+    [B,H_kv,d].  ``quantize_p=False`` skips the FP8 rounding of 448*Pt and keeps
+    every step in float64 (the result is then exact attention on the
+    dequantized inputs).  With ``return_lse`` also L'_i = ln 2 (m_T + log2 l)
+    (natural log) of the dequantized scores the recursion used -- of the
+    smoothed K when the codes are of K - mean(K); ``lse_correction`` restores
+    the unsmoothed value.  ``delta_s`` ([B,H,ceil(N/128),N], from ``delta_s``):
+    with smoothed-Q codes, Delta S[query's 128-block, key] is added to every
+    score.  ``pv="mxfp4"``: vc, vs are ``quantize_v_mxfp4``'s codes and
+    exponents, and P~ of each 32-key block of a row is MX-quantized (no factor
+    448) before the product (the reading stated at ``quantize_v_mxfp4``).
     """
     B, H, N, d = qc.shape
     grp = H // kc.shape[1]
@@ -352,9 +396,10 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
     key_blk = np.arange(N) // blkk
     out = np.zeros((B, H, len(rows), d))
     lse = np.zeros((B, H, len(rows)))
-    chunk = max(1, (1 << 24) // npad)               # bound the [rows, keys] temporaries
+    chunk = max(1, (1 << 23) // npad)               # bound the [rows, keys] temporaries
     mx = pv == "mxfp4"
     assert pv in ("fp8", "mxfp4") and (not mx or kv_tile % mxfp4.MX_BLOCK == 0)
+    lam = sm_log2_f32(sm_scale)
     for b, h in (heads or [(b, h) for b in range(B) for h in range(H)]):
         hk = h // grp
         if mx:
@@ -362,50 +407,56 @@ def attn_quant(qc, qs, kc, ks, vc, vs, *, causal: bool, sm_scale: float,
         else:
             vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
         kf = kc[b, hk].astype(np.float64).T
-        ksc = ks[b, hk, key_blk].astype(np.float64)[None, :]
-        sml32 = sm_log2_f32(sm_scale)
+        dk = ks[b, hk, key_blk].astype(np.float32)
         for r0 in range(0, len(rows), chunk):
             rr = rows[r0:r0 + chunk]
+            R = len(rr)
             # exact integer dot products (|partial sums| <= 127^2 d < 2^53)
             sint = qc[b, h, rr].astype(np.float64) @ kf
-            s = sint * qs[b, h, rr // blkq].astype(np.float64)[:, None]
-            s = s * ksc * sm_scale
-            if delta_s is not None:
-                s = s + np.asarray(delta_s[b, h], dtype=np.float64)[rr // BLKQ] * sm_scale
+            valid = np.ones((R, N), dtype=bool)
             if causal:
-                s = np.where(np.arange(N)[None, :] > rr[:, None], -np.inf, s)
-            sp = np.full((len(rr), npad), -np.inf)
-            sp[:, :N] = s
-            st = sp.reshape(len(rr), nt, kv_tile)
-            m_run = np.maximum.accumulate(st.max(axis=2), axis=1)        # [R, nt]
-            m_fin = m_run[:, -1:]
-            pt = np.exp(st - m_run[:, :, None])                          # P tilde in [0, 1]
-            if mx:
-                # P~ in MX blocks of 32 consecutive keys; scaled back to P~ * 448
-                # so the rest of the recursion is shared with the FP8 form
-                codes, e = mxfp4.quantize_blocks(pt.reshape(len(rr), npad), axis=-1)
-                pq = (P_SCALE * mxfp4.dequantize_blocks(codes, e)).reshape(pt.shape)
-            elif quantize_p:
-                cq32 = (qs[b, h, rr // blkq].astype(np.float32) * sml32).astype(np.float32)
-                ck32 = (cq32[:, None] * ks[b, hk, key_blk].astype(np.float32)[None, :]).astype(
-                    np.float32)
-                dsl32 = None
+                valid = np.arange(N)[None, :] <= rr[:, None]
+            dq = qs[b, h, rr // blkq].astype(np.float32)
+            if not quantize_p:
+                # float64 throughout, natural-log units, P not rounded
+                s = sint * dq.astype(np.float64)[:, None] * dk.astype(np.float64)[None, :]
+                s = s * sm_scale
                 if delta_s is not None:
-                    dsl32 = (np.asarray(delta_s[b, h], dtype=np.float64)[rr // BLKQ] *
-                             np.float64(sml32)).astype(np.float32)
-                valid = np.ones((len(rr), N), dtype=bool)
-                if causal:
-                    valid = np.arange(N)[None, :] <= rr[:, None]
-                pq = np.zeros((len(rr), npad))
-                pq[:, :N] = _p448_decided_f32(sint, ck32, dsl32, valid, kv_tile)
-                pq = pq.reshape(pt.shape)
+                    s = s + np.asarray(delta_s[b, h], dtype=np.float64)[rr // BLKQ] * sm_scale
+                s = np.where(valid, s, -np.inf)
+                sp = np.full((R, npad), -np.inf)
+                sp[:, :N] = s
+                st = sp.reshape(R, nt, kv_tile)
+                m_run = np.maximum.accumulate(st.max(axis=2), axis=1)
+                carry = np.exp(m_run - m_run[:, -1:])
+                pt = np.exp(st - m_run[:, :, None])
+                l = np.sum(pt.sum(axis=2) * carry, axis=1)
+                w = (P_SCALE * pt * carry[:, :, None]).reshape(R, npad)[:, :N]
+                out[b, h, r0:r0 + chunk] = (w @ vdq) / (P_SCALE * l)[:, None]
+                lse[b, h, r0:r0 + chunk] = m_run[:, -1] + np.log(l)
+                continue
+            c32 = rn32(rn32(dq.astype(np.float64)[:, None] * dk.astype(np.float64)[None, :])
+                       .astype(np.float64) * np.float64(lam))
+            g32 = None
+            if delta_s is not None:
+                g32 = rn32(np.asarray(delta_s[b, h], dtype=np.float64)[rr // BLKQ] *
+                           np.float64(lam))
+            pt32, m32 = softmax_f32(sint, c32, g32, valid, kv_tile)
+            ptp = np.zeros((R, npad))
+            ptp[:, :N] = pt32
+            if mx:
+                # P~ in MX blocks of 32 consecutive keys; scaled back to 448 * value
+                # so the rest of the recursion is shared with the FP8 form
+                codes, e = mxfp4.quantize_blocks(ptp, axis=-1)
+                pq = P_SCALE * mxfp4.dequantize_blocks(codes, e)
             else:
-                pq = P_SCALE * pt
-            carry = np.exp(m_run - m_fin)                                # exp(m_t - m_T)
-            l = np.sum(pt.sum(axis=2) * carry, axis=1)
-            w = (pq * carry[:, :, None]).reshape(len(rr), npad)[:, :N]
+                pq = p_fp8(ptp)
+            carry = np.exp2(m32.astype(np.float64) - np.float64(1) * m32[:, -1:])   # 2^(m_t - m_T)
+            l = np.sum(ptp.reshape(R, nt, kv_tile).sum(axis=2) * carry, axis=1)
+            w = (pq.reshape(R, nt, kv_tile) * carry[:, :, None]).reshape(R, npad)[:, :N]
             out[b, h, r0:r0 + chunk] = (w @ vdq) / (P_SCALE * l)[:, None]
-            lse[b, h, r0:r0 + chunk] = m_fin[:, 0] + np.log(l)
+            lse[b, h, r0:r0 + chunk] = math.log(2.0) * (m32[:, -1].astype(np.float64) +
+                                                        np.log2(l))
     return (out, lse) if return_lse else out
 
 
@@ -422,14 +473,37 @@ def lse_correction(q, k_mean, *, sm_scale: float):
     return np.einsum("bhnc,bhc->bhn", q64, km_h) * sm_scale
 
 
+def f32_of_fraction(fr: Fraction) -> float:
+    """The binary32 value nearest (ties to even) to an exact rational, as a
+    Python float (normal and subnormal range; no overflow handling)."""
+    if fr == 0:
+        return 0.0
+    neg = fr < 0
+    a = -fr if neg else fr
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^(e-1) < a < 2^(e+1)
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)                                          # 2^e <= a (or subnormal)
+    quantum = Fraction(2) ** (e - 23)
+    n = a / quantum
+    k = n.numerator // n.denominator
+    rem = n - k
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and k % 2 == 1):
+        k += 1
+    v = float(k * quantum)
+    return -v if neg else v
+
+
 def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
                          b=0, h=0, hk=None, blkq=BLKQ, blkk=BLKK, return_lse=False,
                          delta_s=None, pv="fp8"):
     """Literal online recursion of Algorithm 1 in pure Python loops (tiny sizes).
 
     Used to pin ``attn_quant``'s closed form: the same steps, one key tile at
-    a time, with m, l and O updated in place (and, with ``return_lse``, the
-    final m + ln l of each row).
+    a time, with m, l and O rescaled in place by 2^(m_old - m_new) (and, with
+    ``return_lse``, the final ln 2 (m + log2 l) of each row).  The float32
+    steps are computed here on exact rationals, each rounded once by
+    ``f32_of_fraction`` (an implementation independent of ``rn32_sum``).
     """
     n, d = qc.shape[2], qc.shape[3]
     hk = h if hk is None else hk
@@ -440,38 +514,38 @@ def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
         vdq = fp8_e4m3.decode(vc[b, hk]) * vs[b, hk].astype(np.float64)[None, :]
     out = np.zeros((n, d))
     lse = np.zeros(n)
-    sml32 = sm_log2_f32(sm_scale)
+    lam = Fraction(float(sm_log2_f32(sm_scale)))
     for i in range(n):
-        m, l = -math.inf, 0.0
-        m32 = np.float32(-np.inf)           # the float32 running max of the P~ decisions
-        cq32 = np.float32(np.float32(qs[b, h, i // blkq]) * sml32)
+        m = None                            # float32 running max (a Python float)
+        l = 0.0
         o = [0.0] * d
+        dq = Fraction(float(qs[b, h, i // blkq]))
         for t0 in range(0, n, kv_tile):
-            keys = range(t0, min(t0 + kv_tile, n))
-            srow = {}
-            xs = {}                         # float64 S * ck and float32 x of each key
-            for j in keys:
-                if causal and j > i:
-                    continue
-                acc = sum(int(qc[b, h, i, c]) * int(kc[b, hk, j, c]) for c in range(d))
-                srow[j] = acc * float(qs[b, h, i // blkq]) * float(ks[b, hk, j // blkk]) * sm_scale
-                ck32 = np.float32(cq32 * np.float32(ks[b, hk, j // blkk]))
-                x = acc * float(ck32)
-                if delta_s is not None:
-                    srow[j] += float(delta_s[b, h, i // BLKQ, j]) * sm_scale
-                    dsl = np.float32(float(delta_s[b, h, i // BLKQ, j]) * float(sml32))
-                    xs[j] = (x, np.float32(x + float(dsl)))
-                else:
-                    xs[j] = (x, np.float32(x))
-            if not srow:
+            keys = [j for j in range(t0, min(t0 + kv_tile, n)) if not (causal and j > i)]
+            if not keys:
                 continue
-            m32 = max(m32, max(x32 for _, x32 in xs.values()))
-            mq32 = np.float32(m32 - LOG2_P_SCALE_F32)
-            m_new = max(m, max(srow.values()))
-            alpha = math.exp(m - m_new) if m != -math.inf else 0.0
-            l = alpha * l
-            o = [alpha * x for x in o]
-            pts = {j: math.exp(sv - m_new) for j, sv in srow.items()}
+            acc, x = {}, {}
+            for j in keys:
+                acc[j] = sum(int(qc[b, h, i, c]) * int(kc[b, hk, j, c]) for c in range(d))
+                dk = Fraction(float(ks[b, hk, j // blkk]))
+                cj = Fraction(f32_of_fraction(Fraction(f32_of_fraction(dq * dk)) * lam))
+                prod = acc[j] * cj
+                if delta_s is not None:
+                    g = f32_of_fraction(Fraction(float(delta_s[b, h, i // BLKQ, j])) * lam)
+                    x[j] = (prod, f32_of_fraction(prod + Fraction(g)))
+                else:
+                    x[j] = (prod, f32_of_fraction(prod))
+            m_new = max(x32 for _, x32 in x.values())
+            if m is not None:
+                m_new = max(m, m_new)
+                alpha = 2.0 ** (m - m_new)
+                l *= alpha
+                o = [alpha * v for v in o]
+            m = m_new
+            pts = {}
+            for j in keys:
+                a = f32_of_fraction(Fraction(x[j][1]) - Fraction(m))
+                pts[j] = float(np.float32(2.0 ** a))
             for j, pt in pts.items():
                 l += pt
                 if mx:
@@ -481,17 +555,12 @@ def attn_quant_recursive(qc, qs, kc, ks, vc, vs, *, causal, sm_scale, kv_tile,
                     sc = 2.0 ** int(mxfp4.scale_exponent(amax))
                     pq = P_SCALE * float(mxfp4.decode(mxfp4.encode(pt / sc))) * sc
                 else:
-                    # the E4M3 code decided in float32 (see _p448_decided_f32)
-                    x, x32 = xs[j]
-                    a32 = np.float32(x32 - mq32) if delta_s is not None else np.float32(
-                        x - float(mq32))
-                    e32 = np.float32(np.exp2(np.float64(a32)))
-                    pq = float(fp8_e4m3.round_to_e4m3(float(e32)))
+                    y = f32_of_fraction(Fraction(pt) * int(P_SCALE))
+                    pq = float(fp8_e4m3.round_to_e4m3(y))
                 for c in range(d):
                     o[c] += pq * vdq[j, c]
-            m = m_new
-        out[i] = [x / (P_SCALE * l) for x in o]
-        lse[i] = m + math.log(l)
+        out[i] = [v / (P_SCALE * l) for v in o]
+        lse[i] = math.log(2.0) * (m + math.log2(l))
     return (out, lse) if return_lse else out
 
 

@@ -38,8 +38,11 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
     const uint8_t* __restrict__ v_f8, const float* __restrict__ v_scale,
     const uint8_t* __restrict__ v_e8, const float* __restrict__ delta_s,
     void* __restrict__ out, float* __restrict__ lse,
-    const float* __restrict__ lse_corr, int H, int H_kv, int N, float sm_log2, int qg_shift,
+    const float* __restrict__ lse_corr, int H, int H_kv, int N, float lam, int qg_shift,
     int nqt, int total) {
+  // Every float32 step of the softmax below is the one the oracle takes (each
+  // named quantity rounded once); no multiply may be fused into a following add.
+#pragma clang fp contract(off)
   constexpr int NKC = D / 32;                 // 32-wide channel chunks
   constexpr int KBYTES = kKvTile * D;         // K tile bytes
   constexpr int VBYTES = PV4 ? KBYTES / 2 : KBYTES;   // V tile bytes (FP8 or FP4 codes)
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   // this lane's Q scale: groups of 2^qg_shift consecutive queries (128, 32
   // or 1; rows past N read the last row's group)
   const int nqs = ((N - 1) >> qg_shift) + 1;
-  const float cq = q_scale[(size_t)(b * H + h) * nqs + (min(qi, N - 1) >> qg_shift)] * sm_log2;
+  const float dq = q_scale[(size_t)(b * H + h) * nqs + (min(qi, N - 1) >> qg_shift)];
 
   f32x16 acc_o[NKC];
 #pragma unroll
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[c][r] = 0.f;
   float m_run = -INFINITY;   // running max of the log2-domain scores
-  float l_part = 0.f;        // this lane's share of sum 448*P~ (MXFP4: of sum P~)
+  float l_part = 0.f;        // this lane's share of l = sum P~
 
   // this lane's byte offset inside a 32-key K fragment block (full tiles)
   const uint32_t koff = (uint32_t)((lane % 32) * D + 16 * (lane / 32));
@@ -164,26 +167,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
 
   // One 128-key step of the online softmax.  MASK: the tile holds keys past
   // the diagonal (causal) or past N; only the last tile can.
-  // The exponent argument takes one FMA on the biased float of the int32
-  // sum when every dequant factor ck = cq * k_scale of the tiles this
-  // wave visits is <= kFastCk; otherwise kMagic is subtracted first.
-  // Decided once per wave, so each path is a loop of its own (both paths
-  // pass the same barriers).  Rows that see at most 2 tiles of keys (causal
-  // q tiles 0 and 1, or N <= 256) always take the exact form: with few keys
-  // one P~ code that lands on the other side of an FP8 rounding midpoint
-  // moves the row's output by up to |v| / 12, and the one-FMA form's 2^-11
-  // argument error makes that about 100x likelier than fp32 rounding does.
-  float kmax = 0.f;
-  for (int i = lane; i < min(nkb, ntiles * (kKvTile / kBlkK)); i += 64) kmax = fmaxf(kmax, ksc[i]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, o));
-  float cmax = cq;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, o));
-  const bool few_keys = CAUSAL ? qt < 2 : N <= 2 * kKvTile;
-  const bool fast_wg = cmax * kmax <= kFastCk && !few_keys;
-
-  auto step = [&](int t, auto mask_tag, auto fast_tag) {
+  auto step = [&](int t, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // Tile t has landed in buffer t&1 for every wave; buffer (t+1)&1 was
     // last read in iteration t-1, which every wave has finished.
@@ -218,22 +202,25 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
     }
     prio_valu();
 
-    // Per 32-key block: combined dequant factor (log2 domain).
+    // Per 32-key block: the score factor c = (dQ * dK) * lam, each product
+    // rounded once (the dequantization's scale product, then the softmax
+    // constant sm_scale * log2 e).
     float ck[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int kidx = (t * kKvTile + kb * 32) / kBlkK;
       // in a tail tile a 32-key block may lie wholly past N: clamp the read
       // (its scores are masked anyway)
-      ck[kb] = cq * ksc[MASK ? min(kidx, nkb - 1) : kidx];
+      const float dqk = dq * ksc[MASK ? min(kidx, nkb - 1) : kidx];
+      ck[kb] = dqk * lam;
     }
 
     float xm = -INFINITY;
     float xk[4];   // MXFP4: each 32-key block's max over the whole row block
     if constexpr (SQ) {
-      // ---- with Delta S: s becomes the float score t = (f - kMagic) * ck +
-      // Delta S[key] in log2 units (masked: -inf), and the row max is taken
-      // on those floats.
+      // ---- with Delta S: s becomes the float score x = (f - kMagic) * ck +
+      // Delta S[key] in log2 units, one rounding (masked: -inf), and the row
+      // max is taken on those floats.
       const float* dt = reinterpret_cast<const float*>(lds[t & 1] + DSOFF);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -279,6 +266,8 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         const int m2 = max(max(v[6], v[7]), v[8]), m3 = max(max(v[9], v[10]), v[11]);
         const int m4 = max(max(v[12], v[13]), v[14]);
         const int fm = max(max(max(m0, m1), m2), max(max(m3, m4), v[15]));
+        // the block's largest score x = S * c: rounding is monotonic, so
+        // the max of the rounded products is the product of the max
         const float x = (as_float(fm) - kMagic) * ck[kb];
         if constexpr (PV4) {
           xk[kb] = MASK ? (fm != INT_MIN ? x : -INFINITY) : x;
@@ -306,14 +295,10 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         for (int r = 0; r < 16; ++r) acc_o[c][r] *= alpha;
     }
 
-    // ---- P~ * 448 = exp2(score - m + log2 448), summed unquantized, cast to FP8.
-    // The score is (f - kMagic) * ck with f the biased float of the int32
-    // sum.  When ck is small, f*ck - (kMagic*ck + m') in one FMA is exact up
-    // to ulp(kMagic*ck)/2 <= 2^-11 (log2 units); otherwise subtract kMagic
-    // first (exact) and then apply ck.  The form is fixed per wave.  With
-    // Delta S the score is already a float: exp2(t - m').  Masked scores
-    // give exp2(-inf) = 0 there.
-    const float mq = m_new - kLog2_448;
+    // ---- P~ = 2^(x - m) with x = S * c (S the exact int32 sum, read from the
+    // float f = kMagic + S), each step rounded once; l sums P~ unquantized;
+    // (P~ * 448) is rounded to float32, then to FP8 E4M3 (nearest even,
+    // saturating).  With Delta S, x is already in s.  Masked keys give 0.
     i32x8 pf[2];
     // The first two V fragments are read before the exponentials, the rest
     // two MFMAs ahead, so no FP8 MFMA waits on LDS.
@@ -326,18 +311,14 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
     i32x8 va = vfrag(0), vb = vfrag(1);
     __builtin_amdgcn_sched_barrier(0);
     // P~ of elements r0 .. r0+NE-1 of 32-key block kb into its FP8 slots.
-    auto exp_part = [&](int kb, int r0, auto ne_tag, auto fast_tag) __attribute__((always_inline)) {
+    auto exp_part = [&](int kb, int r0, auto ne_tag) __attribute__((always_inline)) {
       constexpr int NE = decltype(ne_tag)::value;
-      const float off = fmaf(kMagic, ck[kb], mq);
       float e[NE];
 #pragma unroll
       for (int j = 0; j < NE; ++j) {
         const int r = r0 + j;
-        const float a = SQ ? as_float(s[kb][r]) - mq
-                        : decltype(fast_tag)::value
-                            ? fmaf(as_float(s[kb][r]), ck[kb], -off)
-                            : fmaf(as_float(s[kb][r]) - kMagic, ck[kb], -mq);
-        e[j] = __builtin_amdgcn_exp2f(a);
+        const float x = SQ ? as_float(s[kb][r]) : (as_float(s[kb][r]) - kMagic) * ck[kb];
+        e[j] = __builtin_amdgcn_exp2f(x - m_new);
         if constexpr (MASK && !SQ) e[j] = (s[kb][r] == INT_MIN) ? 0.f : e[j];
       }
       // this part's share of l as a tree (not a chain)
@@ -351,10 +332,13 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
       l_part += t[0];
 #pragma unroll
       for (int w = 0; w < NE / 4; ++w) {
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = e[4 * w + j] * 448.0f;
         // the high half is written by the second convert: any old value
-        // does, and e's own register avoids zeroing one first
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], as_int(e[4 * w]), false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], pk, true);
+        // does, and y's own register avoids zeroing one first
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], as_int(y[0]), false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], pk, true);
         pf[kb / 2][(kb % 2) * 4 + r0 / 4 + w] = pk;
       }
     };
@@ -363,12 +347,12 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
     // of keys 64..127 (a wave's MFMAs overlap well with its own VALU work),
     // then those of keys 64..127.  With d = 128 the matrix-core precedence
     // starts with the first of them.
-    auto exp_pv = [&](auto fast_tag) __attribute__((always_inline)) {
+    auto exp_pv = [&]() __attribute__((always_inline)) {
       using E16 = std::integral_constant<int, 16>;
       using EC = std::integral_constant<int, 32 / NKC>;
       {
-        exp_part(0, 0, E16{}, fast_tag);
-        exp_part(1, 0, E16{}, fast_tag);
+        exp_part(0, 0, E16{});
+        exp_part(1, 0, E16{});
         __builtin_amdgcn_sched_barrier(0);
         prio_mfma();
 
@@ -378,7 +362,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
           acc_o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[0], acc_o[c], 0, 0, 0,
                                                                        127, 0, 127);
           const int e0 = c * (32 / NKC);               // element over blocks 2, 3
-          exp_part(2 + e0 / 16, e0 % 16, EC{}, fast_tag);
+          exp_part(2 + e0 / 16, e0 % 16, EC{});
           __builtin_amdgcn_sched_barrier(0);
           va = vb;
           vb = vn;
@@ -395,24 +379,24 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
       }
     };
     if constexpr (PV4) {
-      // ---- MXFP4: block kb's shared exponent e = floor(log2 max P~) - 2 =
-      // floor(xk - m) - 2 (>= -127); exp2(s - m - e) = P~ / 2^e lands in
-      // [0, 8) and is cast to E2M1 (nearest, ties even, saturated to 6); l
-      // sums P~ itself.
+      // ---- MXFP4: P~ = 2^(x - m) as above; block kb's shared exponent is
+      // e = floor(log2 max P~) - 2 (clamped to [-127, 127], -127 for an
+      // all-zero block), taken from the float32 P~ of the block's largest
+      // score (the same value that element's own exponential gives); the
+      // codes are E2M1(P~ / 2^e) (nearest, ties even, saturated to 6) by the
+      // scaled convert; l sums P~ itself.
       int ex[4];
       uint32_t pk4[4][2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        ex[kb] = (int)fmaxf(floorf(xk[kb] - m_new), -125.0f) - 2;
-        const float mqk = m_new + (float)ex[kb];
-        const float off = fmaf(kMagic, ck[kb], mqk);
+        const float pm = __builtin_amdgcn_exp2f(xk[kb] - m_new);
+        ex[kb] = pm > 0.f ? min(max(__builtin_amdgcn_frexp_expf(pm) - 3, -127), 127) : -127;
+        const float sc = as_float((ex[kb] + 127) << 23);   // E8M0 code in the exponent field
         float e[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float a = decltype(fast_tag)::value
-                              ? fmaf(as_float(s[kb][r]), ck[kb], -off)
-                              : fmaf(as_float(s[kb][r]) - kMagic, ck[kb], -mqk);
-          e[r] = __builtin_amdgcn_exp2f(a);
+          const float x = (as_float(s[kb][r]) - kMagic) * ck[kb];
+          e[r] = __builtin_amdgcn_exp2f(x - m_new);
           if constexpr (MASK) e[r] = (s[kb][r] == INT_MIN) ? 0.f : e[r];
         }
         float u[8];
@@ -422,14 +406,14 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         for (int w = 4; w >= 1; w /= 2)
 #pragma unroll
           for (int j = 0; j < w; ++j) u[j] = u[2 * j] + u[2 * j + 1];
-        l_part += ldexpf(u[0], ex[kb]);
+        l_part += u[0];
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
           uint32_t pk = 0u;
           static_for<4>([&](auto ji) {
             constexpr int j = decltype(ji)::value;
             pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, e[8 * w + 2 * j],
-                                                          e[8 * w + 2 * j + 1], 1.0f, j);
+                                                          e[8 * w + 2 * j + 1], sc, j);
           });
           pk4[kb][w] = pk;
         }
@@ -456,33 +440,28 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         });
       }
     } else {
-    exp_pv(fast_tag);
+      exp_pv();
     }
   };
 
   const bool last_masked = CAUSAL || (N % kKvTile) != 0;
   const int nfull = last_masked ? ntiles - 1 : ntiles;
-  auto run = [&](auto fast_tag) __attribute__((always_inline)) {
-    for (int t = 0; t < nfull; ++t) step(t, std::false_type{}, fast_tag);
-    if (last_masked) step(ntiles - 1, std::true_type{}, fast_tag);
-  };
-  if constexpr (SQ) run(std::false_type{});   // one exact form with Delta S
-  else if (fast_wg) run(std::true_type{});
-  else run(std::false_type{});
+  for (int t = 0; t < nfull; ++t) step(t, std::false_type{});
+  if (last_masked) step(ntiles - 1, std::true_type{});
 
-  // ---- O = O / l * dV (l already carries the factor 448; MXFP4: no 448,
-  // and V's scales were applied by the matrix cores).
+  // ---- O = O / (448 l) * dV (MXFP4: O / l, V's scales were applied by the
+  // matrix cores).
 #pragma unroll
   for (int c = 0; c < NKC; ++c) pin(acc_o[c]);
   const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const float inv = 1.0f / l_tot;
-  // Row log-sum-exp (natural log) of the scores S the softmax used: the
-  // running max m (log2 units of S) and l = sum 448 * 2^(S log2 e - m) give
-  // ln sum exp(S) = ln 2 * (m + log2(l) - log2 448); plus the caller's
-  // correction for smoothed K (sm_scale * q . mean K) when given.
+  const float inv = 1.0f / (PV4 ? l_tot : l_tot * 448.0f);
+  // Row log-sum-exp (natural log) of the scores the softmax used: the
+  // running max m (log2 units) and l = sum 2^(x - m) give
+  // ln sum exp(S) = ln 2 * (m + log2(l)); plus the caller's correction for
+  // smoothed K (sm_scale * q . mean K) when given.
   if (lse != nullptr && half == 0 && qi < N) {
     const size_t row = (size_t)(b * H + h) * N + qi;
-    float v = 0.69314718055994531f * (m_run + log2f(l_tot) - (PV4 ? 0.f : kLog2_448));
+    float v = 0.69314718055994531f * (m_run + log2f(l_tot));
     if (lse_corr != nullptr) v += lse_corr[row];
     lse[row] = v;
   }
@@ -530,7 +509,12 @@ __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
   const int8_t* qh = q_i8 + qoff;
   const int8_t* kh = k_i8 + koff;
 
-  load_k_tile<D>(kh, t * kKvTile, N, lds, wave, lane);
+  // full tiles take the attention kernel's full-tile loader (wave-uniform
+  // base plus a fixed per-lane offset); the ragged last tile the clamping one
+  if ((t + 1) * kKvTile <= N)
+    load_k_tile_full<D>(kh, t * kKvTile, (uint32_t)((lane % 32) * D + 16 * (lane / 32)), lds, wave);
+  else
+    load_k_tile<D>(kh, t * kKvTile, N, lds, wave, lane);
   wait_vmem();
   __syncthreads();
   i32x4 qf[NKC];
@@ -570,7 +554,7 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
   const int nqt = (N + kBlockQ - 1) / kBlockQ;
   const long long total = (long long)B * H * nqt;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  const float sm_log2 = sm_scale * kLog2e;
+  const float lam = sm_scale * kLog2e;   // the softmax constant in log2 units
   dim3 grid((unsigned)total), block(kWaves * 64);
   const bool sq = delta_s != nullptr, pv4 = v_e8 != nullptr;
   if (sq && pv4) return hipErrorInvalidValue;
@@ -578,7 +562,7 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
   if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB && sq == SS && pv4 == PP) {          \
     hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB, SS, PP>), grid, block, 0, stream, q_i8,       \
                        q_scale, k_i8, k_scale, v_f8, v_scale, v_e8, delta_s, o, lse, lse_corr, H, \
-                       H_kv, N, sm_log2, qg_shift, nqt, (int)total);                              \
+                       H_kv, N, lam, qg_shift, nqt, (int)total);                              \
     return hipGetLastError();                                                                     \
   }
 #define SAGE_ATTN_CASES(SS, PP)              \

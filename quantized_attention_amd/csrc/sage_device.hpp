@@ -36,12 +36,7 @@ static_assert(kBlkQ == 1 << 7 && kWaveQ == 1 << 5, "Q scale groups are shifts of
 // the MFMA's int32 sum directly readable as a float offset by kMagic.
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;
-constexpr float kLog2_448 = 8.8073549220576041f;   // log2(448)
 constexpr float kLog2e = 1.4426950408889634f;
-// Largest per-element score scale (log2 units per unit of the int32 sum) for
-// which the one-FMA exponent argument is used; its error is at most
-// ulp(kMagic * kFastCk) / 2 = 2^-11.
-constexpr float kFastCk = 1.0f / 1024.0f;
 
 // Bit casts through a by-value parameter.  (Applying __builtin_bit_cast
 // directly to an ext_vector element, e.g. bit_cast<float>(v[r]), makes this

@@ -731,11 +731,11 @@ def test_lse_correction_restores_unsmoothed_lse(causal):
 
 
 @pytest.mark.parametrize("with_ds,causal", [(False, False), (False, True), (True, True)])
-def test_p_codes_decided_in_float32_differ_only_at_midpoints(with_ds, causal):
-    """The E4M3 code of 448 * P~ is taken on float32 values (Algorithm 1's on-chip
-    softmax).  Against the same step in float64 (scores S sQ sK sm log2 e, the running
-    max per 128-key tile, 448 * 2^(x - m)), a code may differ only where the float64 value
-    lies within a few float32 ulps of an E4M3 rounding midpoint, and only rarely.  A wrong
+def test_p_codes_f32_differ_from_float64_only_at_midpoints(with_ds, causal):
+    """The E4M3 code of 448 * P~ is taken on float32 values (reading c25).  Against the
+    same steps in float64 (scores S dQ dK sm log2 e (+ Delta S), the running max per
+    128-key tile, 448 * 2^(x - m)), a code may differ only where the float64 value lies
+    within a few float32 ulps of an E4M3 rounding midpoint, and only rarely.  A wrong
     factor, max, tile or Delta S term would move codes far from any midpoint."""
     g = np.random.default_rng(31)
     n, d = 300, 64
@@ -746,16 +746,16 @@ def test_p_codes_decided_in_float32_differ_only_at_midpoints(with_ds, causal):
     ds = O.delta_s(qz["q_mean"], k, qz["k_mean"]) if with_ds else None
     rows = np.arange(n)
     sint = qz["q_i8"][0, 0].astype(np.float64) @ qz["k_i8"][0, 0].astype(np.float64).T
-    qs = qz["q_scale"][0, 0][rows // O.BLKQ]
-    ks = qz["k_scale"][0, 0][np.arange(n) // O.BLKK]
+    qs = qz["q_scale"][0, 0][rows // O.BLKQ].astype(np.float64)
+    ks = qz["k_scale"][0, 0][np.arange(n) // O.BLKK].astype(np.float64)
     valid = (np.arange(n)[None, :] <= rows[:, None]) if causal else np.ones((n, n), bool)
-    sml = O.sm_log2_f32(sm)
-    ck32 = ((qs.astype(np.float32) * sml).astype(np.float32)[:, None] *
-            ks.astype(np.float32)[None, :]).astype(np.float32)
-    dsl32 = (ds[0, 0][rows // O.BLKQ] * np.float64(sml)).astype(np.float32) if with_ds else None
-    got = O._p448_decided_f32(sint, ck32, dsl32, valid, O.KV_TILE)
+    lam = O.sm_log2_f32(sm)
+    c32 = O.rn32(O.rn32(qs[:, None] * ks[None, :]).astype(np.float64) * np.float64(lam))
+    g32 = O.rn32(ds[0, 0][rows // O.BLKQ] * np.float64(lam)) if with_ds else None
+    pt32, m32 = O.softmax_f32(sint, c32, g32, valid, O.KV_TILE)
+    got = O.p_fp8(pt32)
     # float64: the same scores and running max without any float32 rounding
-    x = sint * qs.astype(np.float64)[:, None] * ks.astype(np.float64)[None, :] * sm / math.log(2)
+    x = sint * qs[:, None] * ks[None, :] * sm / math.log(2)
     if with_ds:
         x = x + ds[0, 0][rows // O.BLKQ] * sm / math.log(2)
     x = np.where(valid, x, -np.inf)
@@ -772,6 +772,124 @@ def test_p_codes_decided_in_float32_differ_only_at_midpoints(with_ds, causal):
         # both codes are neighbours, and p64 sits next to the midpoint between them
         assert abs(got[i, j] - want[i, j]) <= 0.13 * max(got[i, j], want[i, j])
         assert abs(p64[i, j] - mid) <= 2.0 ** -19 * (1 + abs(x[i, j])) * p64[i, j], (i, j)
+    # the row max element has P~ = 1 exactly (x - m = 0), so its code is 448
+    for i in range(n):
+        jm = np.argmax(np.where(valid[i], x[i], -np.inf))
+        if m[i, jm // O.KV_TILE] == m[i, -1]:
+            assert pt32[i, jm] == 1.0 and got[i, jm] == 448.0
     # the decisions are not trivially equal to the float64 ones by construction:
     # the float32 x carries rounding (else this test would not exercise anything)
-    assert np.any(ck32.astype(np.float64) != qs[:, None] * ks[None, :] * sm / math.log(2))
+    assert np.any(c32.astype(np.float64) != qs[:, None] * ks[None, :] * sm / math.log(2))
+
+
+def _exact_f32(fr):
+    """Brute-force nearest float32 of a rational: scan the float32 neighbours of its
+    float64 approximation and keep the closest (ties to the even significand)."""
+    from fractions import Fraction
+    c = np.float32(float(fr))
+    best = None
+    for k in range(-3, 4):
+        v = c
+        for _ in range(abs(k)):
+            v = np.nextafter(v, np.float32(np.inf) if k > 0 else np.float32(-np.inf))
+        dist = abs(Fraction(float(v)) - fr)
+        even = (int(np.array(v).view(np.int32)) & 1) == 0
+        key = (dist, not even)
+        if best is None or key < best[0]:
+            best = (key, v)
+    return float(best[1])
+
+
+def test_float32_rounding_helpers_are_exact():
+    """rn32_sum (float64 sum + TwoSum residual) and f32_of_fraction (rational
+    arithmetic) both give the nearest float32 of an exact sum; checked against a
+    brute-force search over float32 neighbours, on random sums and on sums built to land
+    exactly on a float32 midpoint in float64 while the exact value is just off it."""
+    from fractions import Fraction
+    g = np.random.default_rng(77)
+    # the oracle's use: (integer dot * float32 factor) + float32 term
+    a = g.integers(-2 ** 21, 2 ** 21, 400).astype(np.float64) * \
+        g.standard_normal(400).astype(np.float32).astype(np.float64)
+    b = (g.standard_normal(400) * np.exp(g.uniform(-8, 8, 400))).astype(np.float32).astype(np.float64)
+    # ties: a float32 midpoint m, split as m = a + b with a tiny residual beyond float64
+    mids, lows = [], []
+    for _ in range(200):
+        # a float32 midpoint just above 1 (mid = 1 + (2k + 1) 2^-24), split as
+        # b = 2^e and a = mid - b + tiny with tiny below float64's resolution of the
+        # sum: the float64 sum is exactly mid, the exact sum is just off it
+        e = int(g.integers(0, 3))
+        kk = int(g.integers(0, 2 ** 12))
+        mid = (1.0 + (2 * kk + 1) * 2.0 ** -24) * 2.0 ** e
+        tiny = 2.0 ** (e - 62) * g.choice([-1.0, 1.0])
+        a_part = mid - 2.0 ** e + tiny
+        assert a_part - tiny == mid - 2.0 ** e and a_part + 2.0 ** e == mid
+        mids.append(a_part)
+        lows.append(2.0 ** e)
+    a = np.concatenate([a, np.array(mids)])
+    b = np.concatenate([b, np.array(lows)])
+    got = O.rn32_sum(a, b)
+    for x, y, r in zip(a, b, got):
+        want = _exact_f32(Fraction(x) + Fraction(y))
+        assert float(r) == want, (x, y, r, want)
+        assert O.f32_of_fraction(Fraction(x) + Fraction(y)) == want
+    # on float64 values the rational rounding agrees with numpy's float64 -> float32 cast
+    x = g.standard_normal(2000) * np.exp(g.uniform(-95, 80, 2000))    # subnormal .. 1e35
+    assert all(O.f32_of_fraction(Fraction(v)) == float(np.float32(v)) for v in x)
+
+
+# --------------------------------------------------------------------- per-channel FP8 V
+
+def _read_hex_sections(path):
+    out, sec = {}, None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("# section:"):
+            sec = line.split(":", 1)[1].strip()
+            out[sec] = []
+        elif line and not line.startswith("#"):
+            out[sec].append([int(t, 0) if t.startswith("0x") else float(t) for t in line.split()])
+    return out
+
+
+def test_quantize_v_worked_example():
+    s = _read_hex_sections(os.path.join(GOLD, "v_fp8_channel_example.txt"))
+    v = torch.tensor(s["input"], dtype=torch.float16)[None, None]         # [1, 1, 4, 3]
+    assert torch.equal(v.float()[0, 0], torch.tensor(s["input"]))       # exact in fp16
+    z = O.quantize_v(v)
+    assert np.array_equal(z["v_scale"][0, 0], np.array(s["scale"][0], dtype=np.float32))
+    assert np.array_equal(z["v_f8"][0, 0], np.array(s["codes"], dtype=np.uint8))
+
+
+def test_quantize_v_scale_is_per_channel():
+    """The scale runs over the tokens of one channel: each nonzero channel's largest
+    |v| maps to the code of +-448, changing one token of channel c moves only channel c's
+    scale and codes, and scaling a channel by a power of two scales only its scale."""
+    g = np.random.default_rng(81)
+    B, Hk, N, d = 2, 2, 130, 16
+    v = torch.from_numpy((g.standard_normal((B, Hk, N, d)) *
+                          np.exp(g.uniform(-3, 3, (B, Hk, 1, d)))).astype(np.float32)).half()
+    z = O.quantize_v(v)
+    assert z["v_scale"].shape == (B, Hk, d) and z["v_f8"].shape == (B, Hk, N, d)
+    vv = v.float().numpy()
+    amax_at = np.abs(vv).argmax(axis=2)                                   # [B, Hk, d]
+    top = np.take_along_axis(z["v_f8"], amax_at[:, :, None, :], axis=2)[:, :, 0, :]
+    assert np.all((top & 0x7F) == 0x7E)
+    # reconstruction within half an E4M3 step of each value (relative 1/16, or the
+    # subnormal quantum 2^-9 of the scaled value)
+    dq = F8.decode(z["v_f8"]) * z["v_scale"][:, :, None, :].astype(np.float64)
+    step = np.maximum(np.abs(vv) / 16, 2.0 ** -10 * z["v_scale"][:, :, None, :])
+    assert np.all(np.abs(dq - vv) <= step * (1 + 1e-6))
+    # one token of channel 5 of head (1, 0) made the channel's largest
+    v2 = v.clone()
+    v2[1, 0, 77, 5] = float(np.abs(vv[1, 0, :, 5]).max() * 3)
+    z2 = O.quantize_v(v2)
+    diff_s = np.argwhere(z2["v_scale"] != z["v_scale"])
+    assert diff_s.tolist() == [[1, 0, 5]]
+    diff_c = np.argwhere(z2["v_f8"] != z["v_f8"])
+    assert set(map(tuple, diff_c[:, [0, 1, 3]])) == {(1, 0, 5)}
+    # a power-of-two rescale of one channel scales its scale exactly, codes unchanged
+    v3 = v.clone()
+    v3[:, :, :, 2] *= 4
+    z3 = O.quantize_v(v3)
+    assert np.array_equal(z3["v_f8"], z["v_f8"])
+    assert np.array_equal(z3["v_scale"][..., 2], z["v_scale"][..., 2] * 4)
