@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 5
+#define SAGE_ABI_VERSION 6
 
 /* Q tokens per INT8 scale (default), K tokens per INT8 scale. */
 #define SAGE_BLKQ 128
@@ -87,7 +87,8 @@ typedef enum {
   SAGE_ERR_ARG = 6,       /* sm_scale not finite or <= 0; bad flag or index    */
   SAGE_ERR_WORKSPACE = 7, /* workspace NULL or smaller than required           */
   SAGE_ERR_HIP = 8,       /* a HIP launch or runtime call failed               */
-  SAGE_ERR_ALIGN = 9      /* a pointer is not 16-byte aligned                  */
+  SAGE_ERR_ALIGN = 9,     /* a pointer is not 16-byte aligned                  */
+  SAGE_ERR_SCRATCH = 10   /* the shapes need more than the fixed scratch array */
 } sage_status;
 
 typedef enum { SAGE_FP16 = 0, SAGE_BF16 = 1 } sage_dtype;
@@ -286,6 +287,29 @@ sage_status sage_attn_fwd_mxfp4(const int8_t* q_i8, const float* q_scale, const 
  */
 sage_status sage_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int H_kv,
                           int N, int d, int b, int h, int32_t* s_out, void* stream);
+
+/*
+ * sage_quant_qk without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, outputs and results are those of
+ * sage_quant_qk (bit-identical); the column-statistics scratch is instead a
+ * fixed device array of SAGE_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends.
+ *   Limit: with smooth_k = 1 the shapes need sage_buffer_sizes().ws_quant_qk
+ *     <= SAGE_SCRATCH_BYTES (B * H_kv * ceil(N/256) * d * 8 bytes), else
+ *     SAGE_ERR_SCRATCH and nothing is launched.  smooth_k = 0 needs no scratch.
+ *   The first call on a device looks the array's address up (no allocation);
+ *     it runs on the device of `stream` (the current device for NULL).
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *     on one GPU (other streams, other threads) race.  Calls serialized on a
+ *     stream do not: each call writes every scratch byte it reads.
+ */
+#define SAGE_SCRATCH_BYTES (16u << 20)
+sage_status sage_quant_qk_noalloc(const void* q, const void* k, sage_dtype dtype,
+                                  int B, int H, int H_kv, int N, int d, int q_group,
+                                  int smooth_k, int smooth_q, int8_t* q_i8, float* q_scale,
+                                  int8_t* k_i8, float* k_scale, float* k_mean, float* q_mean,
+                                  void* stream);
 
 /* Static description of a status code. */
 const char* sage_status_str(sage_status s);

@@ -23,6 +23,8 @@ Entry points (same names as the C ABI):
     sage_attn_fwd_mxfp4(qk, vq4, causal=..., sm_scale=..., return_lse=False) -> o or (o, lse)
     sage_lse_correction(q, k_mean, sm_scale) -> fp32 [B, H, N]
     sage_qk_int32(q_i8, k_i8, b, h) -> int32 [N, N] (diagnostic)
+    sage_quant_qk_noalloc(q, k, smooth_k=True, q_group=128, smooth_q=False, out=...)
+        -> as sage_quant_qk, with the library's fixed scratch array (allocates nothing)
 and the composition ``sageattn(q, k, v, is_causal=False, sm_scale=None,
 smooth_k=True, return_lse=False, q_group=128, smooth_q=False)``.  ``q_group`` is the number of
 consecutive Q tokens per scale: 128 (per block), 32 (per wave, the per-warp
@@ -45,7 +47,8 @@ __all__ = ["SageError", "library_path", "load_library", "sage_buffer_sizes", "sa
            "sage_quant_v", "sage_quant_v_mxfp4", "sage_delta_s", "sage_attn_fwd",
            "sage_attn_fwd_lse", "sage_attn_fwd_mxfp4",
            "sage_lse_correction",
-           "sage_qk_int32", "sageattn", "SagePlan", "BLKQ", "BLKK", "KV_TILE", "Q_GROUPS"]
+           "sage_qk_int32", "sage_quant_qk_noalloc", "sageattn", "SagePlan", "BLKQ", "BLKK",
+           "KV_TILE", "Q_GROUPS", "SCRATCH_BYTES"]
 
 BLKQ, BLKK, KV_TILE = 128, 64, 128
 Q_GROUPS = (128, 32, 1)   # Q tokens per scale: per block, per wave, per query
@@ -99,9 +102,11 @@ def load_library():
     lib.sage_attn_fwd_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i,
                                         i, ctypes.c_float, vp]
     lib.sage_qk_int32.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp]
+    lib.sage_quant_qk_noalloc.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp,
+                                          vp, vp]
     for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_delta_s", "sage_quant_v", "sage_attn_fwd",
               "sage_attn_fwd_lse", "sage_lse_correction", "sage_qk_int32", "sage_quant_v_mxfp4",
-              "sage_attn_fwd_mxfp4"):
+              "sage_attn_fwd_mxfp4", "sage_quant_qk_noalloc"):
         getattr(lib, f).restype = i
     _lib = lib
     return lib
@@ -231,6 +236,38 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *,
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream, q.device))
     _check(st, "sage_quant_qk")
+    return out
+
+
+SCRATCH_BYTES = 16 << 20   # SAGE_SCRATCH_BYTES: the library's fixed scratch array
+
+
+def sage_quant_qk_noalloc(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *,
+                          q_group: int = BLKQ, smooth_q: bool = False, out, stream=None) -> dict:
+    """sage_quant_qk with the library's fixed scratch array instead of a workspace: the
+    entry point allocates nothing (``out`` must hold every output buffer).  Calls that
+    overlap on one GPU share that array and race (see sage.h)."""
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share a dtype")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (B, H_kv, N, d):
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if q_group not in Q_GROUPS:
+        raise ValueError(f"q_group must be one of {Q_GROUPS}")
+    if smooth_q and "q_mean" not in out:
+        raise ValueError("smooth_q needs out['q_mean']")
+    sizes = sage_buffer_sizes(B, H, H_kv, N, d, q_group)
+    _check_sizes("sage_quant_qk_noalloc", sizes, q_i8=out["q_i8"], q_scale=out["q_scale"],
+                 k_i8=out["k_i8"], k_scale=out["k_scale"], k_mean=out["k_mean"],
+                 q_mean=out.get("q_mean") if smooth_q else None)
+    _need_gpu(q, k, *(t for n, t in out.items() if n != "q_mean" or smooth_q))
+    st = load_library().sage_quant_qk_noalloc(
+        q.data_ptr(), k.data_ptr(), _dt(q.dtype), B, H, H_kv, N, d, q_group, int(bool(smooth_k)),
+        int(bool(smooth_q)), out["q_i8"].data_ptr(), out["q_scale"].data_ptr(),
+        out["k_i8"].data_ptr(), out["k_scale"].data_ptr(), out["k_mean"].data_ptr(),
+        _ptr(out.get("q_mean")) if smooth_q else None, _stream(stream, q.device))
+    _check(st, "sage_quant_qk_noalloc")
     return out
 
 

@@ -79,6 +79,7 @@ const char* sage_status_str(sage_status s) {
     case SAGE_ERR_WORKSPACE: return "workspace missing or too small";
     case SAGE_ERR_HIP: return "HIP launch or runtime error";
     case SAGE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SAGE_ERR_SCRATCH: return "shapes need more than the library's fixed scratch array";
   }
   return "unknown status";
 }

@@ -27,15 +27,15 @@ def test_library_exports_every_declared_symbol():
     assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse",
             "sage_lse_correction", "sage_buffer_sizes", "sage_qk_int32", "sage_status_str",
             "sage_delta_s", "sage_quant_v_mxfp4", "sage_attn_fwd_mxfp4",
-            "sage_abi_version"} <= set(names)
+            "sage_abi_version", "sage_quant_qk_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sage_abi_version() == 5
+    assert lib.sage_abi_version() == 6
 
 
 def test_status_strings():
     lib = qa.load_library()
-    for s in range(10):
+    for s in range(11):
         assert lib.sage_status_str(s)
     assert lib.sage_status_str(0) == b"ok"
 
@@ -292,3 +292,25 @@ def test_binding_rejects_short_or_mismatched_buffers_before_any_launch():
     # well-formed buffers get as far as the device check
     with pytest.raises(ValueError, match="CUDA"):
         qa.sage_attn_fwd(qk, vq, causal=False, sm_scale=0.125)
+
+
+def _qk_noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, dt=0, B=1, H=2, H_kv=2, N=256, d=64, qg=128, smooth=1, sq=0,
+             q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, q_mean=None,
+             stream=None)
+    a.update(kw)
+    return lib.sage_quant_qk_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k_mean=None), 1), (dict(sq=1), 1), (dict(B=0), 2), (dict(d=32), 3),
+    (dict(H=3), 4), (dict(dt=2), 5), (dict(smooth=2), 6), (dict(qg=64), 6), (dict(sq=-1), 6),
+    (dict(q=FAKE + 8), 9),
+    # B * H_kv * ceil(N/256) * d * 8 bytes of K column sums above the 16 MiB array
+    (dict(B=1, H=64, H_kv=64, N=65536 + 256, d=128), 10),
+])
+def test_quant_qk_noalloc_rejects(kw, code):
+    """The no-allocation entry point validates like sage_quant_qk and refuses shapes whose
+    scratch exceeds its fixed array, before any HIP call."""
+    assert _qk_noalloc(qa.load_library(), **kw) == code
+    assert qa.sage_buffer_sizes(1, 64, 64, 65536, 128)["ws_quant_qk"] == qa.SCRATCH_BYTES
