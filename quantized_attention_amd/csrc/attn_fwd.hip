@@ -30,9 +30,8 @@ namespace sage {
 // PV4: P V on the FP4 matrix cores in MXFP4 (v_f8 holds E2M1 codes, v_e8 the
 // E8M0 scale bytes, see quant_v_mxfp4); P~ is quantized per 32 keys of a row.
 template <int D, bool CAUSAL, bool BF16, bool SQ, bool PV4>
-// d = 64 fits three workgroups per CU (168 registers); d = 128, and d = 64
-// with Delta S, two.
-__global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_kernel(
+// d = 64 fits three workgroups per CU (168 registers); d = 128 two.
+__global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_f8, const float* __restrict__ v_scale,
@@ -47,10 +46,11 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   constexpr int KBYTES = kKvTile * D;         // K tile bytes
   constexpr int VBYTES = PV4 ? KBYTES / 2 : KBYTES;   // V tile bytes (FP8 or FP4 codes)
   constexpr int VSBYTES = PV4 ? kMxScaleBytes : 0;    // a tile's MXFP4 V scale bytes
-  constexpr int DSOFF = KBYTES + VBYTES + VSBYTES;    // a tile's Delta S values
-  constexpr int DSBYTES = SQ ? kKvTile * 4 : 0;
+  constexpr int DSBYTES = SQ ? kKvTile * 4 : 0;      // a tile's Delta S values
   static_assert(!(SQ && PV4), "Delta S and MXFP4 P V are separate variants");
-  __shared__ __attribute__((aligned(16))) char lds[2][DSOFF + DSBYTES];
+  // K (with Delta S) and V tiles are double-buffered.
+  __shared__ __attribute__((aligned(16))) char lds_k[2][KBYTES + DSBYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v[2][VBYTES + VSBYTES];
 
   // ---- which (b, kv head, q tile, group member) this workgroup computes.
   // Non-causal (equal work per workgroup): each XCD takes a contiguous range
@@ -119,6 +119,9 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   const int ntk = (N + kKvTile - 1) / kKvTile;
   const uint8_t* vh = v_f8 + (size_t)(b * H_kv + hk) * ntk * VBYTES;
   const uint8_t* vsh = PV4 ? v_e8 + (size_t)(b * H_kv + hk) * ntk * VSBYTES : nullptr;
+  // buffer resources of this head's K, V (and MXFP4 scales), Delta S row
+  const rsrc_t rk = make_rsrc(kh, (uint32_t)N * D);
+  const rsrc_t rv = make_rsrc(vh, (uint32_t)ntk * VBYTES);
   const int nkb = (N + kBlkK - 1) / kBlkK;
   const float* ksc = k_scale + (size_t)(b * H_kv + hk) * nkb;
   const int ntiles = CAUSAL ? qt + 1 : ntk;
@@ -142,45 +145,50 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
   float m_run = -INFINITY;   // running max of the log2-domain scores
   float l_part = 0.f;        // this lane's share of l = sum P~
 
-  // this lane's byte offset inside a 32-key K fragment block (full tiles)
-  const uint32_t koff = (uint32_t)((lane % 32) * D + 16 * (lane / 32));
+  // this lane's byte offsets of its K blocks inside a tile
+  constexpr int KNB = (kKvTile / 32) * NKC / kWaves;
+  uint32_t koff[KNB];
+#pragma unroll
+  for (int i = 0; i < KNB; ++i) koff[i] = k_tile_offset<D>(i * kWaves + wave, lane);
   // Delta S row of this workgroup's Q block; waves 0 and 1 stage a tile's
-  // 128 values (one float per lane, keys past N read key N-1)
-  const float* dsr = SQ ? delta_s + ((size_t)(b * H + h) * nqt + qt) * N : nullptr;
-  auto load_ds_tile = [&](int t, char* dst) __attribute__((always_inline)) {
-    if (SQ && wave < 2) {
-      const int key = min(t * kKvTile + wave * 64 + lane, N - 1);
-      __builtin_amdgcn_global_load_lds(dsr + key, (lds_void*)(dst + wave * 256), 4, 0, 0);
-    }
+  // 128 values (one float per lane; keys past N read zeros)
+  const rsrc_t rds = make_rsrc(SQ ? delta_s + ((size_t)(b * H + h) * nqt + qt) * N : delta_s,
+                               SQ ? (uint32_t)N * 4 : 0u);
+  const rsrc_t rvs = make_rsrc(vsh, PV4 ? (uint32_t)ntk * VSBYTES : 0u);
+  // K and V codes (and, for MXFP4, the tile's 512 scale bytes; with Delta S
+  // the tile's 128 values: waves 0 and 1, one dword per lane) of tile t into
+  // a stage
+  auto load_k = [&](int t) __attribute__((always_inline)) {
+    char* stage = lds_k[t & 1];
+    load_k_tile<D>(rk, t * kKvTile, koff, stage, wave);
+    if (SQ && wave < 2)
+      buffer_to_lds<4>(rds, stage + KBYTES + wave * 256, (uint32_t)((wave * 64 + lane) * 4),
+                       (uint32_t)t * kKvTile * 4);
   };
-  // V codes (and, for MXFP4, the tile's 512 scale bytes: waves 0 and 1, one
-  // dword per lane) of tile t into a stage
-  auto load_v = [&](int t, char* stage) __attribute__((always_inline)) {
-    load_v_tile<VBYTES>(vh + (size_t)t * VBYTES, stage + KBYTES, wave, lane);
+  auto load_v = [&](int t) __attribute__((always_inline)) {
+    char* stage = lds_v[t & 1];
+    load_v_tile<VBYTES>(rv, t, stage, wave, lane);
     if (PV4 && wave < 2)
-      __builtin_amdgcn_global_load_lds(vsh + (size_t)t * VSBYTES + wave * 256 + lane * 4,
-                                       (lds_void*)(stage + KBYTES + VBYTES + wave * 256), 4, 0, 0);
+      buffer_to_lds<4>(rvs, stage + VBYTES + wave * 256, (uint32_t)(wave * 256 + lane * 4),
+                       (uint32_t)t * VSBYTES);
   };
-  load_k_tile<D>(kh, 0, N, lds[0], wave, lane);
-  load_v(0, lds[0]);
-  load_ds_tile(0, lds[0] + DSOFF);
+  load_k(0);
+  load_v(0);
 
   // One 128-key step of the online softmax.  MASK: the tile holds keys past
   // the diagonal (causal) or past N; only the last tile can.
   auto step = [&](int t, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    // Tile t has landed in buffer t&1 for every wave; buffer (t+1)&1 was
+    // Tile t has landed in buffers t&1 for every wave; buffers (t+1)&1 were
     // last read in iteration t-1, which every wave has finished.
     wait_vmem();
     __syncthreads();
     if (t + 1 < ntiles) {
-      if ((t + 2) * kKvTile <= N) load_k_tile_full<D>(kh, (t + 1) * kKvTile, koff, lds[(t + 1) & 1], wave);
-      else load_k_tile<D>(kh, (t + 1) * kKvTile, N, lds[(t + 1) & 1], wave, lane);
-      load_v(t + 1, lds[(t + 1) & 1]);
-      load_ds_tile(t + 1, lds[(t + 1) & 1] + DSOFF);
+      load_k(t + 1);
+      load_v(t + 1);
     }
-    const char* kt = lds[t & 1];
-    const char* vt = lds[t & 1] + KBYTES;
+    const char* kt = lds_k[t & 1];
+    const char* vt = lds_v[t & 1];
 
     // ---- S^T = K Q^T on the INT8 matrix cores (exact int32 sums).
     // K fragments are read one 32-key block ahead of the MFMAs that use
@@ -218,10 +226,10 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
     float xm = -INFINITY;
     float xk[4];   // MXFP4: each 32-key block's max over the whole row block
     if constexpr (SQ) {
-      // ---- with Delta S: s becomes the float score x = (f - kMagic) * ck +
-      // Delta S[key] in log2 units, one rounding (masked: -inf), and the row
-      // max is taken on those floats.
-      const float* dt = reinterpret_cast<const float*>(lds[t & 1] + DSOFF);
+      // ---- with Delta S: s becomes the float score x = S * ck + Delta S[key]
+      // in log2 units, one rounding (masked: -inf), and the row max is taken
+      // on those floats.
+      const float* dt = reinterpret_cast<const float*>(lds_k[t & 1] + KBYTES);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * j + i;
-            float x = fmaf(as_float(s[kb][r]) - kMagic, ck[kb], dv[i]);
+            float x = fmaf((float)s[kb][r], ck[kb], dv[i]);
             if constexpr (MASK) {
               const int key = t * kKvTile + kb * 32 + 8 * j + 4 * half + i;
               if ((CAUSAL && key > qi) || key >= N) x = -INFINITY;
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         const int fm = max(max(max(m0, m1), m2), max(max(m3, m4), v[15]));
         // the block's largest score x = S * c: rounding is monotonic, so
         // the max of the rounded products is the product of the max
-        const float x = (as_float(fm) - kMagic) * ck[kb];
+        const float x = (float)fm * ck[kb];
         if constexpr (PV4) {
           xk[kb] = MASK ? (fm != INT_MIN ? x : -INFINITY) : x;
         } else {
@@ -295,8 +303,8 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         for (int r = 0; r < 16; ++r) acc_o[c][r] *= alpha;
     }
 
-    // ---- P~ = 2^(x - m) with x = S * c (S the exact int32 sum, read from the
-    // float f = kMagic + S), each step rounded once; l sums P~ unquantized;
+    // ---- P~ = 2^(x - m) with x = S * c (S the exact int32 sum, converted to
+    // float exactly: |S| < 2^22), each step rounded once; l sums P~ unquantized;
     // (P~ * 448) is rounded to float32, then to FP8 E4M3 (nearest even,
     // saturating).  With Delta S, x is already in s.  Masked keys give 0.
     i32x8 pf[2];
@@ -317,7 +325,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
 #pragma unroll
       for (int j = 0; j < NE; ++j) {
         const int r = r0 + j;
-        const float x = SQ ? as_float(s[kb][r]) : (as_float(s[kb][r]) - kMagic) * ck[kb];
+        const float x = SQ ? as_float(s[kb][r]) : (float)s[kb][r] * ck[kb];
         e[j] = __builtin_amdgcn_exp2f(x - m_new);
         if constexpr (MASK && !SQ) e[j] = (s[kb][r] == INT_MIN) ? 0.f : e[j];
       }
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
         float e[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float x = (as_float(s[kb][r]) - kMagic) * ck[kb];
+          const float x = (float)s[kb][r] * ck[kb];
           e[r] = __builtin_amdgcn_exp2f(x - m_new);
           if constexpr (MASK) e[r] = (s[kb][r] == INT_MIN) ? 0.f : e[r];
         }
@@ -494,11 +502,12 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 && !SQ ? 3 : 2) void attn_fwd_
 }
 
 // Diagnostic: exact int32 S = Q^ K^T of one head, through the same K tile
-// loader, LDS fragment layout and qk_frags routine as attn_fwd_kernel.
+// loader (buffer loads, zeros past N), LDS fragment layout and qk_frags
+// routine as attn_fwd_kernel.
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
     const int8_t* __restrict__ q_i8, const int8_t* __restrict__ k_i8, int32_t* __restrict__ s_out,
-    int N, size_t qoff, size_t koff) {
+    int N, size_t qoff, size_t kvoff) {
   constexpr int NKC = D / 32;
   __shared__ __attribute__((aligned(16))) char lds[kKvTile * D];
   const int qt = blockIdx.x, t = blockIdx.y;
@@ -507,14 +516,13 @@ __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
   const int half = lane >> 5;
   const int qi = qt * kBlockQ + wave * kWaveQ + (lane & 31);
   const int8_t* qh = q_i8 + qoff;
-  const int8_t* kh = k_i8 + koff;
+  const int8_t* kh = k_i8 + kvoff;
 
-  // full tiles take the attention kernel's full-tile loader (wave-uniform
-  // base plus a fixed per-lane offset); the ragged last tile the clamping one
-  if ((t + 1) * kKvTile <= N)
-    load_k_tile_full<D>(kh, t * kKvTile, (uint32_t)((lane % 32) * D + 16 * (lane / 32)), lds, wave);
-  else
-    load_k_tile<D>(kh, t * kKvTile, N, lds, wave, lane);
+  constexpr int KNB = (kKvTile / 32) * NKC / kWaves;
+  uint32_t koff[KNB];
+#pragma unroll
+  for (int i = 0; i < KNB; ++i) koff[i] = k_tile_offset<D>(i * kWaves + wave, lane);
+  load_k_tile<D>(make_rsrc(kh, (uint32_t)N * D), t * kKvTile, koff, lds, wave);
   wait_vmem();
   __syncthreads();
   i32x4 qf[NKC];
@@ -532,7 +540,7 @@ __global__ __launch_bounds__(kWaves * 64) void qk_int32_kernel(
     for (int r = 0; r < 16; ++r) {
       const int key = t * kKvTile + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
       if (qi < N && key < N)
-        s_out[(size_t)qi * N + key] = s[r] - kMagicBits;
+        s_out[(size_t)qi * N + key] = s[r];
     }
   }
 }

@@ -31,11 +31,6 @@ constexpr int kBlockQ = kWaveQ * kWaves;   // queries per workgroup (== kBlkQ)
 static_assert(kBlockQ == kBlkQ, "a 128-token Q scale block is one workgroup's queries");
 static_assert(kBlkQ == 1 << 7 && kWaveQ == 1 << 5, "Q scale groups are shifts of the query index");
 
-// 1.5 * 2^23: for |n| < 2^22 the float with bits (0x4B400000 + n) equals
-// 12582912 + n exactly.  Seeding the INT8 accumulator with these bits makes
-// the MFMA's int32 sum directly readable as a float offset by kMagic.
-constexpr int kMagicBits = 0x4B400000;
-constexpr float kMagic = 12582912.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Bit casts through a by-value parameter.  (Applying __builtin_bit_cast
@@ -101,13 +96,13 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 // ---------------------------------------------------------------------------
 // INT8 S^T tile: 32 keys x 32 queries from the lane's K fragments `kf` (A
 // operand, one per 32-channel chunk) and Q fragments `qf` (B operand).
-// Returns the 16 C/D values as the bit patterns of the floats
-// kMagic + sum_c q*k (exact); as signed ints they order like the sums.
+// Returns the 16 C/D values, the exact int32 sums (the accumulator starts
+// from the inline constant 0: no register is seeded per tile).
 template <int NKC>
 __device__ __forceinline__ i32x16 qk_frags(const i32x4* kf, const i32x4* qf) {
   i32x16 acc;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = kMagicBits;
+  for (int r = 0; r < 16; ++r) acc[r] = 0;
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kc], qf[kc], acc, 0, 0, 0);
   return acc;
@@ -128,59 +123,58 @@ typedef __attribute__((address_space(3))) void lds_void;
 // left alone.  Must precede the barrier that publishes LDS-load data.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// K tile (kKvTile keys x D int8) -> LDS in fragment-major order with
-// direct global->LDS loads (16 bytes per lane; lane L of an instruction
-// lands at byte 16*L of the instruction's 1 KB LDS block).  Block
-// (kb32, kc) holds, for lane L, key kb32*32 + L%32 and channel bytes
-// kc*32 + 16*(L/32) .. +16: exactly the A-operand fragment of the INT8
-// MFMA.  Keys >= N read row N-1 (those scores are masked).
-template <int D>
-__device__ __forceinline__ void load_k_tile(const int8_t* kh, int key0, int N, char* lds_k,
-                                            int wave, int lane) {
-  constexpr int NKC = D / 32;
-  constexpr int NB = (kKvTile / 32) * NKC;
-  static_assert(NB % kWaves == 0, "whole blocks per wave");
-#pragma unroll
-  for (int i = 0; i < NB / kWaves; ++i) {
-    const int blk = i * kWaves + wave;
-    const int kb32 = blk / NKC, kc = blk % NKC;
-    const int key = min(key0 + kb32 * 32 + (lane % 32), N - 1);
-    const int8_t* g = kh + (size_t)key * D + kc * 32 + 16 * (lane / 32);
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_k + blk * 1024), 16, 0, 0);
-  }
+// Raw buffer resources (base, byte size; word 3 = the gfx9 raw-buffer format)
+// for the tile loads: each lane passes a 32-bit offset computed once, the
+// tile's offset is a scalar, and reads at or past the size return zero.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 (or 4) bytes per lane from the buffer into LDS: lane L of the
+// instruction lands at byte 16*L (4*L) of `lds`.
+template <int BYTES>
+__device__ __forceinline__ void buffer_to_lds(rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword loads");
+  if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
 }
 
-// The same K tile when every key is < N: each lane's address is a
-// wave-uniform base plus its fixed 32-bit offset `koff` = (L%32)*D + 16*(L/32)
-// (SGPR-base addressing, no per-load vector arithmetic).
+// K tile (kKvTile keys x D int8) -> LDS in fragment-major order, 16 bytes
+// per lane per 1 KB block.  Block (kb32, kc) holds, for lane L, key
+// kb32*32 + L%32 and channel bytes kc*32 + 16*(L/32) .. +16: exactly the
+// A-operand fragment of the INT8 MFMA.  Wave w loads blocks w, w + 4, ...;
+// `koff[i]` is the lane's byte offset of block i*4 + w relative to the
+// tile's first key (tile-invariant).  Keys >= N read zeros (their scores are
+// masked).
 template <int D>
-__device__ __forceinline__ void load_k_tile_full(const int8_t* kh, int key0, uint32_t koff,
-                                                 char* lds_k, int wave) {
+__device__ __forceinline__ uint32_t k_tile_offset(int blk, int lane) {
+  constexpr int NKC = D / 32;
+  const int kb32 = blk / NKC, kc = blk % NKC;
+  return (uint32_t)((kb32 * 32 + lane % 32) * D + kc * 32 + 16 * (lane / 32));
+}
+template <int D>
+__device__ __forceinline__ void load_k_tile(rsrc_t rk, int key0, const uint32_t* koff, char* lds_k,
+                                            int wave) {
   constexpr int NKC = D / 32;
   constexpr int NB = (kKvTile / 32) * NKC;
   static_assert(NB % kWaves == 0, "whole blocks per wave");
+  const uint32_t soff = (uint32_t)key0 * D;
 #pragma unroll
-  for (int i = 0; i < NB / kWaves; ++i) {
-    const int blk = i * kWaves + wave;
-    const int kb32 = blk / NKC, kc = blk % NKC;
-    const int8_t* base = kh + (size_t)(key0 + kb32 * 32) * D + kc * 32;
-    __builtin_amdgcn_global_load_lds(base + koff, (lds_void*)(lds_k + blk * 1024), 16, 0, 0);
-  }
+  for (int i = 0; i < NB / kWaves; ++i)
+    buffer_to_lds<16>(rk, lds_k + (i * kWaves + wave) * 1024, koff[i], soff);
 }
 
 // V tile (already fragment-ordered in HBM, BYTES bytes: kKvTile*D FP8 or
-// half that of FP4 codes) -> LDS, a straight copy with direct global->LDS
-// loads.
+// half that of FP4 codes) -> LDS, a straight copy in 1 KB blocks.
 template <int BYTES>
-__device__ __forceinline__ void load_v_tile(const uint8_t* vtile, char* lds_v, int wave, int lane) {
+__device__ __forceinline__ void load_v_tile(rsrc_t rv, int t, char* lds_v, int wave, int lane) {
   constexpr int NB = BYTES / 1024;
   static_assert(NB % kWaves == 0, "whole blocks per wave");
-  const uint32_t voff = (uint32_t)lane * 16;
+  const uint32_t soff = (uint32_t)t * BYTES;
 #pragma unroll
   for (int i = 0; i < NB / kWaves; ++i) {
     const int blk = i * kWaves + wave;
-    __builtin_amdgcn_global_load_lds(vtile + blk * 1024 + voff, (lds_void*)(lds_v + blk * 1024),
-                                     16, 0, 0);
+    buffer_to_lds<16>(rv, lds_v + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), soff);
   }
 }
 
