@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 6
+#define SAGE_ABI_VERSION 7
 
 /* Q tokens per INT8 scale (default), K tokens per INT8 scale. */
 #define SAGE_BLKQ 128
@@ -109,6 +109,7 @@ typedef struct {
   size_t delta_s;   /* float [B][H][ceil(N/128)][N]   (smooth Q only)           */
   size_t v_f4;      /* uint8 [B][H_kv][ceil(N/128)*64*d]  (MXFP4 V codes)       */
   size_t v_e8;      /* uint8 [B][H_kv][ceil(N/128)*512]   (MXFP4 V scales)      */
+  size_t ws_quant_qkv; /* workspace bytes sage_quant_qkv needs (qk + v)        */
 } sage_sizes;
 
 /*
@@ -158,6 +159,21 @@ sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype,
                           int smooth_q, int8_t* q_i8, float* q_scale, int8_t* k_i8,
                           float* k_scale, float* k_mean, float* q_mean, void* workspace,
                           size_t ws_bytes, void* stream);
+
+/*
+ * Steps 1-3 in one call: sage_quant_qk and sage_quant_v on the same shapes,
+ * with the same arguments, outputs and results (bit-identical), in three
+ * launches instead of six: one pass reads K and V for the K column sums and
+ * the V column maxima, one launch combines them into k_mean and v_scale, and
+ * one launch quantizes Q, K and V (each workgroup one Q block, K block or V
+ * tile).  workspace: >= sizes.ws_quant_qkv bytes (its contents on entry do
+ * not matter).
+ */
+sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dtype dtype,
+                           int B, int H, int H_kv, int N, int d, int q_group, int smooth_k,
+                           int smooth_q, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                           float* k_scale, float* k_mean, float* q_mean, uint8_t* v_f8,
+                           float* v_scale, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * The Delta S table of smooth Q (SageAttention2 detail page, Algorithm 1:

@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
         -> dict(q_i8, q_scale, k_i8, k_scale, k_mean[, q_mean])
     sage_delta_s(k, qk, sm_scale) -> fp32 [B, H, ceil(N/128), N] (smooth Q)
     sage_quant_v(v) -> dict(v_f8, v_scale)
+    sage_quant_qkv(q, k, v, smooth_k=True, q_group=128, smooth_q=False) -> (qk, vq): both in one call
     sage_quant_v_mxfp4(v) -> dict(v_f4, v_e8) (MXFP4 V)
     sage_attn_fwd(qk, vq, causal=..., sm_scale=..., out_dtype=..., delta_s=None) -> o
     sage_attn_fwd_lse(qk, vq, causal=..., sm_scale=..., lse_corr=None, delta_s=None)
@@ -47,7 +48,7 @@ __all__ = ["SageError", "library_path", "load_library", "sage_buffer_sizes", "sa
            "sage_quant_v", "sage_quant_v_mxfp4", "sage_delta_s", "sage_attn_fwd",
            "sage_attn_fwd_lse", "sage_attn_fwd_mxfp4",
            "sage_lse_correction",
-           "sage_qk_int32", "sage_quant_qk_noalloc", "sageattn", "SagePlan", "BLKQ", "BLKK",
+           "sage_qk_int32", "sage_quant_qk_noalloc", "sage_quant_qkv", "sageattn", "SagePlan", "BLKQ", "BLKK",
            "KV_TILE", "Q_GROUPS", "SCRATCH_BYTES"]
 
 BLKQ, BLKK, KV_TILE = 128, 64, 128
@@ -65,7 +66,7 @@ class SageError(RuntimeError):
 class _Sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_f8", "v_scale", "o",
-        "ws_quant_qk", "ws_quant_v", "q_mean", "delta_s", "v_f4", "v_e8")]
+        "ws_quant_qk", "ws_quant_v", "q_mean", "delta_s", "v_f4", "v_e8", "ws_quant_qkv")]
 
 
 _lib = None
@@ -104,9 +105,11 @@ def load_library():
     lib.sage_qk_int32.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp]
     lib.sage_quant_qk_noalloc.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp,
                                           vp, vp]
+    lib.sage_quant_qkv.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp,
+                                   vp, vp, vp, sz, vp]
     for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_delta_s", "sage_quant_v", "sage_attn_fwd",
               "sage_attn_fwd_lse", "sage_lse_correction", "sage_qk_int32", "sage_quant_v_mxfp4",
-              "sage_attn_fwd_mxfp4", "sage_quant_qk_noalloc"):
+              "sage_attn_fwd_mxfp4", "sage_quant_qk_noalloc", "sage_quant_qkv"):
         getattr(lib, f).restype = i
     _lib = lib
     return lib
@@ -237,6 +240,43 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, smooth_k: bool = True, *,
         _stream(stream, q.device))
     _check(st, "sage_quant_qk")
     return out
+
+
+def sage_quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, smooth_k: bool = True, *,
+                   q_group: int = BLKQ, smooth_q: bool = False, out_qk=None, out_v=None,
+                   workspace=None, stream=None):
+    """sage_quant_qk and sage_quant_v in one call (three launches, bit-identical results);
+    returns (qk dict, vq dict)."""
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (B, H_kv, N, d) or v.shape != (B, H_kv, N, d):
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if q_group not in Q_GROUPS:
+        raise ValueError(f"q_group must be one of {Q_GROUPS}")
+    out_qk = out_qk or _alloc_qk(B, H, H_kv, N, d, q.device, q_group, smooth_q)
+    out_v = out_v or _alloc_v(B, H_kv, N, d, q.device)
+    if smooth_q and "q_mean" not in out_qk:
+        raise ValueError("smooth_q needs out_qk['q_mean']")
+    sizes = sage_buffer_sizes(B, H, H_kv, N, d, q_group)
+    _check_sizes("sage_quant_qkv", sizes, q_i8=out_qk["q_i8"], q_scale=out_qk["q_scale"],
+                 k_i8=out_qk["k_i8"], k_scale=out_qk["k_scale"], k_mean=out_qk["k_mean"],
+                 q_mean=out_qk.get("q_mean") if smooth_q else None, v_f8=out_v["v_f8"],
+                 v_scale=out_v["v_scale"])
+    _need_gpu(q, k, v, out_v["v_f8"], out_v["v_scale"],
+              *(t for n, t in out_qk.items() if n != "q_mean" or smooth_q))
+    if workspace is None:
+        workspace = torch.empty(max(sizes["ws_quant_qkv"], 16), dtype=torch.uint8, device=q.device)
+    st = load_library().sage_quant_qkv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q.dtype), B, H, H_kv, N, d, q_group,
+        int(bool(smooth_k)), int(bool(smooth_q)), out_qk["q_i8"].data_ptr(),
+        out_qk["q_scale"].data_ptr(), out_qk["k_i8"].data_ptr(), out_qk["k_scale"].data_ptr(),
+        out_qk["k_mean"].data_ptr(), _ptr(out_qk.get("q_mean")) if smooth_q else None,
+        out_v["v_f8"].data_ptr(), out_v["v_scale"].data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st, "sage_quant_qkv")
+    return out_qk, out_v
 
 
 SCRATCH_BYTES = 16 << 20   # SAGE_SCRATCH_BYTES: the library's fixed scratch array
@@ -519,16 +559,20 @@ class SagePlan:
         self.delta_s = (torch.empty((B, H, -(-N // BLKQ), N), dtype=torch.float32, device=device)
                         if smooth_q else None)
         self.vq = _alloc_v4(B, H_kv, N, d, device) if pv == "mxfp4" else _alloc_v(B, H_kv, N, d, device)
-        self.ws_qk = torch.empty(max(sz["ws_quant_qk"], 16), dtype=torch.uint8, device=device)
+        self.ws_qk = torch.empty(max(sz["ws_quant_qkv"], 16), dtype=torch.uint8, device=device)
         self.ws_v = torch.empty(max(sz["ws_quant_v"], 16), dtype=torch.uint8, device=device)
         self.o = torch.empty((B, H, N, d), dtype=dtype, device=device)
 
     def quant(self, q, k, v, stream=None):
-        sage_quant_qk(q, k, True, q_group=self.q_group, smooth_q=self.smooth_q, out=self.qk,
-                      workspace=self.ws_qk, stream=stream)
+        if self.pv == "mxfp4":
+            sage_quant_qk(q, k, True, q_group=self.q_group, smooth_q=self.smooth_q, out=self.qk,
+                          workspace=self.ws_qk, stream=stream)
+            self.quant_v(v, stream)
+        else:
+            sage_quant_qkv(q, k, v, True, q_group=self.q_group, smooth_q=self.smooth_q,
+                           out_qk=self.qk, out_v=self.vq, workspace=self.ws_qk, stream=stream)
         if self.smooth_q:
             sage_delta_s(k, self.qk, self.sm_scale, out=self.delta_s, stream=stream)
-        self.quant_v(v, stream)
 
     def quant_v(self, v, stream=None):
         if self.pv == "mxfp4":

@@ -66,20 +66,19 @@ __device__ __forceinline__ float div_rn(float v, float s, float y) {
 constexpr float kDivRnMinScale = 1e-30f;
 
 // ---------------------------------------------------------------------------
-// Per-channel statistics over a chunk of kStatChunk tokens.
-// MODE 0: FP64 sum (K).  MODE 1: abs max (V), stored as float.
-// grid (nchunk, B*Hkv); ws layout [B*Hkv][nchunk][D] (double or float).
+// Per-channel statistics of one [N][D] slice over a chunk of kStatChunk
+// tokens: MODE 0 the FP64 sum (K), MODE 1 the absolute max (V, as float).
+// The RPP row groups of the workgroup are combined in a fixed order; ws is
+// [B*Hkv][nchunk][D] (double or float).
 template <int D, bool BF16, int MODE>
-__global__ __launch_bounds__(kQuantThreads) void colstats_partial(const void* __restrict__ x,
-                                                                  void* __restrict__ ws, int N,
-                                                                  int nchunk) {
+__device__ __forceinline__ void colstats_chunk(const void* __restrict__ x, void* __restrict__ ws,
+                                               int N, int nchunk, int chunk, int bh,
+                                               double (*red)[D]) {
   constexpr int TPR = D / 8;                    // threads per token row
   constexpr int RPP = kQuantThreads / TPR;      // rows per pass
-  const int chunk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, cg = tid % TPR, rsub = tid / TPR;
   const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
   const int n0 = chunk * kStatChunk, n1 = min(N, n0 + kStatChunk);
-
   double acc[8];
   float mx[8];
 #pragma unroll
@@ -94,8 +93,6 @@ __global__ __launch_bounds__(kQuantThreads) void colstats_partial(const void* __
       else mx[i] = fmaxf(mx[i], fabsf(v[i]));
     }
   }
-  // combine the RPP row groups in a fixed order
-  __shared__ double red[RPP][D];
 #pragma unroll
   for (int i = 0; i < 8; ++i) red[rsub][cg * 8 + i] = MODE == 0 ? acc[i] : (double)mx[i];
   __syncthreads();
@@ -112,91 +109,77 @@ __global__ __launch_bounds__(kQuantThreads) void colstats_partial(const void* __
   }
 }
 
-// MODE 0: out[bh][c] = float32(sum / N) (the K mean), or 0 when !enable.
-// MODE 1: out[bh][c] = float32(amax / 448) (the V scale).
-// kQuantThreads threads per (b, kv head): thread (r, c) combines chunks
-// r, r + R, ... of channel c in order, then the R partials are combined in
-// order (a fixed order, so the result is deterministic).
-template <int D, int MODE>
-__global__ __launch_bounds__(kQuantThreads) void colstats_final(const void* __restrict__ ws,
-                                                                float* __restrict__ out, int N,
-                                                                int nchunk, int enable) {
+// One pass over a chunk of tokens of K and/or V: the FP64 column sums of K
+// (for its mean) and the column amax of V (for its scales).  grid (nchunk,
+// B*Hkv).
+template <int D, bool BF16>
+__global__ __launch_bounds__(kQuantThreads) void kv_stats_partial(const void* __restrict__ k,
+                                                                  const void* __restrict__ v,
+                                                                  double* __restrict__ kws,
+                                                                  float* __restrict__ vws, int N,
+                                                                  int nchunk, int do_k, int do_v) {
+  __shared__ double red[kQuantThreads / (D / 8)][D];
+  if (do_k) colstats_chunk<D, BF16, 0>(k, kws, N, nchunk, blockIdx.x, blockIdx.y, red);
+  if (do_k && do_v) __syncthreads();
+  if (do_v) colstats_chunk<D, BF16, 1>(v, vws, N, nchunk, blockIdx.x, blockIdx.y, red);
+}
+
+// The chunks combined: k_mean[bh][c] = float32(sum / N) (0 when !smooth_k)
+// and v_scale[bh][c] = float32(amax / 448).  kQuantThreads threads per (b, kv
+// head): thread (r, c) combines chunks r, r + R, ... of channel c in order,
+// then the R partials are combined in order (a fixed order, so the result is
+// deterministic; the K sums are exact, so order-free anyway).  grid (B*Hkv).
+template <int D>
+__global__ __launch_bounds__(kQuantThreads) void kv_stats_final(const double* __restrict__ kws,
+                                                                const float* __restrict__ vws,
+                                                                float* __restrict__ k_mean,
+                                                                float* __restrict__ v_scale, int N,
+                                                                int nchunk, int do_k, int smooth_k,
+                                                                int do_v) {
   constexpr int R = kQuantThreads / D;
   const int bh = blockIdx.x, c = threadIdx.x % D, r = threadIdx.x / D;
   __shared__ double red[R][D];
-  if (MODE == 0) {
-    const double* w = reinterpret_cast<const double*>(ws) + (size_t)bh * nchunk * D + c;
+  if (do_k) {
+    const double* w = kws + (size_t)bh * nchunk * D + c;
     double s = 0.0;
-    if (enable) {
+    if (smooth_k) {
 #pragma unroll 8
-      for (int k = r; k < nchunk; k += R) s += w[(size_t)k * D];
+      for (int kk = r; kk < nchunk; kk += R) s += w[(size_t)kk * D];
     }
     red[r][c] = s;
-  } else {
-    const float* w = reinterpret_cast<const float*>(ws) + (size_t)bh * nchunk * D + c;
+    __syncthreads();
+    if (r == 0) {
+      double t = red[0][c];
+#pragma unroll
+      for (int i = 1; i < R; ++i) t += red[i][c];
+      k_mean[(size_t)bh * D + c] = smooth_k ? (float)(t / (double)N) : 0.f;
+    }
+    __syncthreads();
+  }
+  if (do_v) {
+    const float* w = vws + (size_t)bh * nchunk * D + c;
     float m = 0.f;
 #pragma unroll 8
-    for (int k = r; k < nchunk; k += R) m = fmaxf(m, w[(size_t)k * D]);
+    for (int kk = r; kk < nchunk; kk += R) m = fmaxf(m, w[(size_t)kk * D]);
     red[r][c] = m;
-  }
-  __syncthreads();
-  if (r == 0) {
-    if (MODE == 0) {
-      double s = red[0][c];
+    __syncthreads();
+    if (r == 0) {
+      float t = (float)red[0][c];
 #pragma unroll
-      for (int i = 1; i < R; ++i) s += red[i][c];
-      out[(size_t)bh * D + c] = enable ? (float)(s / (double)N) : 0.f;
-    } else {
-      float m = (float)red[0][c];
-#pragma unroll
-      for (int i = 1; i < R; ++i) m = fmaxf(m, (float)red[i][c]);
-      out[(size_t)bh * D + c] = m / 448.0f;
+      for (int i = 1; i < R; ++i) t = fmaxf(t, (float)red[i][c]);
+      v_scale[(size_t)bh * D + c] = t / 448.0f;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// q_mean[bh][blk][c] = float32(sum / count) over the valid tokens of 128-token
-// block blk: float64 partial sums per thread (exact for fp16/bf16 inputs under
-// the K mean's condition), combined in a fixed order.  grid (nblk, B*H).
-template <int D, bool BF16>
-__global__ __launch_bounds__(kQuantThreads) void q_block_mean(const void* __restrict__ x,
-                                                              float* __restrict__ q_mean, int N,
-                                                              int nblk) {
-  constexpr int TPR = D / 8;
-  constexpr int RPP = kQuantThreads / TPR;   // rows per pass
-  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int rr = tid / TPR, cg = tid % TPR;
-  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
-  double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int p = 0; p < kBlkQ / RPP; ++p) {
-    const int row = blk * kBlkQ + p * RPP + rr;
-    if (row < N) {
-      float v[8];
-      unpack8<BF16>(*reinterpret_cast<const uint4*>(xs + (size_t)row * D + cg * 8), v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] += (double)v[i];
-    }
-  }
-  __shared__ double red[RPP][D];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) red[rr][cg * 8 + i] = s[i];
-  __syncthreads();
-  if (tid < D) {
-    double t = red[0][tid];
-    for (int r = 1; r < RPP; ++r) t += red[r][tid];
-    const int cnt = min(kBlkQ, N - blk * kBlkQ);
-    q_mean[((size_t)bh * nblk + blk) * D + tid] = (float)(t / (double)cnt);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Block max over the workgroup (all threads get the result).
+// Max over the workgroup (all threads get the result); `red` holds one float
+// per wave.
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   const int wave = threadIdx.x / 64;
+  __syncthreads();
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
   float m = red[0];
@@ -205,194 +188,262 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return m;
 }
 
-// Mean subtracted before quantizing: none, the head's K mean mean[bh][c], or
-// the Q mean of the token's 128-block mean[bh][row / 128][c].
-enum { kNoMean = 0, kHeadMean = 1, kBlockMean = 2 };
-
-// Per-block INT8 quantization of one block of BLK tokens x D channels
-// (BLK <= 128, so a block lies in one 128-token mean block).
-// SMOOTH: which mean (float32) is subtracted first.  grid (nblk, B*heads).
-template <int D, int BLK, bool BF16, int SMOOTH>
-__global__ __launch_bounds__(kQuantThreads) void quant_int8(const void* __restrict__ x,
-                                                            const float* __restrict__ mean,
-                                                            int8_t* __restrict__ codes,
-                                                            float* __restrict__ scales, int N,
-                                                            int nblk) {
-  constexpr int TPR = D / 8;
-  constexpr int PER = BLK * TPR / kQuantThreads;   // 16-byte chunks per thread
-  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int cg = tid % TPR;
-  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
-  int8_t* cs = codes + (size_t)bh * N * D;
-
-  static_assert(BLK <= kBlkQ, "a block lies in one mean block");
-  float mu[8];
-  const size_t mrow = SMOOTH == kBlockMean
-                          ? (size_t)bh * ((N + kBlkQ - 1) / kBlkQ) + (blk * BLK) / kBlkQ
-                          : (size_t)bh;
+// 8 values of one token row -> 8 INT8 codes: RNE(x / sc) clamped to +-127,
+// 0 when sc == 0.  FAST: Markstein's three-operation quotient (sc normal and
+// >= kDivRnMinScale), else the IEEE division.
+template <bool FAST>
+__device__ __forceinline__ uint2 codes8(const float* v, float sc) {
+  const float rs = FAST ? 1.0f / sc : 0.f;
+  uint32_t w[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) mu[i] = SMOOTH ? mean[mrow * D + cg * 8 + i] : 0.f;
+  for (int i = 0; i < 8; ++i) {
+    float q = 0.f;
+    if (FAST || sc > 0.f) {
+      const float x = FAST ? div_rn(v[i], sc, rs) : v[i] / sc;
+      q = fminf(fmaxf(__builtin_rintf(x), -127.f), 127.f);
+    }
+    w[i / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (i % 4));
+  }
+  return uint2{w[0], w[1]};
+}
 
+// Everything the quantization launch writes, and the shapes.
+struct QuantArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int8_t* q_i8;
+  float* q_scale;
+  float* q_mean;
+  int8_t* k_i8;
+  float* k_scale;
+  const float* k_mean;
+  uint8_t* v_f8;
+  const float* v_scale;
+  int N, nbq, nbk, ntile, nvw;   // per head: 128-token Q blocks, 64-token K blocks, V tiles, V workgroups
+  int nQ, nK;                    // workgroups of the Q and K roles (the V role takes the rest)
+  int smooth_k;
+};
+
+// Q role: one 128-token block (the smoothing block of Algorithm 1), with one
+// scale per QG consecutive tokens (128, 32 or 1).  SQ: the block's
+// per-channel mean q_bar = float32(exact sum / count) over its valid tokens
+// is written to q_mean and subtracted (float32) before quantizing.
+template <int D, bool BF16, int QG, bool SQ>
+__device__ __forceinline__ void quant_q_block(const QuantArgs& a, int bh, int blk, double (*red)[D],
+                                              float* fs) {
+  constexpr int TPR = D / 8;                    // threads per token row
+  constexpr int RPP = kQuantThreads / TPR;      // rows per pass
+  constexpr int PER = kBlkQ / RPP;              // passes
+  static_assert(RPP <= 32 && 32 % RPP == 0, "a 32-token group is whole passes");
+  const int N = a.N;
+  const int tid = threadIdx.x, cg = tid % TPR, rr = tid / TPR;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(a.q) + (size_t)bh * N * D;
+  int8_t* cs = a.q_i8 + (size_t)bh * N * D;
   float v[PER][8];
-  float amax = 0.f;
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int row = blk * BLK + (p * kQuantThreads + tid) / TPR;
+    const int row = blk * kBlkQ + p * RPP + rr;
     if (row < N) {
-      const uint4 u = *reinterpret_cast<const uint4*>(xs + (size_t)row * D + cg * 8);
-      unpack8<BF16>(u, v[p]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (SMOOTH != kNoMean) v[p][i] = v[p][i] - mu[i];
-        amax = fmaxf(amax, fabsf(v[p][i]));
-      }
+      unpack8<BF16>(*reinterpret_cast<const uint4*>(xs + (size_t)row * D + cg * 8), v[p]);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[p][i] = 0.f;
     }
   }
-  __shared__ float red[kQuantThreads / 64];
-  amax = block_max(amax, red);
-  const float sc = amax / 127.0f;            // IEEE division
-  if (tid == 0) scales[(size_t)bh * nblk + blk] = sc;
-  auto emit = [&](auto fast_tag) __attribute__((always_inline)) {
-    constexpr bool FAST = decltype(fast_tag)::value;
-    const float rs = FAST ? 1.0f / sc : 0.f;
+  if constexpr (SQ) {
+    double sm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm[i] += (double)v[p][i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[rr][cg * 8 + i] = sm[i];
+    __syncthreads();
+    if (tid < D) {
+      double t = red[0][tid];
+      for (int r = 1; r < RPP; ++r) t += red[r][tid];
+      const int cnt = min(kBlkQ, N - blk * kBlkQ);
+      const float mu = (float)(t / (double)cnt);
+      a.q_mean[((size_t)bh * a.nbq + blk) * D + tid] = mu;
+      fs[tid] = mu;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+      if (blk * kBlkQ + p * RPP + rr < N) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] - fs[cg * 8 + i];
+      }
+  }
+  float* wred = fs + D;   // per-wave partial maxima
+  if constexpr (QG == kBlkQ) {
+    float am = 0.f;
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[p][i]));
+    const float sc = block_max(am, wred) / 127.0f;   // IEEE division
+    if (tid == 0) a.q_scale[(size_t)bh * a.nbq + blk] = sc;
+    const bool fast = __builtin_amdgcn_readfirstlane(sc >= kDivRnMinScale ? 1 : 0);
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int row = blk * BLK + (p * kQuantThreads + tid) / TPR;
+      const int row = blk * kBlkQ + p * RPP + rr;
       if (row >= N) continue;
-      uint32_t w[2] = {0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float q = 0.f;
-        if (FAST || sc > 0.f) {   // the fast path implies sc > 0
-          const float x = FAST ? div_rn(v[p][i], sc, rs) : v[p][i] / sc;
-          q = fminf(fmaxf(__builtin_rintf(x), -127.f), 127.f);
-        }
-        w[i / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (i % 4));
-      }
-      *reinterpret_cast<uint2*>(cs + (size_t)row * D + cg * 8) = uint2{w[0], w[1]};
+      const uint2 w = fast ? codes8<true>(v[p], sc) : codes8<false>(v[p], sc);
+      *reinterpret_cast<uint2*>(cs + (size_t)row * D + cg * 8) = w;
     }
-  };
-  // sc is the same for every thread of the block: branch on the scalar unit.
-  if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc >= kDivRnMinScale ? 1.f : 0.f)))
-    emit(std::true_type{});
-  else
-    emit(std::false_type{});
-}
-
-// Per-token INT8 quantization: one scale per token.  The D/8 consecutive
-// threads of a token each load 8 channels; the token's amax is reduced by
-// xor-shuffles among them.  SMOOTH: subtract the Q mean of the token's
-// 128-block first.  grid (ceil(N / tokens per workgroup), B*heads).
-template <int D, bool BF16, bool SMOOTH>
-__global__ __launch_bounds__(kQuantThreads) void quant_int8_tok(const void* __restrict__ x,
-                                                                const float* __restrict__ mean,
-                                                                int8_t* __restrict__ codes,
-                                                                float* __restrict__ scales, int N) {
-  constexpr int TPR = D / 8;
-  constexpr int TPB = kQuantThreads / TPR;   // tokens per workgroup
-  static_assert(TPR <= 64 && (TPR & (TPR - 1)) == 0, "a token's threads share one wave");
-  const int bh = blockIdx.y, tid = threadIdx.x;
-  const int row = blockIdx.x * TPB + tid / TPR, cg = tid % TPR;
-  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
-  float v[8];
-  float amax = 0.f;
-  if (row < N) {
-    unpack8<BF16>(*reinterpret_cast<const uint4*>(xs + (size_t)row * D + cg * 8), v);
-    if (SMOOTH) {
-      const float* mu =
-          mean + ((size_t)bh * ((N + kBlkQ - 1) / kBlkQ) + row / kBlkQ) * D + cg * 8;
+  } else if constexpr (QG == 32) {
+    // pass p holds rows p*RPP .. +RPP of the block: group p*RPP/32
+    float am[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = v[i] - mu[i];
+    for (int p = 0; p < PER; ++p)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am[p * RPP / 32] = fmaxf(am[p * RPP / 32], fabsf(v[p][i]));
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) am[g] = fmaxf(am[g], __shfl_xor(am[g], o));
+    const int wave = tid / 64;
+    __syncthreads();
+    if ((tid & 63) == 0) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) wred[wave * 4 + g] = am[g];
     }
+    __syncthreads();
+    float sc[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int g = 0; g < 4; ++g) {
+      float m = wred[g];
+#pragma unroll
+      for (int w = 1; w < kQuantThreads / 64; ++w) m = fmaxf(m, wred[w * 4 + g]);
+      sc[g] = m / 127.0f;                             // IEEE division
+    }
+    const int nq = (N + 31) / 32;
+    if (tid < 4 && blk * 4 + tid < nq) a.q_scale[(size_t)bh * nq + blk * 4 + tid] = sc[tid];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int row = blk * kBlkQ + p * RPP + rr;
+      if (row >= N) continue;
+      const float s = sc[p * RPP / 32];
+      const bool fast = __builtin_amdgcn_readfirstlane(s >= kDivRnMinScale ? 1 : 0);
+      const uint2 w = fast ? codes8<true>(v[p], s) : codes8<false>(v[p], s);
+      *reinterpret_cast<uint2*>(cs + (size_t)row * D + cg * 8) = w;
+    }
   } else {
+    static_assert(QG == 1, "Q groups of 128, 32 or 1 tokens");
+    // one scale per token: its TPR threads are consecutive lanes of a wave
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  }
+    for (int p = 0; p < PER; ++p) {
+      const int row = blk * kBlkQ + p * RPP + rr;
+      float am = 0.f;
 #pragma unroll
-  for (int o = TPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  const float sc = amax / 127.0f;            // IEEE division
-  auto emit = [&](auto fast_tag) __attribute__((always_inline)) {
-    constexpr bool FAST = decltype(fast_tag)::value;
-    uint32_t w[2] = {0u, 0u};
-    const float rs = FAST ? 1.0f / sc : 0.f;
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[p][i]));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float q = 0.f;
-      if (FAST || sc > 0.f) {
-        const float y = FAST ? div_rn(v[i], sc, rs) : v[i] / sc;
-        q = fminf(fmaxf(__builtin_rintf(y), -127.f), 127.f);
-      }
-      w[i / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (i % 4));
+      for (int o = TPR / 2; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+      const float s = am / 127.0f;                    // IEEE division
+      // the three-operation division when every token of the wave allows it
+      const bool fast = __builtin_amdgcn_ballot_w64(!(s >= kDivRnMinScale)) == 0;
+      if (row >= N) continue;
+      if (cg == 0) a.q_scale[(size_t)bh * N + row] = s;
+      const uint2 w = fast ? codes8<true>(v[p], s) : codes8<false>(v[p], s);
+      *reinterpret_cast<uint2*>(cs + (size_t)row * D + cg * 8) = w;
     }
-    *reinterpret_cast<uint2*>(codes + (size_t)bh * N * D + (size_t)row * D + cg * 8) =
-        uint2{w[0], w[1]};
-  };
-  if (row < N) {
-    if (cg == 0) scales[(size_t)bh * N + row] = sc;
-    // the three-operation division when every token of the wave allows it
-    if (__builtin_amdgcn_ballot_w64(!(sc >= kDivRnMinScale)) == 0) emit(std::true_type{});
-    else emit(std::false_type{});
   }
 }
 
-// ---------------------------------------------------------------------------
-// FP8 V.  Each 16-byte chunk of the v_f8 layout (sage.h) holds one channel
+// K role: one 64-token block of K (minus its mean when smoothing K).
+template <int D, bool BF16>
+__device__ __forceinline__ void quant_k_block(const QuantArgs& a, int bh, int blk, float* wred) {
+  constexpr int TPR = D / 8;
+  constexpr int PER = kBlkK * TPR / kQuantThreads;   // 16-byte chunks per thread
+  const int N = a.N;
+  const int tid = threadIdx.x, cg = tid % TPR;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(a.k) + (size_t)bh * N * D;
+  int8_t* cs = a.k_i8 + (size_t)bh * N * D;
+  float mu[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mu[i] = a.smooth_k ? a.k_mean[(size_t)bh * D + cg * 8 + i] : 0.f;
+  float v[PER][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int row = blk * kBlkK + (p * kQuantThreads + tid) / TPR;
+    if (row < N) {
+      unpack8<BF16>(*reinterpret_cast<const uint4*>(xs + (size_t)row * D + cg * 8), v[p]);
+      if (a.smooth_k) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] - mu[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[p][i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[p][i] = 0.f;
+    }
+  }
+  const float sc = block_max(amax, wred) / 127.0f;   // IEEE division
+  if (tid == 0) a.k_scale[(size_t)bh * a.nbk + blk] = sc;
+  const bool fast = __builtin_amdgcn_readfirstlane(sc >= kDivRnMinScale ? 1 : 0);
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int row = blk * kBlkK + (p * kQuantThreads + tid) / TPR;
+    if (row >= N) continue;
+    const uint2 w = fast ? codes8<true>(v[p], sc) : codes8<false>(v[p], sc);
+    *reinterpret_cast<uint2*>(cs + (size_t)row * D + cg * 8) = w;
+  }
+}
+
+// V role.  Each 16-byte chunk of the v_f8 layout (sage.h) holds one channel
 // and 16 keys, so one wave writes the 64 chunks (kb, cb, p, L = lane) of a
 // (128-key tile, 32-channel block) pair for kb, p in {0, 1}: lane L gathers
 // its channel cb*32 + L%32 for the 64 keys of its lane half straight from
 // HBM (for each key, 32 lanes read 64 contiguous bytes) and stores whole
-// 16-byte chunks, consecutive across the wave.  No LDS staging.
-// grid (ceil(ntile * D/32 / 4), B*Hkv), 4 waves per workgroup.
+// 16-byte chunks, consecutive across the wave.  No LDS staging.  Workgroup
+// w of a (b, kv head) takes pairs 4w .. 4w+3 (one per wave).
 template <int D, bool BF16>
-__global__ __launch_bounds__(kQuantThreads) void quant_v_fp8(const void* __restrict__ x,
-                                                             const float* __restrict__ vscale,
-                                                             uint8_t* __restrict__ out, int N,
-                                                             int ntile) {
+__device__ __forceinline__ void quant_v_wg(const QuantArgs& a, int bh, int w) {
   constexpr int NCB = D / 32;
-  const int bh = blockIdx.y, lane = threadIdx.x % 64;
-  const int pair = blockIdx.x * (kQuantThreads / 64) + threadIdx.x / 64;
+  const int N = a.N, ntile = a.ntile;
+  const int lane = threadIdx.x % 64;
+  const int pair = w * (kQuantThreads / 64) + threadIdx.x / 64;
   if (pair >= ntile * NCB) return;
   const int tile = pair / NCB, cb = pair % NCB;
   const int chan = cb * 32 + (lane % 32), g = lane / 32;
-  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D + chan;
-  const float sv = vscale[(size_t)bh * D + chan];
-  uint8_t* ot = out + ((size_t)bh * ntile + tile) * kKvTile * D;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(a.v) + (size_t)bh * N * D + chan;
+  const float sv = a.v_scale[(size_t)bh * D + chan];
+  uint8_t* ot = a.v_f8 + ((size_t)bh * ntile + tile) * kKvTile * D;
   auto emit = [&](auto fast_tag, auto full_tag) __attribute__((always_inline)) {
-  constexpr bool FAST = decltype(fast_tag)::value;
-  constexpr bool FULL = decltype(full_tag)::value;   // every key of the tile is < N
-  const float rv = FAST ? 1.0f / sv : 0.f;
+    constexpr bool FAST = decltype(fast_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;   // every key of the tile is < N
+    const float rv = FAST ? 1.0f / sv : 0.f;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      // byte i of the chunk: key = kb*64 + fp8_slot_key(g, p*16 + i)
-      float y[16];
+      for (int p = 0; p < 2; ++p) {
+        // byte i of the chunk: key = kb*64 + fp8_slot_key(g, p*16 + i)
+        float y[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int n = tile * kKvTile + kb * 64 + fp8_slot_key(g, p * 16 + i);
-        float v = 0.f;
-        if (FULL || n < N) {
-          const uint16_t h = xs[(size_t)n * D];
-          v = BF16 ? as_float((int)((uint32_t)h << 16)) : (float)__builtin_bit_cast(_Float16, h);
+        for (int i = 0; i < 16; ++i) {
+          const int n = tile * kKvTile + kb * 64 + fp8_slot_key(g, p * 16 + i);
+          float v = 0.f;
+          if (FULL || n < N) {
+            const uint16_t h = xs[(size_t)n * D];
+            v = BF16 ? as_float((int)((uint32_t)h << 16)) : (float)__builtin_bit_cast(_Float16, h);
+          }
+          const float x = FAST ? div_rn(v, sv, rv) : v / sv;
+          y[i] = (sv > 0.f) ? fminf(fmaxf(x, -448.f), 448.f) : 0.f;
         }
-        const float x = FAST ? div_rn(v, sv, rv) : v / sv;
-        y[i] = (sv > 0.f) ? fminf(fmaxf(x, -448.f), 448.f) : 0.f;
-      }
-      uint32_t w[4];
+        uint32_t wd[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * q], y[4 * q + 1], 0, false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * q + 2], y[4 * q + 3], pk, true);
-        w[q] = (uint32_t)pk;
+        for (int q = 0; q < 4; ++q) {
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * q], y[4 * q + 1], 0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * q + 2], y[4 * q + 3], pk, true);
+          wd[q] = (uint32_t)pk;
+        }
+        const int chunk = ((kb * NCB + cb) * 2 + p) * 64 + lane;
+        *reinterpret_cast<uint4*>(ot + (size_t)chunk * 16) = uint4{wd[0], wd[1], wd[2], wd[3]};
       }
-      const int chunk = ((kb * NCB + cb) * 2 + p) * 64 + lane;
-      *reinterpret_cast<uint4*>(ot + (size_t)chunk * 16) = uint4{w[0], w[1], w[2], w[3]};
-    }
   };
   const bool fast = sv >= kDivRnMinScale || sv <= 0.f;   // sv <= 0: codes 0 either way
   if ((tile + 1) * kKvTile <= N) {
@@ -402,6 +453,28 @@ __global__ __launch_bounds__(kQuantThreads) void quant_v_fp8(const void* __restr
     if (fast) emit(std::true_type{}, std::false_type{});
     else emit(std::false_type{}, std::false_type{});
   }
+}
+
+// The quantization launch: workgroups [0, nQ) quantize 128-token Q blocks,
+// [nQ, nQ + nK) 64-token K blocks, the rest V tiles (each role's work is
+// independent; the K mean and V scales come from kv_stats_final).  One
+// launch for what took one per tensor.  grid (nQ + nK + nV).
+template <int D, bool BF16, int QG, bool SQ>
+__global__ __launch_bounds__(kQuantThreads) void quant_qkv_kernel(QuantArgs a) {
+  __shared__ double red[kQuantThreads / (D / 8)][D];
+  __shared__ float fs[D + 16];
+  int id = blockIdx.x;
+  if (id < a.nQ) {
+    quant_q_block<D, BF16, QG, SQ>(a, id / a.nbq, id % a.nbq, red, fs);
+    return;
+  }
+  id -= a.nQ;
+  if (id < a.nK) {
+    quant_k_block<D, BF16>(a, id / a.nbk, id % a.nbk, fs);
+    return;
+  }
+  id -= a.nK;
+  quant_v_wg<D, BF16>(a, id / a.nvw, id % a.nvw);
 }
 
 // ---------------------------------------------------------------------------
@@ -507,99 +580,96 @@ size_t sage_ws_quant_v_bytes(int B, int H_kv, int N, int d) {
   return (size_t)B * H_kv * nchunks(N) * d * sizeof(float);
 }
 
-template <int D, bool BF16, bool SQ>
-static void launch_quant_q(const void* q, const float* q_mean, int B, int H, int N, int q_group,
-                           int8_t* q_i8, float* q_scale, hipStream_t st) {
+// The three launches of a quantization call: column statistics of K (when
+// smoothing it) and/or V, their combination into the K mean and V scales, and
+// one launch quantizing Q and K (q != nullptr) and/or V (v != nullptr).
+// ws: K sums [B*Hkv][nchunk][d] doubles, then V maxima as floats.
+template <int D, bool BF16, int QG, bool SQ>
+static hipError_t quant_impl(const void* q, const void* k, const void* v, int B, int H, int H_kv,
+                             int N, int smooth_k, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                             float* k_scale, float* k_mean, float* q_mean, uint8_t* v_f8,
+                             float* v_scale, void* ws, hipStream_t st) {
   using namespace sage;
-  constexpr int QM = SQ ? kBlockMean : kNoMean;
-  if (q_group == kBlkQ) {
-    const int nbq = (N + kBlkQ - 1) / kBlkQ;
-    hipLaunchKernelGGL((quant_int8<D, kBlkQ, BF16, QM>), dim3(nbq, B * H), dim3(kQuantThreads), 0,
-                       st, q, q_mean, q_i8, q_scale, N, nbq);
-  } else if (q_group == kWaveQ) {
-    const int nbq = (N + kWaveQ - 1) / kWaveQ;
-    hipLaunchKernelGGL((quant_int8<D, kWaveQ, BF16, QM>), dim3(nbq, B * H), dim3(kQuantThreads), 0,
-                       st, q, q_mean, q_i8, q_scale, N, nbq);
-  } else {
-    constexpr int tpb = kQuantThreads / (D / 8);
-    hipLaunchKernelGGL((quant_int8_tok<D, BF16, SQ>), dim3((N + tpb - 1) / tpb, B * H),
-                       dim3(kQuantThreads), 0, st, q, q_mean, q_i8, q_scale, N);
-  }
-}
-
-template <int D, bool BF16>
-static hipError_t quant_qk_impl(const void* q, const void* k, int B, int H, int H_kv, int N,
-                                int q_group, int smooth_k, int smooth_q, int8_t* q_i8,
-                                float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                                float* q_mean, void* ws, hipStream_t st) {
-  using namespace sage;
-  if (q_group != kBlkQ && q_group != kWaveQ && q_group != 1) return hipErrorInvalidValue;
+  const bool do_qk = q != nullptr, do_v = v != nullptr;
   const int nc = nchunks(N);
-  const int nbk = (N + kBlkK - 1) / kBlkK;
-  if (smooth_k) {
-    hipLaunchKernelGGL((colstats_partial<D, BF16, 0>), dim3(nc, B * H_kv), dim3(kQuantThreads), 0,
-                       st, k, ws, N, nc);
-  }
-  hipLaunchKernelGGL((colstats_final<D, 0>), dim3(B * H_kv), dim3(kQuantThreads), 0, st, ws, k_mean,
-                     N, nc, smooth_k);
-  if (smooth_q) {
-    const int nmb = (N + kBlkQ - 1) / kBlkQ;
-    hipLaunchKernelGGL((q_block_mean<D, BF16>), dim3(nmb, B * H), dim3(kQuantThreads), 0, st, q,
-                       q_mean, N, nmb);
-    launch_quant_q<D, BF16, true>(q, q_mean, B, H, N, q_group, q_i8, q_scale, st);
-  } else {
-    launch_quant_q<D, BF16, false>(q, nullptr, B, H, N, q_group, q_i8, q_scale, st);
-  }
-  if (smooth_k)
-    hipLaunchKernelGGL((quant_int8<D, kBlkK, BF16, kHeadMean>), dim3(nbk, B * H_kv),
-                       dim3(kQuantThreads), 0, st, k, k_mean, k_i8, k_scale, N, nbk);
-  else
-    hipLaunchKernelGGL((quant_int8<D, kBlkK, BF16, kNoMean>), dim3(nbk, B * H_kv),
-                       dim3(kQuantThreads), 0, st, k, nullptr, k_i8, k_scale, N, nbk);
+  double* kws = reinterpret_cast<double*>(ws);
+  float* vws = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                        (do_qk && smooth_k ? sage_ws_quant_qk_bytes(B, H_kv, N, D) : 0));
+  if ((do_qk && smooth_k) || do_v)
+    hipLaunchKernelGGL((kv_stats_partial<D, BF16>), dim3(nc, B * H_kv), dim3(kQuantThreads), 0, st,
+                       k, v, kws, vws, N, nc, (int)(do_qk && smooth_k), (int)do_v);
+  hipLaunchKernelGGL((kv_stats_final<D>), dim3(B * H_kv), dim3(kQuantThreads), 0, st, kws, vws,
+                     k_mean, v_scale, N, nc, (int)do_qk, smooth_k, (int)do_v);
+  QuantArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.q_i8 = q_i8; a.q_scale = q_scale; a.q_mean = q_mean;
+  a.k_i8 = k_i8; a.k_scale = k_scale; a.k_mean = k_mean;
+  a.v_f8 = v_f8; a.v_scale = v_scale;
+  a.N = N;
+  a.nbq = (N + kBlkQ - 1) / kBlkQ;
+  a.nbk = (N + kBlkK - 1) / kBlkK;
+  a.ntile = (N + kKvTile - 1) / kKvTile;
+  a.nvw = (a.ntile * (D / 32) + kQuantThreads / 64 - 1) / (kQuantThreads / 64);
+  a.nQ = do_qk ? B * H * a.nbq : 0;
+  a.nK = do_qk ? B * H_kv * a.nbk : 0;
+  a.smooth_k = smooth_k;
+  const long long nV = do_v ? (long long)B * H_kv * a.nvw : 0;
+  const long long grid = (long long)a.nQ + a.nK + nV;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_qkv_kernel<D, BF16, QG, SQ>), dim3((unsigned)grid), dim3(kQuantThreads),
+                     0, st, a);
   return hipGetLastError();
 }
 
 template <int D, bool BF16>
-static hipError_t quant_v_impl(const void* v, int B, int H_kv, int N, uint8_t* v_f8,
-                               float* v_scale, void* ws, hipStream_t st) {
-  using namespace sage;
-  const int nc = nchunks(N);
-  const int nt = (N + kKvTile - 1) / kKvTile;
-  hipLaunchKernelGGL((colstats_partial<D, BF16, 1>), dim3(nc, B * H_kv), dim3(kQuantThreads), 0, st,
-                     v, ws, N, nc);
-  hipLaunchKernelGGL((colstats_final<D, 1>), dim3(B * H_kv), dim3(kQuantThreads), 0, st, ws, v_scale,
-                     N, nc, 1);
-  const int pairs = nt * (D / 32), wpg = kQuantThreads / 64;
-  hipLaunchKernelGGL((quant_v_fp8<D, BF16>), dim3((pairs + wpg - 1) / wpg, B * H_kv),
-                     dim3(kQuantThreads), 0, st, v, v_scale, v_f8, N, nt);
-  return hipGetLastError();
+static hipError_t quant_dispatch(const void* q, const void* k, const void* v, int B, int H,
+                                 int H_kv, int N, int q_group, int smooth_k, int smooth_q,
+                                 int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                 float* k_mean, float* q_mean, uint8_t* v_f8, float* v_scale,
+                                 void* ws, hipStream_t st) {
+#define SAGE_QI(QG, SQ)                                                                     \
+  if (q_group == QG && (smooth_q != 0) == SQ)                                               \
+    return quant_impl<D, BF16, QG, SQ>(q, k, v, B, H, H_kv, N, smooth_k, q_i8, q_scale, k_i8, \
+                                       k_scale, k_mean, q_mean, v_f8, v_scale, ws, st);
+  SAGE_QI(128, false)
+  SAGE_QI(128, true)
+  SAGE_QI(32, false)
+  SAGE_QI(32, true)
+  SAGE_QI(1, false)
+  SAGE_QI(1, true)
+#undef SAGE_QI
+  return hipErrorInvalidValue;
+}
+
+hipError_t sage_launch_quant(const void* q, const void* k, const void* v, int bf16, int B, int H,
+                             int H_kv, int N, int d, int q_group, int smooth_k, int smooth_q,
+                             int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                             float* k_mean, float* q_mean, uint8_t* v_f8, float* v_scale, void* ws,
+                             hipStream_t st) {
+#define SAGE_QD(DD, BB)                                                                       \
+  if (d == DD && (bf16 != 0) == BB)                                                           \
+    return quant_dispatch<DD, BB>(q, k, v, B, H, H_kv, N, q_group, smooth_k, smooth_q, q_i8,   \
+                                  q_scale, k_i8, k_scale, k_mean, q_mean, v_f8, v_scale, ws, st);
+  SAGE_QD(64, false)
+  SAGE_QD(64, true)
+  SAGE_QD(128, false)
+  SAGE_QD(128, true)
+#undef SAGE_QD
+  return hipErrorInvalidValue;
 }
 
 hipError_t sage_launch_quant_qk(const void* q, const void* k, int bf16, int B, int H, int H_kv,
                                 int N, int d, int q_group, int smooth_k, int smooth_q,
                                 int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
                                 float* k_mean, float* q_mean, void* ws, hipStream_t st) {
-#define SAGE_QQK(DD, BB)                                                                       \
-  if (d == DD && (bf16 != 0) == BB)                                                            \
-    return quant_qk_impl<DD, BB>(q, k, B, H, H_kv, N, q_group, smooth_k, smooth_q, q_i8,       \
-                                 q_scale, k_i8, k_scale, k_mean, q_mean, ws, st);
-  SAGE_QQK(64, false)
-  SAGE_QQK(64, true)
-  SAGE_QQK(128, false)
-  SAGE_QQK(128, true)
-#undef SAGE_QQK
-  return hipErrorInvalidValue;
+  return sage_launch_quant(q, k, nullptr, bf16, B, H, H_kv, N, d, q_group, smooth_k, smooth_q, q_i8,
+                           q_scale, k_i8, k_scale, k_mean, q_mean, nullptr, nullptr, ws, st);
 }
 
 hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, int d,
                                uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st) {
-  if (d == 64)
-    return bf16 ? quant_v_impl<64, true>(v, B, H_kv, N, v_f8, v_scale, ws, st)
-                : quant_v_impl<64, false>(v, B, H_kv, N, v_f8, v_scale, ws, st);
-  if (d == 128)
-    return bf16 ? quant_v_impl<128, true>(v, B, H_kv, N, v_f8, v_scale, ws, st)
-                : quant_v_impl<128, false>(v, B, H_kv, N, v_f8, v_scale, ws, st);
-  return hipErrorInvalidValue;
+  return sage_launch_quant(nullptr, nullptr, v, bf16, B, H_kv, H_kv, N, d, 128, 0, 0, nullptr,
+                           nullptr, nullptr, nullptr, nullptr, nullptr, v_f8, v_scale, ws, st);
 }
 
 hipError_t sage_launch_quant_v_mxfp4(const void* v, int bf16, int B, int H_kv, int N, int d,

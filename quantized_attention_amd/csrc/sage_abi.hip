@@ -12,6 +12,11 @@ hipError_t sage_launch_quant_qk(const void* q, const void* k, int bf16, int B, i
                                 int N, int d, int q_group, int smooth_k, int smooth_q,
                                 int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
                                 float* k_mean, float* q_mean, void* ws, hipStream_t st);
+hipError_t sage_launch_quant(const void* q, const void* k, const void* v, int bf16, int B, int H,
+                             int H_kv, int N, int d, int q_group, int smooth_k, int smooth_q,
+                             int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                             float* k_mean, float* q_mean, uint8_t* v_f8, float* v_scale, void* ws,
+                             hipStream_t st);
 hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
                                int B, int H, int H_kv, int N, int d, float sm_scale, float* out,
                                hipStream_t st);
@@ -103,6 +108,7 @@ sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, int q_group,
   out->o = b * h * n * dd * 2;
   out->ws_quant_qk = sage_ws_quant_qk_bytes(B, H_kv, N, d);
   out->ws_quant_v = sage_ws_quant_v_bytes(B, H_kv, N, d);
+  out->ws_quant_qkv = out->ws_quant_qk + out->ws_quant_v;
   const size_t nmb = (n + SAGE_BLKQ - 1) / SAGE_BLKQ;
   out->q_mean = b * h * nmb * dd * sizeof(float);
   out->delta_s = (size_t)delta_s_elems(B, H, N) * sizeof(float);
@@ -131,6 +137,31 @@ sage_status sage_quant_qk(const void* q, const void* k, sage_dtype dtype, int B,
   return from_hip(sage_launch_quant_qk(q, k, dtype == SAGE_BF16, B, H, H_kv, N, d, q_group,
                                        smooth_k, smooth_q, q_i8, q_scale, k_i8, k_scale, k_mean,
                                        q_mean, workspace, (hipStream_t)stream));
+}
+
+sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dtype dtype, int B,
+                           int H, int H_kv, int N, int d, int q_group, int smooth_k, int smooth_q,
+                           int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                           float* k_mean, float* q_mean, uint8_t* v_f8, float* v_scale,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !v_f8 || !v_scale)
+    return SAGE_ERR_NULL;
+  if (smooth_q == 1 && !q_mean) return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!valid_q_group(q_group)) return SAGE_ERR_ARG;
+  if (smooth_k != 0 && smooth_k != 1) return SAGE_ERR_ARG;
+  if (smooth_q != 0 && smooth_q != 1) return SAGE_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_i8) || !aligned16(k_i8) ||
+      !aligned16(v_f8))
+    return SAGE_ERR_ALIGN;
+  if (!workspace) return SAGE_ERR_WORKSPACE;
+  if (ws_bytes < sage_ws_quant_qk_bytes(B, H_kv, N, d) + sage_ws_quant_v_bytes(B, H_kv, N, d))
+    return SAGE_ERR_WORKSPACE;
+  return from_hip(sage_launch_quant(q, k, v, dtype == SAGE_BF16, B, H, H_kv, N, d, q_group,
+                                    smooth_k, smooth_q, q_i8, q_scale, k_i8, k_scale, k_mean,
+                                    q_mean, v_f8, v_scale, workspace, (hipStream_t)stream));
 }
 
 sage_status sage_delta_s(const void* k, sage_dtype dtype, const float* k_mean,

@@ -27,10 +27,10 @@ def test_library_exports_every_declared_symbol():
     assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse",
             "sage_lse_correction", "sage_buffer_sizes", "sage_qk_int32", "sage_status_str",
             "sage_delta_s", "sage_quant_v_mxfp4", "sage_attn_fwd_mxfp4",
-            "sage_abi_version", "sage_quant_qk_noalloc"} <= set(names)
+            "sage_abi_version", "sage_quant_qk_noalloc", "sage_quant_qkv"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sage_abi_version() == 6
+    assert lib.sage_abi_version() == 7
 
 
 def test_status_strings():
@@ -54,6 +54,7 @@ def test_buffer_sizes(B, H, H_kv, N, d, q_group):
     assert s["o"] == 2 * B * H * N * d
     assert s["ws_quant_qk"] == 8 * B * H_kv * math.ceil(N / 256) * d
     assert s["ws_quant_v"] == 4 * B * H_kv * math.ceil(N / 256) * d
+    assert s["ws_quant_qkv"] == s["ws_quant_qk"] + s["ws_quant_v"]
     assert s["q_mean"] == 4 * B * H * math.ceil(N / 128) * d
     assert s["delta_s"] == 4 * B * H * math.ceil(N / 128) * N
     assert s["v_f4"] == B * H_kv * math.ceil(N / 128) * 64 * d
@@ -314,3 +315,23 @@ def test_quant_qk_noalloc_rejects(kw, code):
     scratch exceeds its fixed array, before any HIP call."""
     assert _qk_noalloc(qa.load_library(), **kw) == code
     assert qa.sage_buffer_sizes(1, 64, 64, 65536, 128)["ws_quant_qk"] == qa.SCRATCH_BYTES
+
+
+def _qkv(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dt=0, B=1, H=2, H_kv=2, N=256, d=64, qg=128, smooth=1, sq=0,
+             q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, k_mean=FAKE, q_mean=None,
+             v_f8=FAKE, v_scale=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.sage_quant_qkv(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(v=None), 1), (dict(v_scale=None), 1), (dict(sq=1), 1),
+    (dict(B=0), 2), (dict(d=32), 3), (dict(H=3), 4), (dict(dt=2), 5), (dict(smooth=2), 6),
+    (dict(qg=64), 6), (dict(v=FAKE + 8), 9), (dict(v_f8=FAKE + 4), 9), (dict(ws=None), 7),
+    (dict(ws_bytes=1024 + 511), 7),
+])
+def test_quant_qkv_rejects(kw, code):
+    """The one-call quantization validates like sage_quant_qk and sage_quant_v together
+    (its workspace holds both scratch areas: 1024 + 512 bytes at these shapes)."""
+    assert _qkv(qa.load_library(), **kw) == code

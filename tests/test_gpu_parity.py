@@ -256,6 +256,33 @@ def test_deterministic(gpu_lib):
     assert all(torch.equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype,q_group,smooth_k,smooth_q", [
+    (2, 4, 2, 700, 128, torch.float16, 128, True, False),
+    (1, 4, 1, 385, 64, torch.bfloat16, 32, True, True),
+    (1, 8, 2, 257, 128, torch.bfloat16, 1, False, True),
+    (1, 2, 2, 1, 64, torch.float16, 128, True, False),
+    (2, 2, 2, 1000, 64, torch.float16, 1, True, False),
+])
+def test_quant_qkv_matches_oracle(gpu_lib, B, H, H_kv, N, d, dtype, q_group, smooth_k, smooth_q):
+    """The one-call quantization (statistics of K and V in one pass, one launch for all
+    codes): every output bit-exact against the oracle, V codes by decoded value."""
+    print(f"quant_qkv case B{B} H{H}/{H_kv} N{N} d{d} {dtype} q_group {q_group} "
+          f"smooth_k {smooth_k} smooth_q {smooth_q}", flush=True)
+    q, k, v = _rand_inputs(B, H, H_kv, N, d, dtype, seed=N * 19 + d)
+    qk, vq = gpu_lib.sage_quant_qkv(q.to(DEV), k.to(DEV), v.to(DEV), smooth_k, q_group=q_group,
+                                    smooth_q=smooth_q)
+    torch.cuda.synchronize()
+    ref = O.quantize_qk(q, k, smooth_k=smooth_k, q_group=q_group, smooth_q=smooth_q)
+    refv = O.quantize_v(v)
+    names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean"] + (["q_mean"] if smooth_q else [])
+    for n in names:
+        assert np.array_equal(to_np(qk[n]), ref[n]), n
+    assert np.array_equal(to_np(vq["v_scale"]), refv["v_scale"])
+    vn, vpad = v_natural(to_np(vq["v_f8"]), N, d)
+    assert (vpad == 0).all()
+    assert np.array_equal(F8.decode(vn), F8.decode(refv["v_f8"]))
+
+
 # ------------------------------------------------------------------ tile choice (c11)
 
 @pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", [SMALL[i] for i in (0, 1, 2, 3, 6, 9, 10)])
