@@ -1,21 +1,19 @@
 // quant.hip -- smoothing and quantization kernels for gfx950 (HBM-bound).
 //
-//   colstats_partial / colstats_final : per-channel token statistics of a
-//       [N][d] slice: the exact FP64 sum of K (its mean smooths K: the
-//       SageAttention synthesis page's Smooth K, Algorithm 1 preprocessing
-//       on the SageAttention2 detail page) or the absolute max of V (the
-//       per-channel FP8 scale of Algorithm 1's psi_V).
-//   quant_int8        : per-block INT8 quantization of Q (128 or 32 tokens)
-//       and of smoothed K (64 tokens): scale = amax/127, code = RNE(x/scale)
-//       (deployment-guide page, quantization formula).
-//   quant_int8_tok    : the same rules with one scale per Q token (the
-//       per-thread granularity of the SageAttention2 detail page, Figure 4,
-//       when each matrix-core lane holds one query).
-//   q_block_mean      : per-channel mean of each 128-token Q block (Smooth Q,
-//       Algorithm 1 of the SageAttention2 detail page: q_bar_i = mean(Q_i));
-//       the quantizers then subtract the mean of the token's own block.
-//   quant_v_fp8       : per-channel FP8 E4M3 quantization of V, written
-//       transposed and key-permuted in the fragment layout of sage.h.
+//   kv_stats_partial / kv_stats_final : per-channel token statistics of K
+//       and V in one pass over both: the exact FP64 sum of K (its mean
+//       smooths K: the SageAttention synthesis page's Smooth K, Algorithm 1
+//       preprocessing on the SageAttention2 detail page) and the absolute
+//       max of V (the per-channel FP8 scale of Algorithm 1's psi_V).
+//   quant_qkv_kernel  : one launch for every code, each workgroup in one role:
+//       a 128-token Q block (Algorithm 1's smoothing block; optional smooth-Q
+//       mean q_bar_i = mean(Q_i) subtracted; one scale per 128, 32 or 1
+//       tokens, the per-block / per-warp / per-thread granularities of the
+//       SageAttention2 detail page, Figure 4 and Table 6), a 64-token K block
+//       (minus the K mean), or V tiles (per-channel FP8 E4M3, written
+//       transposed and key-permuted in the fragment layout of sage.h).  INT8
+//       rules: scale = amax/127, code = RNE(x/scale) (deployment-guide page,
+//       quantization formula).
 //   quant_v_mxfp4     : MXFP4 V (E2M1 codes, one E8M0 scale per 32
 //       consecutive keys of a channel: the OCP microscaling format the
 //       SageAttention3 synthesis page names), in the FP4 fragment layout.
