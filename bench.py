@@ -114,8 +114,9 @@ def main():
                     help="Q tokens per INT8 scale: 128 per block (default), 32 per wave, "
                          "1 per query")
     ap.add_argument("--smooth-q", action="store_true",
-                    help="smooth Q by its 128-block means and add the Delta S table back "
-                         "(sage_delta_s, timed separately)")
+                    help="smooth Q by its 128-block means and add the Delta S term back "
+                         "(sage_attn_fwd_smooth_q: Delta S passes and attention in chunks of Q "
+                         "blocks; the Delta S passes are also timed alone)")
     ap.add_argument("--pv", default="fp8", choices=("fp8", "mxfp4"),
                     help="P V format: FP8 E4M3 (the method's) or MXFP4 on the FP4 matrix cores")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
@@ -210,6 +211,30 @@ def run_lse(w, steps: int, warmup: int) -> dict:
             "attn_fwd_lse_tops": round(w.ops() / (t_al * 1e-3) / 1e12, 2)}
 
 
+def delta_s_alone(plan, k, steps: int) -> float:
+    """Milliseconds of the Delta S passes sage_attn_fwd_smooth_q runs per call (the same
+    chunks of Q blocks, into the plan's workspace), without the attention between them."""
+    import torch
+    import quantized_attention_amd as qa
+    B, H, _, N, _ = plan.shape
+    nmb = -(-N // qa.BLKQ)
+    rows = min(nmb, plan.ws_sq.numel() // (B * H * N * 4))
+    if 16 < rows < nmb:
+        rows -= rows % 16
+    ws = plan.ws_sq[:B * H * rows * N * 4].view(torch.float32)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        for i0 in range(0, nmb, rows):
+            n = min(rows, nmb - i0)
+            qa.sage_delta_s(k, plan.qk, plan.sm_scale, i0=i0, nrows=n,
+                            out=ws[:B * H * n * N].view(B, H, n, N))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 128,
                smooth_q: bool = False, pv: str = "fp8") -> dict:
     """Time `steps` whole steps of workload `w` (inputs resident on the GPU)."""
@@ -242,16 +267,15 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
             qa.sage_quant_qkv(q, k, v, True, q_group=q_group, smooth_q=smooth_q, out_qk=plan.qk,
                               out_v=plan.vq, workspace=plan.ws_qk)
         e[1].record(stream)
-        if smooth_q:
-            qa.sage_delta_s(k, plan.qk, plan.sm_scale, out=plan.delta_s)
         e[2].record(stream)
         plan.attn()
         e[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # smooth Q: the attention phase includes the Delta S passes; time them alone too
+    t_ds = delta_s_alone(plan, k, steps) if smooth_q else 0.0
 
     t_q = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    t_ds = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     t_attn = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
     t_attn_med = statistics.median(e[2].elapsed_time(e[3]) for e in ev)
     ms_step = wall * 1e3 / steps
@@ -284,9 +308,11 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
         "attn_ms_median": round(t_attn_med, 4),
         "attn_tops_median": round(ops / (t_attn_med * 1e-3) / 1e12, 2),
         "quant_ms": round(t_q, 4),
-        "quant_share": round(t_q / (t_q + t_ds + t_attn), 4),
+        "quant_share": round(t_q / (t_q + t_attn), 4),
         "quant_gbs": round(quant_bytes / (t_q * 1e-3) / 1e9, 1),
+        # smooth Q: the Delta S passes inside attn_ms, timed alone, and the workspace
         "delta_s_ms": round(t_ds, 4) if smooth_q else None,
+        "delta_s_ws_bytes": plan.ws_sq.numel() if smooth_q else None,
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_fwd_kernel",
@@ -299,7 +325,8 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
     }
     if not full:
         keep = ("value", "ms_per_step", "config", "attn_tops", "attn_ms", "attn_ms_median",
-                "attn_tops_median", "quant_ms", "quant_share", "quant_gbs", "delta_s_ms")
+                "attn_tops_median", "quant_ms", "quant_share", "quant_gbs", "delta_s_ms",
+                "delta_s_ws_bytes")
         res = {k: res[k] for k in keep}
         res["attn_frac_of_peak"] = round(res["attn_tops"] / PEAK_TOPS, 4)
     return res

@@ -6,8 +6,8 @@
  *   1. Smooth K: subtract the per-channel mean of K over tokens
  *      (SageAttention synthesis page, Smooth K; Algorithm 1 preprocessing).
  *   2. Optionally smooth Q by the per-channel mean of each 128-token block
- *      (Algorithm 1's q_bar_i); the Delta S table q_bar_i . K_j, computed
- *      once by sage_delta_s, adds the removed part back to the scores.
+ *      (Algorithm 1's q_bar_i); the Delta S term q_bar_i . K_j adds the
+ *      removed part back to the scores (sage_attn_fwd_smooth_q).
  *      Quantize Q (or Q - q_bar) per group of 128, 32 or 1 tokens and
  *      smoothed K per block of 64 tokens to INT8 with one FP32 scale per
  *      group: scale = amax / 127, code = round-half-even(x / scale)
@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 7
+#define SAGE_ABI_VERSION 8
 
 /* Q tokens per INT8 scale (default), K tokens per INT8 scale. */
 #define SAGE_BLKQ 128
@@ -106,7 +106,9 @@ typedef struct {
   size_t ws_quant_qk; /* workspace bytes sage_quant_qk needs                    */
   size_t ws_quant_v;  /* workspace bytes sage_quant_v needs                     */
   size_t q_mean;    /* float [B][H][ceil(N/128)][d]   (smooth Q only)           */
-  size_t delta_s;   /* float [B][H][ceil(N/128)][N]   (smooth Q only)           */
+  size_t ws_smooth_q; /* default workspace of sage_attn_fwd_smooth_q, float
+                         [B][H][R][N]: the Delta S rows of R Q blocks (smooth
+                         Q only; R in sage_attn_fwd_smooth_q's comment)       */
   size_t v_f4;      /* uint8 [B][H_kv][ceil(N/128)*64*d]  (MXFP4 V codes)       */
   size_t v_e8;      /* uint8 [B][H_kv][ceil(N/128)*512]   (MXFP4 V scales)      */
   size_t ws_quant_qkv; /* workspace bytes sage_quant_qkv needs (qk + v)        */
@@ -176,23 +178,26 @@ sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dty
                            float* v_scale, void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * The Delta S table of smooth Q (SageAttention2 detail page, Algorithm 1:
- * S_ij = dequant(Q^_i K^_j^T) + GEMV(q_bar_i, K_j^T); its pipeline figure
- * computes the GEMV before quantization, on the smoothed K):
- *   delta_s[b][h][i][j] = float32( sum_c q_mean[b][h][i][c] *
+ * Rows of the Delta S term of smooth Q (SageAttention2 detail page,
+ * Algorithm 1: S_ij = dequant(Q^_i K^_j^T) + GEMV(q_bar_i, K_j^T); its
+ * pipeline figure computes the GEMV before quantization, on the smoothed K):
+ *   delta_s[b][h][r][j] = float32( sum_c q_mean[b][h][i0+r][c] *
  *                         (float32(k[b][h/(H/H_kv)][j][c]) - k_mean[b][h/(H/H_kv)][c])
  *                         * float32(sm_scale * log2(e)) )
- * for every 128-token Q block i and key j < N, in the attention kernel's
- * log2 score units.  The products are exact and the sums are FP64 (FP64
- * matrix cores), rounded once: each entry is the float32 rounding of the
- * exact value up to the FP64 sum's rounding, whatever the summation order.
+ * for the 128-token Q blocks i0 .. i0 + nrows - 1 and every key j < N, in
+ * the attention kernel's log2 score units.  The products are exact and the
+ * sums are FP64 (FP64 matrix cores), rounded once: each entry is the
+ * float32 rounding of the exact value up to the FP64 sum's rounding,
+ * whatever the summation order.  sage_attn_fwd_smooth_q computes these rows
+ * itself; this entry point exposes them for inspection.
  *   k: the original K in `dtype`; k_mean, q_mean: from sage_quant_qk
- *   (k_mean is zeros when K was not smoothed).  sm_scale must be the one
- *   passed to sage_attn_fwd.  delta_s: float, sizes.delta_s bytes.
+ *   (k_mean is zeros when K was not smoothed).  0 <= i0, 1 <= nrows,
+ *   i0 + nrows <= ceil(N/128), else SAGE_ERR_ARG.
+ *   delta_s: float [B][H][nrows][N], caller-owned.
  */
 sage_status sage_delta_s(const void* k, sage_dtype dtype, const float* k_mean,
                          const float* q_mean, int B, int H, int H_kv, int N, int d,
-                         float sm_scale, float* delta_s, void* stream);
+                         float sm_scale, int i0, int nrows, float* delta_s, void* stream);
 
 /*
  * Step 3: per-channel FP8 E4M3 quantization of V.
@@ -208,23 +213,22 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N
                          void* stream);
 
 /*
- * Step 4: the attention kernel.
+ * Step 4: the attention kernel (Q not smoothed; see sage_attn_fwd_smooth_q).
  *   Inputs are the outputs of sage_quant_qk / sage_quant_v for the same
  *   shapes and q_group.  o [B][H][N][d] is written in `out_dtype` (round to
  *   nearest even).
- *   delta_s: NULL for plain Q; for smoothed Q the table of sage_delta_s,
- *     added to every score (the scores then take the exact exponent form).
  *   causal: 1 = key j visible to query i iff j <= i; fully masked key tiles
  *     are skipped.  sm_scale: the softmax scale (> 0, finite), commonly
  *     1/sqrt(d).
- *   P~ is quantized against the running max of the keys seen so far, one
- *   128-key tile at a time; l sums the unquantized P~.
+ *   Per 128-key tile, in float32 with every step rounded once (Algorithm 1's
+ *   inner loop): x = S_int * float32(float32(dQ * dK) * float32(sm_scale *
+ *   log2(e))), m = running max of x, P~ = exp2(x - m), code of P~ = E4M3 RNE
+ *   of P~ * 448; l sums the unquantized P~.
  */
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                           const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                          const float* delta_s, void* o, sage_dtype out_dtype, int B, int H,
-                          int H_kv, int N, int d, int q_group, int causal, float sm_scale,
-                          void* stream);
+                          void* o, sage_dtype out_dtype, int B, int H, int H_kv, int N, int d,
+                          int q_group, int causal, float sm_scale, void* stream);
 
 /*
  * Step 4 with the row log-sum-exp (the per-row softmax state a forward pass
@@ -233,22 +237,53 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
  *   lse: float [B][H][N], required (caller-owned):
  *     lse[b][h][i] = ln sum_j exp(S_ij) + (lse_corr ? lse_corr[b][h][i] : 0)
  *     with S the dequantized scores the softmax used (sm_scale applied, the
- *     causal mask applied, K smoothed if sage_quant_qk smoothed it, Delta S
- *     added when given).
+ *     causal mask applied, K smoothed if sage_quant_qk smoothed it),
+ *     computed as ln(2) * (m + log2 l) from the final running max m and sum l.
  *   lse_corr: float [B][H][N] or NULL.  With smoothed K, pass the output of
  *     sage_lse_correction to get the log-sum-exp of the unsmoothed logits
  *     sm_scale * q . k (smoothing removed sm_scale * q . mean(K) from every
  *     logit of a row; the source-analysis page, smooth_k and LSE correction).
- * Accuracy: the one-FMA exponent form bounds the error of each exponent by
- * 2^-11 in log2 units, so lse is within about 4e-4 of the same quantity in
- * exact arithmetic.
+ * Accuracy: each exponent is the float32 rounding of the score in log2
+ * units, so lse carries a relative error of a few float32 ulps of |lse|
+ * plus the float32 rounding of l's N-term sum.
  */
 sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                               const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                              const float* delta_s, void* o, sage_dtype out_dtype, float* lse,
-                              const float* lse_corr,
+                              void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
                               int B, int H, int H_kv, int N, int d, int q_group, int causal,
                               float sm_scale, void* stream);
+
+/*
+ * Step 4 for smoothed Q (sage_quant_qk with smooth_q = 1): the attention of
+ * sage_attn_fwd / sage_attn_fwd_lse with the Delta S term of Algorithm 1
+ * (SageAttention2 detail page) added to every score before the softmax:
+ *   x = float32(S_int * c + g), rounded once, with c as in sage_attn_fwd and
+ *   g the value sage_delta_s gives for the query's Q block and the key.
+ * The Delta S rows are computed on the fly, a chunk of Q blocks at a time,
+ * into `workspace`: each chunk's rows are written by the Delta S pass and
+ * consumed by the attention of those Q blocks, so memory is B*H*rows*N
+ * floats for a chunk of `rows` blocks, never the whole B*H*ceil(N/128)*N
+ * table.  Results do not depend on the chunk size (each row's arithmetic
+ * is the same).
+ *   k: the original K in k_dtype; k_mean, q_mean: from sage_quant_qk.
+ *   lse: float [B][H][N] or NULL (then lse_corr must be NULL, else
+ *     SAGE_ERR_ARG); meaning as in sage_attn_fwd_lse.
+ *   workspace: device memory of ws_bytes >= B*H*N*4 (one Q block per
+ *     chunk), else SAGE_ERR_WORKSPACE; the chunk is the largest number of
+ *     Q blocks that fits (a multiple of 16 above 16).  sizes.ws_smooth_q is
+ *     the default: R = min(ceil(N/128), max(32, 16 * ceil(ceil(2048 / (B*H))
+ *     / 16))) blocks, enough for 2048 workgroups per attention launch, at
+ *     least 32 blocks per Delta S pass.  Its contents on entry do not
+ *     matter.
+ */
+sage_status sage_attn_fwd_smooth_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                   const float* k_scale, const uint8_t* v_f8,
+                                   const float* v_scale, const void* k, sage_dtype k_dtype,
+                                   const float* k_mean, const float* q_mean, void* o,
+                                   sage_dtype out_dtype, float* lse, const float* lse_corr,
+                                   int B, int H, int H_kv, int N, int d, int q_group, int causal,
+                                   float sm_scale, void* workspace, size_t ws_bytes,
+                                   void* stream);
 
 /*
  * corr[b][h][i] = sm_scale * sum_c q[b][h][i][c] * k_mean[b][h / (H/H_kv)][c]

@@ -14,13 +14,14 @@ Entry points (same names as the C ABI):
     sage_buffer_sizes(B, H, H_kv, N, d, q_group=128) -> dict of byte sizes
     sage_quant_qk(q, k, smooth_k=True, q_group=128, smooth_q=False)
         -> dict(q_i8, q_scale, k_i8, k_scale, k_mean[, q_mean])
-    sage_delta_s(k, qk, sm_scale) -> fp32 [B, H, ceil(N/128), N] (smooth Q)
+    sage_delta_s(k, qk, sm_scale, i0=0, nrows=None) -> fp32 [B, H, nrows, N] (smooth Q rows)
     sage_quant_v(v) -> dict(v_f8, v_scale)
     sage_quant_qkv(q, k, v, smooth_k=True, q_group=128, smooth_q=False) -> (qk, vq): both in one call
     sage_quant_v_mxfp4(v) -> dict(v_f4, v_e8) (MXFP4 V)
-    sage_attn_fwd(qk, vq, causal=..., sm_scale=..., out_dtype=..., delta_s=None) -> o
-    sage_attn_fwd_lse(qk, vq, causal=..., sm_scale=..., lse_corr=None, delta_s=None)
-        -> (o, lse)
+    sage_attn_fwd(qk, vq, causal=..., sm_scale=..., out_dtype=...) -> o
+    sage_attn_fwd_lse(qk, vq, causal=..., sm_scale=..., lse_corr=None) -> (o, lse)
+    sage_attn_fwd_smooth_q(qk, vq, k, causal=..., sm_scale=..., return_lse=False,
+        lse_corr=None, workspace=None) -> o or (o, lse) (smoothed Q, Delta S in chunks)
     sage_attn_fwd_mxfp4(qk, vq4, causal=..., sm_scale=..., return_lse=False) -> o or (o, lse)
     sage_lse_correction(q, k_mean, sm_scale) -> fp32 [B, H, N]
     sage_qk_int32(q_i8, k_i8, b, h) -> int32 [N, N] (diagnostic)
@@ -31,8 +32,9 @@ smooth_k=True, return_lse=False, q_group=128, smooth_q=False)``.  ``q_group`` is
 consecutive Q tokens per scale: 128 (per block), 32 (per wave, the per-warp
 granularity) or 1 (per query, the per-thread granularity); the attention
 entry points read it from the length of ``q_scale``.  ``smooth_q`` subtracts each
-128-token Q block's mean before quantizing and adds the Delta S table back to
-the scores (Algorithm 1's GEMV compensation).  ``pv="mxfp4"`` runs P V in MXFP4
+128-token Q block's mean before quantizing and adds the Delta S term back to
+the scores (Algorithm 1's GEMV compensation), computed a chunk of Q blocks at a
+time into a bounded workspace.  ``pv="mxfp4"`` runs P V in MXFP4
 (E2M1 with E8M0 scales per 32 keys, the OCP format the pages name for MI350-class
 GPUs) on the FP4 matrix cores.
 """
@@ -46,9 +48,10 @@ import torch
 
 __all__ = ["SageError", "library_path", "load_library", "sage_buffer_sizes", "sage_quant_qk",
            "sage_quant_v", "sage_quant_v_mxfp4", "sage_delta_s", "sage_attn_fwd",
-           "sage_attn_fwd_lse", "sage_attn_fwd_mxfp4",
+           "sage_attn_fwd_lse", "sage_attn_fwd_smooth_q", "sage_attn_fwd_mxfp4",
            "sage_lse_correction",
-           "sage_qk_int32", "sage_quant_qk_noalloc", "sage_quant_qkv", "sageattn", "SagePlan", "BLKQ", "BLKK",
+           "sage_qk_int32", "sage_quant_qk_noalloc", "sage_quant_qkv", "sageattn", "SagePlan",
+           "smooth_q_workspace", "BLKQ", "BLKK",
            "KV_TILE", "Q_GROUPS", "SCRATCH_BYTES"]
 
 BLKQ, BLKK, KV_TILE = 128, 64, 128
@@ -66,7 +69,7 @@ class SageError(RuntimeError):
 class _Sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_f8", "v_scale", "o",
-        "ws_quant_qk", "ws_quant_v", "q_mean", "delta_s", "v_f4", "v_e8", "ws_quant_qkv")]
+        "ws_quant_qk", "ws_quant_v", "q_mean", "ws_smooth_q", "v_f4", "v_e8", "ws_quant_qkv")]
 
 
 _lib = None
@@ -92,12 +95,14 @@ def load_library():
     lib.sage_buffer_sizes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(_Sizes)]
     lib.sage_quant_qk.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp,
                                   sz, vp]
-    lib.sage_delta_s.argtypes = [vp, i, vp, vp, i, i, i, i, i, ctypes.c_float, vp, vp]
+    lib.sage_delta_s.argtypes = [vp, i, vp, vp, i, i, i, i, i, ctypes.c_float, i, i, vp, vp]
     lib.sage_quant_v.argtypes = [vp, i, i, i, i, i, vp, vp, vp, sz, vp]
-    lib.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+    lib.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                   ctypes.c_float, vp]
-    lib.sage_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i,
+    lib.sage_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i,
                                       i, i, ctypes.c_float, vp]
+    lib.sage_attn_fwd_smooth_q.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, vp, i, vp, vp,
+                                           i, i, i, i, i, i, i, ctypes.c_float, vp, sz, vp]
     lib.sage_lse_correction.argtypes = [vp, i, vp, i, i, i, i, i, ctypes.c_float, vp, vp]
     lib.sage_quant_v_mxfp4.argtypes = [vp, i, i, i, i, i, vp, vp, vp]
     lib.sage_attn_fwd_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i,
@@ -109,7 +114,8 @@ def load_library():
                                    vp, vp, vp, sz, vp]
     for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_delta_s", "sage_quant_v", "sage_attn_fwd",
               "sage_attn_fwd_lse", "sage_lse_correction", "sage_qk_int32", "sage_quant_v_mxfp4",
-              "sage_attn_fwd_mxfp4", "sage_quant_qk_noalloc", "sage_quant_qkv"):
+              "sage_attn_fwd_mxfp4", "sage_quant_qk_noalloc", "sage_quant_qkv",
+              "sage_attn_fwd_smooth_q"):
         getattr(lib, f).restype = i
     _lib = lib
     return lib
@@ -364,24 +370,28 @@ def sage_attn_fwd_mxfp4(qk: dict, vq4: dict, *, causal: bool, sm_scale: float,
     return (out, lse) if return_lse else out
 
 
-def sage_delta_s(k: torch.Tensor, qk: dict, sm_scale: float, *, out=None,
-                 stream=None) -> torch.Tensor:
-    """The Delta S table of smooth Q: sm_scale * log2(e) * q_mean . (k - k_mean) for
-    every 128-token Q block and key, fp32 [B, H, ceil(N/128), N] (see sage.h)."""
+def sage_delta_s(k: torch.Tensor, qk: dict, sm_scale: float, *, i0: int = 0,
+                 nrows: int | None = None, out=None, stream=None) -> torch.Tensor:
+    """Rows of the Delta S term of smooth Q: sm_scale * log2(e) * q_mean . (k - k_mean)
+    for the 128-token Q blocks i0 .. i0 + nrows - 1 (default: all) and every key,
+    fp32 [B, H, nrows, N] (see sage.h)."""
     _need_gpu(k, qk["k_mean"], qk["q_mean"])
     B, H, nmb, d = qk["q_mean"].shape
     H_kv, N = k.shape[1], k.shape[2]
     if tuple(k.shape) != (B, H_kv, N, d) or nmb != -(-N // BLKQ):
         raise ValueError(f"sage_delta_s: k {list(k.shape)} does not match q_mean "
                          f"{list(qk['q_mean'].shape)}")
+    if nrows is None:
+        nrows = nmb - i0
     if out is None:
-        out = torch.empty((B, H, nmb, N), dtype=torch.float32, device=k.device)
+        out = torch.empty((B, H, max(nrows, 0), N), dtype=torch.float32, device=k.device)
     _check_tensor("sage_delta_s", "k_mean", qk["k_mean"], (B, H_kv, d), torch.float32)
-    _check_tensor("sage_delta_s", "out", out, (B, H, nmb, N), torch.float32)
+    _check_tensor("sage_delta_s", "out", out, (B, H, max(nrows, 0), N), torch.float32)
     _need_gpu(out)
     st = load_library().sage_delta_s(k.data_ptr(), _dt(k.dtype), qk["k_mean"].data_ptr(),
                                      qk["q_mean"].data_ptr(), B, H, H_kv, N, d, float(sm_scale),
-                                     out.data_ptr(), _stream(stream, k.device))
+                                     int(i0), int(nrows), out.data_ptr(),
+                                     _stream(stream, k.device))
     _check(st, "sage_delta_s")
     return out
 
@@ -404,9 +414,8 @@ def sage_quant_v(v: torch.Tensor, *, out=None, workspace=None, stream=None) -> d
 
 
 def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
-                  out_dtype=torch.float16, delta_s=None, out=None, stream=None) -> torch.Tensor:
-    """Attention on quantized inputs; returns O [B, H, N, d] in out_dtype.
-    delta_s: the sage_delta_s table when Q was smoothed."""
+                  out_dtype=torch.float16, out=None, stream=None) -> torch.Tensor:
+    """Attention on quantized inputs (Q not smoothed); returns O [B, H, N, d] in out_dtype."""
     q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
     B, H, N, d = q_i8.shape
     H_kv = k_i8.shape[1]
@@ -414,11 +423,10 @@ def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
     _check_attn_inputs("sage_attn_fwd", qk, out, v_f8=vq["v_f8"], v_scale=vq["v_scale"])
     _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"], out)
-    _check_delta_s(delta_s, qk)
+    _no_q_mean("sage_attn_fwd", qk)
     st = load_library().sage_attn_fwd(
         q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
-        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), _ptr(delta_s), out.data_ptr(),
-        _dt(out.dtype),
+        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
         B, H, H_kv, N, d, _q_group_of(qk["q_scale"], N), int(bool(causal)), float(sm_scale),
         _stream(stream, q_i8.device))
     _check(st, "sage_attn_fwd")
@@ -440,18 +448,14 @@ def _check_attn_inputs(where: str, qk: dict, out, **vbufs):
                          f"{list(out.shape)}")
 
 
-def _check_delta_s(delta_s, qk):
-    B, H, N, _ = qk["q_i8"].shape
-    if delta_s is None:
-        return
-    _need_gpu(delta_s)
-    if delta_s.shape != (B, H, -(-N // BLKQ), N) or delta_s.dtype != torch.float32:
-        raise ValueError("delta_s must be float32 [B, H, ceil(N/128), N]")
+def _no_q_mean(where: str, qk: dict):
+    """Codes of smoothed Q need the Delta S term: only sage_attn_fwd_smooth_q takes them."""
+    if qk.get("q_mean") is not None:
+        raise ValueError(f"{where}: Q was smoothed (qk has q_mean); use sage_attn_fwd_smooth_q")
 
 
 def sage_attn_fwd_lse(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
-                      out_dtype=torch.float16, lse_corr=None, delta_s=None, out=None, lse=None,
-                      stream=None):
+                      out_dtype=torch.float16, lse_corr=None, out=None, lse=None, stream=None):
     """Attention on quantized inputs plus the row log-sum-exp; returns (o, lse).
     lse [B, H, N] fp32 is ln sum_j exp(S_ij) of the scores the softmax used,
     plus lse_corr (the output of sage_lse_correction) when given."""
@@ -469,15 +473,68 @@ def sage_attn_fwd_lse(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
         _need_gpu(lse_corr)
         if lse_corr.shape != (B, H, N) or lse_corr.dtype != torch.float32:
             raise ValueError("lse_corr must be float32 [B, H, N]")
-    _check_delta_s(delta_s, qk)
+    _no_q_mean("sage_attn_fwd_lse", qk)
     st = load_library().sage_attn_fwd_lse(
         q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
-        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), _ptr(delta_s), out.data_ptr(),
-        _dt(out.dtype),
+        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
         lse.data_ptr(), _ptr(lse_corr), B, H, H_kv, N, d, _q_group_of(qk["q_scale"], N),
         int(bool(causal)), float(sm_scale), _stream(stream, q_i8.device))
     _check(st, "sage_attn_fwd_lse")
     return out, lse
+
+
+def smooth_q_workspace(B: int, H: int, N: int, d: int, rows: int | None = None,
+                       device="cuda") -> torch.Tensor:
+    """Workspace of sage_attn_fwd_smooth_q: the library's default (sizes.ws_smooth_q), or
+    room for the Delta S rows of `rows` Q blocks per chunk."""
+    nbytes = (sage_buffer_sizes(B, H, H, N, d)["ws_smooth_q"] if rows is None
+              else B * H * rows * N * 4)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def sage_attn_fwd_smooth_q(qk: dict, vq: dict, k: torch.Tensor, *, causal: bool,
+                           sm_scale: float, out_dtype=torch.float16, return_lse: bool = False,
+                           lse_corr=None, workspace=None, out=None, lse=None, stream=None):
+    """Attention of smoothed Q (sage_quant_qk with smooth_q): the Delta S term
+    q_mean . (k - k_mean) is computed a chunk of Q blocks at a time into `workspace`
+    (default: smooth_q_workspace) and added to the scores.  k: the original K.
+    Returns O, or (O, lse) with return_lse."""
+    q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
+    B, H, N, d = q_i8.shape
+    H_kv = k_i8.shape[1]
+    if qk.get("q_mean") is None:
+        raise ValueError("sage_attn_fwd_smooth_q: qk has no q_mean (Q was not smoothed)")
+    _check_tensor("sage_attn_fwd_smooth_q", "q_mean", qk["q_mean"], (B, H, -(-N // BLKQ), d),
+                  torch.float32)
+    _check_tensor("sage_attn_fwd_smooth_q", "k_mean", qk["k_mean"], (B, H_kv, d), torch.float32)
+    if tuple(k.shape) != (B, H_kv, N, d):
+        raise ValueError(f"sage_attn_fwd_smooth_q: k {list(k.shape)} does not match k_i8 "
+                         f"{list(k_i8.shape)}")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q_i8.device)
+    if not return_lse:
+        lse, lse_corr = None, None
+    _check_attn_inputs("sage_attn_fwd_smooth_q", qk, out, v_f8=vq["v_f8"], v_scale=vq["v_scale"])
+    if lse is not None:
+        _check_tensor("sage_attn_fwd_smooth_q", "lse", lse, (B, H, N), torch.float32)
+    if lse_corr is not None:
+        _check_tensor("sage_attn_fwd_smooth_q", "lse_corr", lse_corr, (B, H, N), torch.float32)
+    if workspace is None:
+        workspace = smooth_q_workspace(B, H, N, d, device=q_i8.device)
+    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"], out, k,
+              qk["k_mean"], qk["q_mean"], workspace,
+              *(t for t in (lse, lse_corr) if t is not None))
+    st = load_library().sage_attn_fwd_smooth_q(
+        q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
+        vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), k.data_ptr(), _dt(k.dtype),
+        qk["k_mean"].data_ptr(), qk["q_mean"].data_ptr(), out.data_ptr(), _dt(out.dtype),
+        _ptr(lse), _ptr(lse_corr), B, H, H_kv, N, d, _q_group_of(qk["q_scale"], N),
+        int(bool(causal)), float(sm_scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream, q_i8.device))
+    _check(st, "sage_attn_fwd_smooth_q")
+    return (out, lse) if return_lse else out
 
 
 def sage_lse_correction(q: torch.Tensor, k_mean: torch.Tensor, sm_scale: float, *, out=None,
@@ -533,14 +590,15 @@ def sageattn(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
         return sage_attn_fwd_mxfp4(qk, vq4, causal=is_causal, sm_scale=sm_scale,
                                    out_dtype=q.dtype, return_lse=return_lse, lse_corr=corr)
     qk = sage_quant_qk(q, k, smooth_k, q_group=q_group, smooth_q=smooth_q)
-    ds = sage_delta_s(k, qk, sm_scale) if smooth_q else None
     vq = sage_quant_v(v)
+    corr = sage_lse_correction(q, qk["k_mean"], sm_scale) if return_lse and smooth_k else None
+    if smooth_q:
+        return sage_attn_fwd_smooth_q(qk, vq, k, causal=is_causal, sm_scale=sm_scale,
+                                      out_dtype=q.dtype, return_lse=return_lse, lse_corr=corr)
     if not return_lse:
-        return sage_attn_fwd(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype,
-                             delta_s=ds)
-    corr = sage_lse_correction(q, qk["k_mean"], sm_scale) if smooth_k else None
+        return sage_attn_fwd(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype)
     return sage_attn_fwd_lse(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype,
-                             lse_corr=corr, delta_s=ds)
+                             lse_corr=corr)
 
 
 class SagePlan:
@@ -556,8 +614,8 @@ class SagePlan:
         self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
         sz = sage_buffer_sizes(B, H, H_kv, N, d, q_group)
         self.qk = _alloc_qk(B, H, H_kv, N, d, device, q_group, smooth_q)
-        self.delta_s = (torch.empty((B, H, -(-N // BLKQ), N), dtype=torch.float32, device=device)
-                        if smooth_q else None)
+        self.ws_sq = smooth_q_workspace(B, H, N, d, device=device) if smooth_q else None
+        self.k = None   # the original K of the last quant() (read by attn() for smooth Q)
         self.vq = _alloc_v4(B, H_kv, N, d, device) if pv == "mxfp4" else _alloc_v(B, H_kv, N, d, device)
         self.ws_qk = torch.empty(max(sz["ws_quant_qkv"], 16), dtype=torch.uint8, device=device)
         self.ws_v = torch.empty(max(sz["ws_quant_v"], 16), dtype=torch.uint8, device=device)
@@ -571,8 +629,7 @@ class SagePlan:
         else:
             sage_quant_qkv(q, k, v, True, q_group=self.q_group, smooth_q=self.smooth_q,
                            out_qk=self.qk, out_v=self.vq, workspace=self.ws_qk, stream=stream)
-        if self.smooth_q:
-            sage_delta_s(k, self.qk, self.sm_scale, out=self.delta_s, stream=stream)
+        self.k = k
 
     def quant_v(self, v, stream=None):
         if self.pv == "mxfp4":
@@ -585,9 +642,12 @@ class SagePlan:
             return sage_attn_fwd_mxfp4(self.qk, self.vq, causal=self.causal,
                                        sm_scale=self.sm_scale, out_dtype=self.dtype, out=self.o,
                                        stream=stream)
+        if self.smooth_q:
+            return sage_attn_fwd_smooth_q(self.qk, self.vq, self.k, causal=self.causal,
+                                          sm_scale=self.sm_scale, out_dtype=self.dtype,
+                                          workspace=self.ws_sq, out=self.o, stream=stream)
         return sage_attn_fwd(self.qk, self.vq, causal=self.causal, sm_scale=self.sm_scale,
-                             out_dtype=self.dtype, delta_s=self.delta_s, out=self.o,
-                             stream=stream)
+                             out_dtype=self.dtype, out=self.o, stream=stream)
 
     def __call__(self, q, k, v, stream=None):
         self.quant(q, k, v, stream)

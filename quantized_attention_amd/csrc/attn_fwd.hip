@@ -25,8 +25,9 @@
 
 namespace sage {
 
-// SQ: Q was smoothed by its 128-block means; delta_s holds the Delta S table
-// [B][H][ceil(N/128)][N] (log2 units) that is added to every score.
+// The grid covers q tiles qt0 .. qt0 + nqt - 1 of every (b, h).
+// SQ: Q was smoothed by its 128-block means; delta_s holds the Delta S rows
+// of those q tiles, [B][H][nqt][N] (log2 units), added to every score.
 // PV4: P V on the FP4 matrix cores in MXFP4 (v_f8 holds E2M1 codes, v_e8 the
 // E8M0 scale bytes, see quant_v_mxfp4); P~ is quantized per 32 keys of a row.
 template <int D, bool CAUSAL, bool BF16, bool SQ, bool PV4>
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     const uint8_t* __restrict__ v_e8, const float* __restrict__ delta_s,
     void* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ lse_corr, int H, int H_kv, int N, float lam, int qg_shift,
-    int nqt, int total) {
+    int qt0, int nqt, int total) {
   // Every float32 step of the softmax below is the one the oracle takes (each
   // named quantity rounded once); no multiply may be fused into a following add.
 #pragma clang fp contract(off)
@@ -69,13 +70,13 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     int rest = blockIdx.x;
     const int bk = rest % nbk; rest /= nbk;
     gm = rest % group;
-    qt = nqt - 1 - rest / group;
+    qt = qt0 + nqt - 1 - rest / group;
     b = bk / H_kv;
     hk = bk % H_kv;
   } else {
     int rest = xcd_remap(blockIdx.x, total);
     gm = rest % group; rest /= group;
-    qt = rest % nqt; rest /= nqt;
+    qt = qt0 + rest % nqt; rest /= nqt;
     hk = rest % H_kv;
     b = rest / H_kv;
   }
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
   for (int i = 0; i < KNB; ++i) koff[i] = k_tile_offset<D>(i * kWaves + wave, lane);
   // Delta S row of this workgroup's Q block; waves 0 and 1 stage a tile's
   // 128 values (one float per lane; keys past N read zeros)
-  const rsrc_t rds = make_rsrc(SQ ? delta_s + ((size_t)(b * H + h) * nqt + qt) * N : delta_s,
+  const rsrc_t rds = make_rsrc(SQ ? delta_s + ((size_t)(b * H + h) * nqt + qt - qt0) * N : delta_s,
                                SQ ? (uint32_t)N * 4 : 0u);
   const rsrc_t rvs = make_rsrc(vsh, PV4 ? (uint32_t)ntk * VSBYTES : 0u);
   // K and V codes (and, for MXFP4, the tile's 512 scale bytes; with Delta S
@@ -554,12 +555,13 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                                 const uint8_t* v_e8, const float* delta_s, void* o, int bf16_out,
                                 float* lse, const float* lse_corr, int B, int H, int H_kv, int N,
-                                int d, int q_group, int causal, float sm_scale,
+                                int d, int q_group, int causal, float sm_scale, int qt0, int nqt,
                                 hipStream_t stream) {
   using namespace sage;
   const int qg_shift = q_group == kBlkQ ? 7 : q_group == kWaveQ ? 5 : q_group == 1 ? 0 : -1;
   if (qg_shift < 0) return hipErrorInvalidValue;
-  const int nqt = (N + kBlockQ - 1) / kBlockQ;
+  const int ntq = (N + kBlockQ - 1) / kBlockQ;
+  if (qt0 < 0 || nqt <= 0 || qt0 + nqt > ntq) return hipErrorInvalidValue;
   const long long total = (long long)B * H * nqt;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const float lam = sm_scale * kLog2e;   // the softmax constant in log2 units
@@ -570,7 +572,7 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
   if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB && sq == SS && pv4 == PP) {          \
     hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB, SS, PP>), grid, block, 0, stream, q_i8,       \
                        q_scale, k_i8, k_scale, v_f8, v_scale, v_e8, delta_s, o, lse, lse_corr, H, \
-                       H_kv, N, lam, qg_shift, nqt, (int)total);                              \
+                       H_kv, N, lam, qg_shift, qt0, nqt, (int)total);                         \
     return hipGetLastError();                                                                     \
   }
 #define SAGE_ATTN_CASES(SS, PP)              \

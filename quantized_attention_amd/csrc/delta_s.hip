@@ -15,10 +15,13 @@
 // entry decides scores that the FP8 rounding of P~ turns into codes, so its
 // value must not move with the order of an FP32 sum.
 //
+// A range of Q blocks at a time: the attention of smoothed Q consumes the
+// table in chunks of Q blocks, so its memory is rows x N, never N^2/128.
+//
 // Work split: a workgroup of 4 waves owns 64 keys of one (b, h).  Each wave
 // keeps its 16 keys' smoothed K rows in registers as FP64 (the B operand,
-// d/4 doubles per lane) and walks the ceil(N/128) mean rows 16 at a time
-// (the A operand, read from L2).  Contraction index: MFMA s of a lane in
+// d/4 doubles per lane) and walks the range's mean rows 16 at a time (the
+// A operand, read from L2).  Contraction index: MFMA s of a lane in
 // group g = L/16 uses channel g*d/4 + s for both operands, so the d/4 MFMAs
 // cover every channel, and each lane's channels are contiguous.
 #include <hip/hip_runtime.h>
@@ -35,7 +38,8 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
                                                       const float* __restrict__ k_mean,
                                                       const float* __restrict__ q_mean,
                                                       float* __restrict__ out, int H, int H_kv,
-                                                      int N, int nmb, float sm_log2) {
+                                                      int N, int nmb, int i0, int nrows,
+                                                      float sm_log2) {
   constexpr int QD = D / 4;   // channels per lane group
   const int bh = blockIdx.y, b = bh / H, h = bh % H, hk = h / (H / H_kv);
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
@@ -67,12 +71,13 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
       }
     }
   }
-  const float* qm = q_mean + (size_t)bh * nmb * D;
-  float* ob = out + (size_t)bh * nmb * N;
+  const float* qm = q_mean + ((size_t)bh * nmb + i0) * D;
+  float* ob = out + (size_t)bh * nrows * N;
   const double scale = (double)sm_log2;
-  for (int r0 = 0; r0 < nmb; r0 += 16) {
-    // A operand: mean row r0 + col (rows past nmb read the last row, not stored)
-    const float* qr = qm + (size_t)min(r0 + col, nmb - 1) * D + g * QD;
+  for (int r0 = 0; r0 < nrows; r0 += 16) {
+    // A operand: mean row i0 + r0 + col (rows past the range read its last
+    // row and are not stored)
+    const float* qr = qm + (size_t)min(r0 + col, nrows - 1) * D + g * QD;
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int i = 0; i < QD; i += 4) {
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = r0 + 4 * r + g;
-        if (row < nmb) ob[(size_t)row * N + key] = (float)(acc[r] * scale);
+        if (row < nrows) ob[(size_t)row * N + key] = (float)(acc[r] * scale);
       }
     }
   }
@@ -96,16 +101,17 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
 }  // namespace sage
 
 hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
-                               int B, int H, int H_kv, int N, int d, float sm_scale, float* out,
-                               hipStream_t st) {
+                               int B, int H, int H_kv, int N, int d, float sm_scale, int i0,
+                               int nrows, float* out, hipStream_t st) {
   using namespace sage;
   const int nmb = (N + kBlkQ - 1) / kBlkQ;
+  if (i0 < 0 || nrows <= 0 || i0 + nrows > nmb) return hipErrorInvalidValue;
   const dim3 grid((N + 63) / 64, B * H), block(256);
   const float sm_log2 = sm_scale * kLog2e;
 #define SAGE_DS(DD, BB)                                                                         \
   if (d == DD && (bf16 != 0) == BB) {                                                           \
     hipLaunchKernelGGL((delta_s_kernel<DD, BB>), grid, block, 0, st, k, k_mean, q_mean, out, H, \
-                       H_kv, N, nmb, sm_log2);                                                  \
+                       H_kv, N, nmb, i0, nrows, sm_log2);                                       \
     return hipGetLastError();                                                                   \
   }
   SAGE_DS(64, false)

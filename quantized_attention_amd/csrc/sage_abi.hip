@@ -18,15 +18,15 @@ hipError_t sage_launch_quant(const void* q, const void* k, const void* v, int bf
                              float* k_mean, float* q_mean, uint8_t* v_f8, float* v_scale, void* ws,
                              hipStream_t st);
 hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
-                               int B, int H, int H_kv, int N, int d, float sm_scale, float* out,
-                               hipStream_t st);
+                               int B, int H, int H_kv, int N, int d, float sm_scale, int i0,
+                               int nrows, float* out, hipStream_t st);
 hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, int d,
                                uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st);
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                                 const uint8_t* v_e8, const float* delta_s, void* o, int bf16_out,
                                 float* lse, const float* lse_corr, int B, int H, int H_kv, int N,
-                                int d, int q_group, int causal, float sm_scale,
+                                int d, int q_group, int causal, float sm_scale, int qt0, int nqt,
                                 hipStream_t stream);
 hipError_t sage_launch_quant_v_mxfp4(const void* v, int bf16, int B, int H_kv, int N, int d,
                                      uint8_t* v_f4, uint8_t* v_e8, hipStream_t st);
@@ -53,9 +53,18 @@ sage_status check_shape(int B, int H, int H_kv, int N, int d) {
   return SAGE_OK;
 }
 
-// elements of the Delta S table, B*H*ceil(N/128)*N
-int64_t delta_s_elems(int B, int H, int N) {
-  return (int64_t)B * H * (((int64_t)N + SAGE_BLKQ - 1) / SAGE_BLKQ) * N;
+int64_t q_blocks(int N) { return ((int64_t)N + SAGE_BLKQ - 1) / SAGE_BLKQ; }
+
+// Q blocks per chunk of sage_attn_fwd_smooth_q's default workspace: enough
+// for 2048 attention workgroups per launch, at least 32 rows per Delta S
+// pass (each pass reads all of K once), a multiple of 16 (the pass's row
+// group), at most the number of Q blocks.
+int64_t smooth_q_default_rows(int B, int H, int N) {
+  const int64_t bh = (int64_t)B * H;
+  int64_t r = (2048 + bh - 1) / bh;
+  r = (r + 15) / 16 * 16;
+  if (r < 32) r = 32;
+  return r < q_blocks(N) ? r : q_blocks(N);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -111,7 +120,7 @@ sage_status sage_buffer_sizes(int B, int H, int H_kv, int N, int d, int q_group,
   out->ws_quant_qkv = out->ws_quant_qk + out->ws_quant_v;
   const size_t nmb = (n + SAGE_BLKQ - 1) / SAGE_BLKQ;
   out->q_mean = b * h * nmb * dd * sizeof(float);
-  out->delta_s = (size_t)delta_s_elems(B, H, N) * sizeof(float);
+  out->ws_smooth_q = (size_t)((int64_t)B * H * smooth_q_default_rows(B, H, N) * N) * sizeof(float);
   out->v_f4 = b * hk * npad * dd / 2;
   out->v_e8 = b * hk * (npad / SAGE_KV_TILE) * 512;
   return SAGE_OK;
@@ -166,16 +175,17 @@ sage_status sage_quant_qkv(const void* q, const void* k, const void* v, sage_dty
 
 sage_status sage_delta_s(const void* k, sage_dtype dtype, const float* k_mean,
                          const float* q_mean, int B, int H, int H_kv, int N, int d,
-                         float sm_scale, float* delta_s, void* stream) {
+                         float sm_scale, int i0, int nrows, float* delta_s, void* stream) {
   if (!k || !k_mean || !q_mean || !delta_s) return SAGE_ERR_NULL;
   sage_status st = check_shape(B, H, H_kv, N, d);
   if (st != SAGE_OK) return st;
   if (dtype != SAGE_FP16 && dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
-  if (delta_s_elems(B, H, N) > kMaxElems) return SAGE_ERR_SHAPE;
+  if (i0 < 0 || nrows < 1 || (int64_t)i0 + nrows > q_blocks(N)) return SAGE_ERR_ARG;
+  if ((int64_t)B * H * nrows * N > kMaxElems) return SAGE_ERR_SHAPE;
   if (!aligned16(k) || !aligned16(q_mean) || !aligned16(delta_s)) return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_delta_s(k, dtype == SAGE_BF16, k_mean, q_mean, B, H, H_kv, N, d,
-                                      sm_scale, delta_s, (hipStream_t)stream));
+                                      sm_scale, i0, nrows, delta_s, (hipStream_t)stream));
 }
 
 sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N, int d,
@@ -194,9 +204,8 @@ sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N
 
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                           const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                          const float* delta_s, void* o, sage_dtype out_dtype, int B, int H,
-                          int H_kv, int N, int d, int q_group, int causal, float sm_scale,
-                          void* stream) {
+                          void* o, sage_dtype out_dtype, int B, int H, int H_kv, int N, int d,
+                          int q_group, int causal, float sm_scale, void* stream) {
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8 || !v_scale || !o) return SAGE_ERR_NULL;
   sage_status st = check_shape(B, H, H_kv, N, d);
   if (st != SAGE_OK) return st;
@@ -206,17 +215,15 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
     return SAGE_ERR_ALIGN;
-  if (delta_s && !aligned16(delta_s)) return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr,
-                                       delta_s, o, out_dtype == SAGE_BF16, nullptr, nullptr, B, H,
-                                       H_kv, N,
-                                       d, q_group, causal, sm_scale, (hipStream_t)stream));
+                                       nullptr, o, out_dtype == SAGE_BF16, nullptr, nullptr, B, H,
+                                       H_kv, N, d, q_group, causal, sm_scale, 0,
+                                       (int)q_blocks(N), (hipStream_t)stream));
 }
 
 sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                               const float* k_scale, const uint8_t* v_f8, const float* v_scale,
-                              const float* delta_s, void* o, sage_dtype out_dtype, float* lse,
-                              const float* lse_corr,
+                              void* o, sage_dtype out_dtype, float* lse, const float* lse_corr,
                               int B, int H, int H_kv, int N, int d, int q_group, int causal,
                               float sm_scale, void* stream) {
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8 || !v_scale || !o || !lse)
@@ -229,11 +236,55 @@ sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const in
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o))
     return SAGE_ERR_ALIGN;
-  if (delta_s && !aligned16(delta_s)) return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr,
-                                       delta_s, o, out_dtype == SAGE_BF16, lse, lse_corr, B, H,
-                                       H_kv, N, d,
-                                       q_group, causal, sm_scale, (hipStream_t)stream));
+                                       nullptr, o, out_dtype == SAGE_BF16, lse, lse_corr, B, H,
+                                       H_kv, N, d, q_group, causal, sm_scale, 0,
+                                       (int)q_blocks(N), (hipStream_t)stream));
+}
+
+sage_status sage_attn_fwd_smooth_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                   const float* k_scale, const uint8_t* v_f8,
+                                   const float* v_scale, const void* k, sage_dtype k_dtype,
+                                   const float* k_mean, const float* q_mean, void* o,
+                                   sage_dtype out_dtype, float* lse, const float* lse_corr,
+                                   int B, int H, int H_kv, int N, int d, int q_group, int causal,
+                                   float sm_scale, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8 || !v_scale || !k || !k_mean || !q_mean ||
+      !o)
+    return SAGE_ERR_NULL;
+  sage_status st = check_shape(B, H, H_kv, N, d);
+  if (st != SAGE_OK) return st;
+  if (k_dtype != SAGE_FP16 && k_dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (out_dtype != SAGE_FP16 && out_dtype != SAGE_BF16) return SAGE_ERR_DTYPE;
+  if (!valid_q_group(q_group)) return SAGE_ERR_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_ARG;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SAGE_ERR_ARG;
+  if (lse_corr && !lse) return SAGE_ERR_ARG;
+  if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o) ||
+      !aligned16(k) || !aligned16(q_mean))
+    return SAGE_ERR_ALIGN;
+  // Q blocks per chunk: as many Delta S rows as the workspace holds
+  const int64_t nmb = q_blocks(N), row_bytes = (int64_t)B * H * N * (int64_t)sizeof(float);
+  if (!workspace || (int64_t)(ws_bytes / (size_t)row_bytes) < 1) return SAGE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SAGE_ERR_ALIGN;
+  int64_t rows = (int64_t)(ws_bytes / (size_t)row_bytes);
+  if (rows >= nmb) rows = nmb;
+  else if (rows > 16) rows -= rows % 16;
+  if ((int64_t)B * H * rows * N > kMaxElems) return SAGE_ERR_SHAPE;
+  float* ds = static_cast<float*>(workspace);
+  const hipStream_t hs = (hipStream_t)stream;
+  for (int64_t i0 = 0; i0 < nmb; i0 += rows) {
+    const int n = (int)(nmb - i0 < rows ? nmb - i0 : rows);
+    hipError_t e = sage_launch_delta_s(k, k_dtype == SAGE_BF16, k_mean, q_mean, B, H, H_kv, N, d,
+                                       sm_scale, (int)i0, n, ds, hs);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+    e = sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr, ds, o,
+                             out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d, q_group,
+                             causal, sm_scale, (int)i0, n, hs);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+  }
+  return SAGE_OK;
 }
 
 sage_status sage_quant_v_mxfp4(const void* v, sage_dtype dtype, int B, int H_kv, int N, int d,
@@ -264,7 +315,8 @@ sage_status sage_attn_fwd_mxfp4(const int8_t* q_i8, const float* q_scale, const 
     return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f4, nullptr, v_e8, nullptr,
                                        o, out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d,
-                                       q_group, causal, sm_scale, (hipStream_t)stream));
+                                       q_group, causal, sm_scale, 0, (int)q_blocks(N),
+                                       (hipStream_t)stream));
 }
 
 sage_status sage_lse_correction(const void* q, sage_dtype dtype, const float* k_mean, int B, int H,

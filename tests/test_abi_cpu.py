@@ -27,10 +27,11 @@ def test_library_exports_every_declared_symbol():
     assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attn_fwd_lse",
             "sage_lse_correction", "sage_buffer_sizes", "sage_qk_int32", "sage_status_str",
             "sage_delta_s", "sage_quant_v_mxfp4", "sage_attn_fwd_mxfp4",
-            "sage_abi_version", "sage_quant_qk_noalloc", "sage_quant_qkv"} <= set(names)
+            "sage_abi_version", "sage_quant_qk_noalloc", "sage_quant_qkv",
+            "sage_attn_fwd_smooth_q"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sage_abi_version() == 7
+    assert lib.sage_abi_version() == 8
 
 
 def test_status_strings():
@@ -56,9 +57,28 @@ def test_buffer_sizes(B, H, H_kv, N, d, q_group):
     assert s["ws_quant_v"] == 4 * B * H_kv * math.ceil(N / 256) * d
     assert s["ws_quant_qkv"] == s["ws_quant_qk"] + s["ws_quant_v"]
     assert s["q_mean"] == 4 * B * H * math.ceil(N / 128) * d
-    assert s["delta_s"] == 4 * B * H * math.ceil(N / 128) * N
+    assert s["ws_smooth_q"] == 4 * B * H * _smooth_q_rows(B * H, N) * N
     assert s["v_f4"] == B * H_kv * math.ceil(N / 128) * 64 * d
     assert s["v_e8"] == B * H_kv * math.ceil(N / 128) * 512
+
+
+def _smooth_q_rows(bh, N):
+    """Default Q blocks per chunk of sage_attn_fwd_smooth_q (the rule sage.h states)."""
+    r = max(32, 16 * math.ceil(math.ceil(2048 / bh) / 16))
+    return min(math.ceil(N / 128), r)
+
+
+def test_smooth_q_workspace_is_linear_in_n():
+    """The default smooth-Q workspace holds a bounded number of Delta S rows: it grows
+    linearly with N (the whole table, B*H*ceil(N/128)*N floats, grows as N^2)."""
+    per_n = set()
+    for N in (1 << 16, 1 << 18, 1 << 20):
+        s = qa.sage_buffer_sizes(1, 32, 8, N, 128)
+        per_n.add(s["ws_smooth_q"] / N)
+        assert s["ws_smooth_q"] * 8 <= 4 * 32 * math.ceil(N / 128) * N
+    assert len(per_n) == 1
+    # sequence sweep at N = 32K: 128 heads x 32 rows x 32768 keys (512 MiB, not 4 GiB)
+    assert qa.sage_buffer_sizes(4, 32, 32, 32768, 128)["ws_smooth_q"] == 4 * 128 * 32 * 32768
 
 
 @pytest.mark.parametrize("args,code", [
@@ -89,7 +109,7 @@ def _v(lib, **kw):
 
 
 def _attn(lib, **kw):
-    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, ds=None,
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE,
              o=FAKE, dt=0, B=1, H=2, H_kv=2, N=256, d=64, qg=128, causal=0, sm_scale=0.125,
              stream=None)
     a.update(kw)
@@ -97,11 +117,20 @@ def _attn(lib, **kw):
 
 
 def _attn_lse(lib, **kw):
-    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, ds=None,
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE,
              o=FAKE, dt=0, lse=FAKE, corr=None, B=1, H=2, H_kv=2, N=256, d=64, qg=128, causal=0,
              sm_scale=0.125, stream=None)
     a.update(kw)
     return lib.sage_attn_fwd_lse(*a.values())
+
+
+def _attn_sq(lib, **kw):
+    a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, k=FAKE,
+             k_dt=0, k_mean=FAKE, q_mean=FAKE, o=FAKE, dt=0, lse=None, corr=None, B=1, H=2,
+             H_kv=2, N=256, d=64, qg=128, causal=0, sm_scale=0.125, ws=FAKE,
+             ws_bytes=2 * 256 * 4, stream=None)
+    a.update(kw)
+    return lib.sage_attn_fwd_smooth_q(*a.values())
 
 
 def _lse_corr(lib, **kw):
@@ -113,7 +142,7 @@ def _lse_corr(lib, **kw):
 
 def _ds(lib, **kw):
     a = dict(k=FAKE, dt=0, k_mean=FAKE, q_mean=FAKE, B=1, H=2, H_kv=2, N=256, d=64,
-             sm_scale=0.125, out=FAKE, stream=None)
+             sm_scale=0.125, i0=0, nrows=2, out=FAKE, stream=None)
     a.update(kw)
     return lib.sage_delta_s(*a.values())
 
@@ -183,7 +212,7 @@ def test_quant_v_rejects(kw, code):
     (dict(o=None), 1), (dict(v_scale=None), 1), (dict(H_kv=0), 2), (dict(d=16), 3),
     (dict(H=4, H_kv=3), 4), (dict(dt=7), 5), (dict(causal=3), 6), (dict(sm_scale=0.0), 6),
     (dict(sm_scale=-1.0), 6), (dict(sm_scale=float("inf")), 6), (dict(sm_scale=float("nan")), 6),
-    (dict(o=FAKE + 2), 9), (dict(qg=16), 6), (dict(qg=-1), 6), (dict(ds=FAKE + 4), 9),
+    (dict(o=FAKE + 2), 9), (dict(qg=16), 6), (dict(qg=-1), 6), (dict(v_f8=FAKE + 4), 9),
 ])
 def test_attn_fwd_rejects(kw, code):
     assert _attn(qa.load_library(), **kw) == code
@@ -211,10 +240,22 @@ def test_lse_correction_rejects(kw, code):
     (dict(k=None), 1), (dict(k_mean=None), 1), (dict(q_mean=None), 1), (dict(out=None), 1),
     (dict(B=0), 2), (dict(d=96), 3), (dict(H=3), 4), (dict(dt=4), 5), (dict(sm_scale=0.0), 6),
     (dict(sm_scale=float("inf")), 6), (dict(q_mean=FAKE + 8), 9), (dict(out=FAKE + 4), 9),
-    (dict(B=8, H=512, H_kv=512, N=1 << 20), 2),
+    (dict(B=8, H=512, H_kv=512, N=1 << 20, nrows=1024), 2), (dict(i0=-1), 6), (dict(nrows=0), 6),
+    (dict(i0=1, nrows=2), 6), (dict(nrows=3), 6),
 ])
 def test_delta_s_rejects(kw, code):
     assert _ds(qa.load_library(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_i8=None), 1), (dict(k=None), 1), (dict(k_mean=None), 1), (dict(q_mean=None), 1),
+    (dict(o=None), 1), (dict(N=0), 2), (dict(d=96), 3), (dict(H=3), 4), (dict(k_dt=2), 5),
+    (dict(dt=7), 5), (dict(qg=64), 6), (dict(causal=2), 6), (dict(sm_scale=0.0), 6),
+    (dict(corr=FAKE), 6), (dict(k=FAKE + 2), 9), (dict(q_mean=FAKE + 4), 9),
+    (dict(ws=None), 7), (dict(ws_bytes=2 * 256 * 4 - 1), 7), (dict(ws=FAKE + 8), 9),
+])
+def test_attn_fwd_smooth_q_rejects(kw, code):
+    assert _attn_sq(qa.load_library(), **kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [

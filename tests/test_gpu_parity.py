@@ -397,6 +397,8 @@ def _biased_q_inputs(B, H, H_kv, N, d, dtype, seed, qbias=1.5):
 
 
 def _check_smooth_q(qa, q, k, v, sm, q_group=128, smooth_k=True):
+    """Quantize with smooth Q on the GPU; check the codes, scales and means bit-exact and
+    every Delta S row within its bound.  Returns the GPU buffers and the oracle's."""
     qk = qa.sage_quant_qk(q.to(DEV), k.to(DEV), smooth_k, q_group=q_group, smooth_q=True)
     ds = qa.sage_delta_s(k.to(DEV), qk, sm)
     vq = qa.sage_quant_v(v.to(DEV))
@@ -430,7 +432,8 @@ def test_smooth_q_parity(gpu_lib, B, H, H_kv, N, d, dtype, causal, q_group):
     q, k, v = _biased_q_inputs(B, H, H_kv, N, d, dtype, seed=N * 11 + d + q_group)
     sm = 1 / math.sqrt(d)
     qk, vq, ds, ref, refv, ds_ref = _check_smooth_q(gpu_lib, q, k, v, sm, q_group)
-    o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=sm, out_dtype=dtype, delta_s=ds)
+    o = gpu_lib.sage_attn_fwd_smooth_q(qk, vq, k.to(DEV), causal=causal, sm_scale=sm,
+                                       out_dtype=dtype)
     torch.cuda.synchronize()
     o_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"], refv["v_f8"],
                          refv["v_scale"], causal=causal, sm_scale=sm, blkq=q_group,
@@ -453,8 +456,8 @@ def test_smooth_q_parity_over_seeds(gpu_lib, B, H, H_kv, N, d, dtype, causal):
               f"seed {seed}", flush=True)
         q, k, v = _biased_q_inputs(B, H, H_kv, N, d, dtype, seed=seed)
         qk, vq, ds, ref, refv, ds_ref = _check_smooth_q(gpu_lib, q, k, v, sm)
-        o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=sm, out_dtype=dtype,
-                                  delta_s=ds)
+        o = gpu_lib.sage_attn_fwd_smooth_q(qk, vq, k.to(DEV), causal=causal, sm_scale=sm,
+                                           out_dtype=dtype)
         torch.cuda.synchronize()
         compare_output(o, O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
                                        refv["v_f8"], refv["v_scale"], causal=causal, sm_scale=sm,
@@ -465,8 +468,8 @@ def test_smooth_q_without_smooth_k(gpu_lib):
     q, k, v = _biased_q_inputs(1, 2, 2, 300, 64, torch.float16, seed=51)
     qk, vq, ds, ref, refv, ds_ref = _check_smooth_q(gpu_lib, q, k, v, 0.125, smooth_k=False)
     assert (to_np(qk["k_mean"]) == 0).all()
-    o = gpu_lib.sage_attn_fwd(qk, vq, causal=False, sm_scale=0.125, out_dtype=torch.float16,
-                              delta_s=ds)
+    o = gpu_lib.sage_attn_fwd_smooth_q(qk, vq, k.to(DEV), causal=False, sm_scale=0.125,
+                                       out_dtype=torch.float16)
     torch.cuda.synchronize()
     compare_output(o, O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
                                    refv["v_f8"], refv["v_scale"], causal=False, sm_scale=0.125,
@@ -477,10 +480,10 @@ def test_smooth_q_lse(gpu_lib):
     q, k, v = _biased_q_inputs(1, 4, 2, 300, 128, torch.bfloat16, seed=52)
     sm = 1 / math.sqrt(128)
     qk, vq, ds, ref, refv, ds_ref = _check_smooth_q(gpu_lib, q, k, v, sm)
-    o0 = gpu_lib.sage_attn_fwd(qk, vq, causal=True, sm_scale=sm, out_dtype=torch.bfloat16,
-                               delta_s=ds)
-    o1, lse = gpu_lib.sage_attn_fwd_lse(qk, vq, causal=True, sm_scale=sm,
-                                        out_dtype=torch.bfloat16, delta_s=ds)
+    o0 = gpu_lib.sage_attn_fwd_smooth_q(qk, vq, k.to(DEV), causal=True, sm_scale=sm,
+                                        out_dtype=torch.bfloat16)
+    o1, lse = gpu_lib.sage_attn_fwd_smooth_q(qk, vq, k.to(DEV), causal=True, sm_scale=sm,
+                                             out_dtype=torch.bfloat16, return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(o0, o1)
     _, l_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"],
@@ -493,6 +496,58 @@ def test_smooth_q_lse(gpu_lib):
     ds_err = (128 + 4) * 2.0 ** -24 * sm * absb.max(axis=(2, 3))[..., None]
     err = np.abs(to_np(lse).astype(np.float64) - l_ref)
     assert np.all(err <= lse_tol(300, l_ref) + ds_err), err.max()
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", [
+    (1, 4, 2, 1000, 64, torch.float16, True),
+    (2, 2, 1, 2200, 128, torch.bfloat16, False),
+])
+def test_smooth_q_chunks_do_not_change_the_result(gpu_lib, B, H, H_kv, N, d, dtype, causal):
+    """sage_attn_fwd_smooth_q computes the Delta S rows a chunk of Q blocks at a time in
+    its workspace.  Every chunk size (one block, a ragged 3, 16, the default, a workspace
+    larger than the whole table) gives the same output and LSE bit for bit, and the
+    workspace's previous contents do not matter."""
+    print(f"smooth_q chunks case B{B} H{H}/{H_kv} N{N} d{d} {dtype} causal={causal}",
+          flush=True)
+    q, k, v = _biased_q_inputs(B, H, H_kv, N, d, dtype, seed=N + d)
+    sm = 1 / math.sqrt(d)
+    qk = gpu_lib.sage_quant_qk(q.to(DEV), k.to(DEV), True, smooth_q=True)
+    vq = gpu_lib.sage_quant_v(v.to(DEV))
+    kd = k.to(DEV)
+    nmb = -(-N // 128)
+    runs = {}
+    for rows in (None, 1, 3, 16, nmb + 5):
+        ws = gpu_lib.smooth_q_workspace(B, H, N, d, rows=rows, device=DEV)
+        ws.fill_(0xFF)   # NaN bit patterns: a row the kernel read before writing would show
+        runs[rows] = gpu_lib.sage_attn_fwd_smooth_q(qk, vq, kd, causal=causal, sm_scale=sm,
+                                                    out_dtype=dtype, return_lse=True,
+                                                    workspace=ws)
+    torch.cuda.synchronize()
+    o0, l0 = runs[None]
+    assert torch.isfinite(o0).all() and torch.isfinite(l0).all()
+    for rows, (o, lse) in runs.items():
+        assert torch.equal(o, o0), rows
+        assert torch.equal(lse, l0), rows
+    # and the result is the oracle's (sampled rows)
+    ref = O.quantize_qk(q, k, smooth_q=True)
+    refv = O.quantize_v(v)
+    rws = np.array([0, 1, 127, 128, N // 2, N - 1])
+    o_ref = O.attn_quant(ref["q_i8"], ref["q_scale"], ref["k_i8"], ref["k_scale"], refv["v_f8"],
+                         refv["v_scale"], causal=causal, sm_scale=sm, rows=rws,
+                         delta_s=O.delta_s(ref["q_mean"], k, ref["k_mean"]))
+    compare_output(o0[:, :, torch.from_numpy(rws).to(DEV)], o_ref)
+
+
+def test_delta_s_row_ranges(gpu_lib):
+    """sage_delta_s over a range of Q blocks writes exactly those rows of the whole table."""
+    q, k, v = _biased_q_inputs(1, 3, 1, 1100, 64, torch.float16, seed=77)
+    qk = gpu_lib.sage_quant_qk(q.to(DEV), k.to(DEV), True, smooth_q=True)
+    kd = k.to(DEV)
+    full = gpu_lib.sage_delta_s(kd, qk, 0.125)
+    for i0, n in ((0, 1), (2, 3), (8, 1), (0, 9), (5, 4)):
+        part = gpu_lib.sage_delta_s(kd, qk, 0.125, i0=i0, nrows=n)
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[:, :, i0:i0 + n]), (i0, n)
 
 
 def test_smooth_q_tracks_exact_attention(gpu_lib):
@@ -637,13 +692,17 @@ def _workload_check(gpu_lib, name, heads, nrows, seed=0, q_group=128, smooth_q=F
     qsel_i8 = ref["q_i8"]
     kv_index = [hk_set.index((b, h // (w.H // w.H_kv))) for b, h in heads]
     o_ref = np.zeros((len(heads), len(rows), w.d))
+    if smooth_q:
+        # Delta S rows of two Q blocks (the attention computes its own, chunk by chunk)
+        i0 = (-(-w.N // 128)) // 2
+        ds_rows = to_np(gpu_lib.sage_delta_s(kd, plan.qk, w.sm_scale, i0=i0, nrows=2))
     for j, (b, h) in enumerate(heads):
         kvj = kv_index[j]
         ds = None
         if smooth_q:
             ds = O.delta_s(ref["q_mean"][:, j:j + 1], ksel[:, kvj:kvj + 1],
                            ref["k_mean"][:, kvj:kvj + 1])
-            _check_delta_s_table(to_np(plan.delta_s[b, h]), ds[0, 0], ref["q_mean"][0, j],
+            _check_delta_s_table(ds_rows[b, h], ds[0, 0, i0:i0 + 2], ref["q_mean"][0, j],
                                  ksel[0, kvj].float().numpy(), ref["k_mean"][0, kvj], w.sm_scale)
         o1 = O.attn_quant(qsel_i8[:, j:j + 1], ref["q_scale"][:, j:j + 1],
                           ref["k_i8"][:, kvj:kvj + 1], ref["k_scale"][:, kvj:kvj + 1],
