@@ -48,7 +48,7 @@ def _dtype_name(t) -> str:
 
 def compare_output(o_gpu: torch.Tensor, o_ref: np.ndarray, max_abs=2e-2, cos_min=0.9995):
     """The HIP output against the oracle's float64 result rounded once to the
-    output dtype (as the kernel rounds its own), at the benchmark spec bar."""
+    output dtype (as the kernel rounds its own): max-abs <= 2e-2 and cosine >= 0.9995."""
     a = o_gpu.detach().float().cpu().numpy().astype(np.float64)
     ref = O.round_output(np.asarray(o_ref, dtype=np.float64), _dtype_name(o_gpu))
     m = O.metrics(a, ref)

@@ -111,7 +111,7 @@ def test_q_group_parity(gpu_lib, B, H, H_kv, N, d, dtype, causal, q_group):
     compare_output(o, _oracle_o(ref, refv, causal, sm, q_group=q_group))
 
 
-def test_q_group_token_scales_mixed_exponent_forms(gpu_lib):
+def test_q_group_token_scales_of_very_different_size(gpu_lib):
     """Per-query scales where one query of a wave is 3000 times the others: its scale,
     score factors and running max differ by that much from its neighbours'."""
     q, k, v = _rand_inputs(1, 2, 2, 384, 128, torch.float16, seed=23)
@@ -589,7 +589,7 @@ MX_CASES = [SMALL[i] for i in (0, 1, 3, 5, 9, 10)]
 @pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", MX_CASES)
 def test_mxfp4_parity(gpu_lib, B, H, H_kv, N, d, dtype, causal):
     """MXFP4 P V: V codes and E8M0 exponents bit-exact; the output against the oracle's
-    MXFP4 recursion at the benchmark spec bar."""
+    MXFP4 recursion within max-abs 2e-2 and cosine 0.9995."""
     print(f"mxfp4 case B{B} H{H}/{H_kv} N{N} d{d} {dtype} causal={causal}", flush=True)
     q, k, v = _rand_inputs(B, H, H_kv, N, d, dtype, seed=N * 13 + d)
     qk = gpu_lib.sage_quant_qk(q.to(DEV), k.to(DEV))
