@@ -297,12 +297,17 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     l_part *= alpha;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    // O is rescaled (when some row's max moved) just before the first P V
+    // MFMA, so the max chain above, the conversions and the first
+    // exponentials form one block the scheduler can interleave.
+    auto rescale_o = [&]() __attribute__((always_inline)) {
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-      for (int c = 0; c < NKC; ++c)
+        for (int c = 0; c < NKC; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[c][r] *= alpha;
-    }
+          for (int r = 0; r < 16; ++r) acc_o[c][r] *= alpha;
+      }
+    };
 
     // ---- P~ = 2^(x - m) with x = S * c (S the exact int32 sum, converted to
     // float exactly: |S| < 2^22), each step rounded once; l sums P~ unquantized;
@@ -318,7 +323,6 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
       return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
     i32x8 va = vfrag(0), vb = vfrag(1);
-    __builtin_amdgcn_sched_barrier(0);
     // P~ of elements r0 .. r0+NE-1 of 32-key block kb into its FP8 slots.
     auto exp_part = [&](int kb, int r0, auto ne_tag) __attribute__((always_inline)) {
       constexpr int NE = decltype(ne_tag)::value;
@@ -362,6 +366,8 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
       {
         exp_part(0, 0, E16{});
         exp_part(1, 0, E16{});
+        pin(pf[0]);
+        rescale_o();
         __builtin_amdgcn_sched_barrier(0);
         prio_mfma();
 
@@ -427,6 +433,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
           pk4[kb][w] = pk;
         }
       }
+      rescale_o();
       prio_mfma();
       // ---- O^T += V^T P^T on the FP4 matrix cores, 64 keys per MFMA: after
       // exchanging lane halves, half g holds all 32 keys of block 2h + g
