@@ -422,8 +422,8 @@ def sage_attn_fwd(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_i8.device)
     _check_attn_inputs("sage_attn_fwd", qk, out, v_f8=vq["v_f8"], v_scale=vq["v_scale"])
-    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"], out)
     _no_q_mean("sage_attn_fwd", qk)
+    _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"], out)
     st = load_library().sage_attn_fwd(
         q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
         vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
@@ -468,12 +468,12 @@ def sage_attn_fwd_lse(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q_i8.device)
     _check_attn_inputs("sage_attn_fwd_lse", qk, out, v_f8=vq["v_f8"], v_scale=vq["v_scale"])
     _check_tensor("sage_attn_fwd_lse", "lse", lse, (B, H, N), torch.float32)
+    _no_q_mean("sage_attn_fwd_lse", qk)
     _need_gpu(q_i8, qk["q_scale"], k_i8, qk["k_scale"], vq["v_f8"], vq["v_scale"], out, lse)
     if lse_corr is not None:
         _need_gpu(lse_corr)
         if lse_corr.shape != (B, H, N) or lse_corr.dtype != torch.float32:
             raise ValueError("lse_corr must be float32 [B, H, N]")
-    _no_q_mean("sage_attn_fwd_lse", qk)
     st = load_library().sage_attn_fwd_lse(
         q_i8.data_ptr(), qk["q_scale"].data_ptr(), k_i8.data_ptr(), qk["k_scale"].data_ptr(),
         vq["v_f8"].data_ptr(), vq["v_scale"].data_ptr(), out.data_ptr(), _dt(out.dtype),
@@ -643,6 +643,8 @@ class SagePlan:
                                        sm_scale=self.sm_scale, out_dtype=self.dtype, out=self.o,
                                        stream=stream)
         if self.smooth_q:
+            if self.k is None:
+                raise RuntimeError("SagePlan.attn: smooth Q needs the original K; call quant() first")
             return sage_attn_fwd_smooth_q(self.qk, self.vq, self.k, causal=self.causal,
                                           sm_scale=self.sm_scale, out_dtype=self.dtype,
                                           workspace=self.ws_sq, out=self.o, stream=stream)

@@ -376,3 +376,22 @@ def test_quant_qkv_rejects(kw, code):
     """The one-call quantization validates like sage_quant_qk and sage_quant_v together
     (its workspace holds both scratch areas: 1024 + 512 bytes at these shapes)."""
     assert _qkv(qa.load_library(), **kw) == code
+
+
+def test_smooth_q_entry_points_refuse_the_wrong_codes():
+    """Codes of smoothed Q need the Delta S term: the plain attention entry points refuse
+    them and the smooth-Q one refuses plain codes (on the host, before any launch)."""
+    import torch
+    qk_sq = qa._alloc_qk(1, 2, 2, 256, 64, "cpu", smooth_q=True)
+    qk = qa._alloc_qk(1, 2, 2, 256, 64, "cpu")
+    vq = qa._alloc_v(1, 2, 256, 64, "cpu")
+    k = torch.zeros(1, 2, 256, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="smooth_q"):
+        qa.sage_attn_fwd(qk_sq, vq, causal=False, sm_scale=0.125)
+    with pytest.raises(ValueError, match="smooth_q"):
+        qa.sage_attn_fwd_lse(qk_sq, vq, causal=False, sm_scale=0.125)
+    with pytest.raises(ValueError, match="q_mean"):
+        qa.sage_attn_fwd_smooth_q(qk, vq, k, causal=False, sm_scale=0.125)
+    plan = qa.SagePlan(1, 2, 2, 256, 64, torch.float16, False, device="cpu", smooth_q=True)
+    with pytest.raises(RuntimeError, match="quant"):
+        plan.attn()
