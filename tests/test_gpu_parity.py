@@ -419,7 +419,7 @@ def _check_smooth_q(qa, q, k, v, sm, q_group=128, smooth_k=True):
     return qk, vq, ds, ref, refv, ds_ref
 
 
-SQ_CASES = [SMALL[i] for i in (1, 2, 3, 5, 9, 10)]
+SQ_CASES = [SMALL[i] for i in (1, 2, 3, 4, 5, 9, 10)]
 
 
 @pytest.mark.parametrize("q_group", [128, 1])
