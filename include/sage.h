@@ -39,6 +39,9 @@
  *     head h / (H / H_kv) (GQA: H must be a multiple of H_kv).
  *   - d must be 64 or 128 (the pages' kernels cover head dims 64 and 128 and
  *     reject d > 128).  Inputs are fp16 or bf16 (the pages accept only these).
+ *   - Size limits (else SAGE_ERR_SHAPE): B*H <= 65535; B*H*N*d < 2^40; and
+ *     N rounded up to 128, times d, below 2^32 (one head's codes are
+ *     addressed with 32-bit buffer ranges): N < 2^25 at d = 128.
  *   - Non-finite inputs are outside the method's domain (the pages do not
  *     treat NaN/Inf); results for them are unspecified.
  */

@@ -47,9 +47,12 @@ sage_status check_shape(int B, int H, int H_kv, int N, int d) {
   if (d != 64 && d != 128) return SAGE_ERR_HEADDIM;
   if (H % H_kv != 0) return SAGE_ERR_GQA;
   // every tensor must be indexable: B*H*N*d (and the padded V) below 2^40;
-  // B*H is a grid y-dimension (at most 65535)
+  // B*H is a grid y-dimension (at most 65535); one head's K, V codes (and a
+  // Delta S row, 4*N bytes) are read through 32-bit buffer-resource ranges,
+  // so the padded N*d must stay below 2^32
   const int64_t npad = ((int64_t)N + SAGE_KV_TILE - 1) / SAGE_KV_TILE * SAGE_KV_TILE;
   if ((int64_t)B * H > 65535 || (int64_t)B * H * npad * d > kMaxElems) return SAGE_ERR_SHAPE;
+  if (npad * d >= ((int64_t)1 << 32)) return SAGE_ERR_SHAPE;
   return SAGE_OK;
 }
 

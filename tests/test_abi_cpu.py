@@ -68,6 +68,15 @@ def _smooth_q_rows(bh, N):
     return min(math.ceil(N / 128), r)
 
 
+def test_largest_head_fits_32_bit_buffer_ranges():
+    """One head's K codes are read through a 32-bit buffer range: N*d just below 2^32
+    is accepted, the next 128 keys are not."""
+    n = (1 << 25) - 128
+    assert qa.sage_buffer_sizes(1, 1, 1, n, 128)["k_i8"] == n * 128
+    with pytest.raises(qa.SageError):
+        qa.sage_buffer_sizes(1, 1, 1, n + 1, 128)
+
+
 def test_smooth_q_workspace_is_linear_in_n():
     """The default smooth-Q workspace holds a bounded number of Delta S rows: it grows
     linearly with N (the whole table, B*H*ceil(N/128)*N floats, grows as N^2)."""
@@ -85,6 +94,7 @@ def test_smooth_q_workspace_is_linear_in_n():
     ((0, 2, 2, 256, 64), 2), ((1, 2, 2, 0, 64), 2), ((1, 0, 1, 256, 64), 2),
     ((1, 2, 2, 256, 96), 3), ((1, 2, 2, 256, 256), 3), ((1, 6, 4, 256, 64), 4),
     ((1, 70000, 1, 16, 64), 2), ((64, 512, 512, 1 << 30, 128), 2),
+    ((1, 1, 1, 1 << 25, 128), 2), ((1, 1, 1, 1 << 26, 64), 2),
     ((1, 2, 2, 256, 64, 64), 6), ((1, 2, 2, 256, 64, 0), 6), ((1, 2, 2, 256, 64, -32), 6),
 ])
 def test_buffer_sizes_rejects(args, code):
