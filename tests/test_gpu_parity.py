@@ -208,6 +208,36 @@ def test_large_magnitudes(gpu_lib):
     compare_output(o, _oracle_o(ref, refv, False, 1 / 11.3), max_abs=2e-2 * 1e-3 * 4)
 
 
+def test_largest_head_count(gpu_lib):
+    """B*H = 65535, the most heads the ABI accepts (the Delta S pass's grid
+    y-dimension), with a ragged N = 3: codes and scales bit-exact over every head,
+    and the output of sampled heads (first, middle, last) against the oracle, plain
+    and smoothed Q, causal and not."""
+    B, H, N, d = 3, 21845, 3, 64
+    print(f"largest head count case B{B} H{H} N{N} d{d}", flush=True)
+    q, k, v = _rand_inputs(B, H, H, N, d, torch.float16, seed=91)
+    qk, vq, ref, refv = _check_quant(gpu_lib, q, k, v)
+    heads = [(0, 0), (1, H // 2), (2, H - 1)]
+    sel = lambda x: np.stack([np.asarray(x[b, h]) for b, h in heads])
+    sm = 0.125
+    qsq = gpu_lib.sage_quant_qk(q.to(DEV), k.to(DEV), True, smooth_q=True)
+    refsq = O.quantize_qk(q, k, smooth_q=True)
+    for n in ("q_i8", "q_scale", "q_mean"):
+        assert np.array_equal(to_np(qsq[n]), refsq[n]), n
+    ds_ref = O.delta_s(refsq["q_mean"], k, refsq["k_mean"])
+    for causal in (False, True):
+        o = gpu_lib.sage_attn_fwd(qk, vq, causal=causal, sm_scale=sm, out_dtype=torch.float16)
+        o_sq = gpu_lib.sage_attn_fwd_smooth_q(qsq, vq, k.to(DEV), causal=causal, sm_scale=sm,
+                                              out_dtype=torch.float16)
+        torch.cuda.synchronize()
+        o_ref = _oracle_o(ref, refv, causal, sm, heads=heads)
+        compare_output(torch.stack([o[b, h] for b, h in heads]), sel(o_ref))
+        o_ref_sq = O.attn_quant(refsq["q_i8"], refsq["q_scale"], refsq["k_i8"], refsq["k_scale"],
+                                refv["v_f8"], refv["v_scale"], causal=causal, sm_scale=sm,
+                                heads=heads, delta_s=ds_ref)
+        compare_output(torch.stack([o_sq[b, h] for b, h in heads]), sel(o_ref_sq))
+
+
 def test_quantization_ties_round_to_even(gpu_lib):
     """Every x/scale lands exactly on a rounding midpoint: INT8 codes at k + 1/2 and FP8 codes
     halfway between neighbours must round to even, bit-exactly as the oracle does."""
