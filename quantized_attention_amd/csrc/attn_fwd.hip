@@ -300,8 +300,9 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     // O is rescaled (when some row's max moved) just before the first P V
     // MFMA, so the max chain above, the conversions and the first
     // exponentials form one block the scheduler can interleave.
+    // (Tile 0 skips it: O is still zero there.)
     auto rescale_o = [&]() __attribute__((always_inline)) {
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+      if (t > 0 && __builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
         for (int c = 0; c < NKC; ++c)
 #pragma unroll
