@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 8
+#define SAGE_ABI_VERSION 9
 
 /* Q tokens per INT8 scale (default), K tokens per INT8 scale. */
 #define SAGE_BLKQ 128
@@ -262,22 +262,31 @@ sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const in
  * (SageAttention2 detail page) added to every score before the softmax:
  *   x = float32(S_int * c + g), rounded once, with c as in sage_attn_fwd and
  *   g the value sage_delta_s gives for the query's Q block and the key.
- * The Delta S rows are computed on the fly, a chunk of Q blocks at a time,
- * into `workspace`: each chunk's rows are written by the Delta S pass and
- * consumed by the attention of those Q blocks, so memory is B*H*rows*N
- * floats for a chunk of `rows` blocks, never the whole B*H*ceil(N/128)*N
- * table.  Results do not depend on the chunk size (each row's arithmetic
- * is the same).
+ * The Delta S rows are computed on the fly, a chunk at a time, into
+ * `workspace`: each chunk's rows are written by the Delta S pass and consumed
+ * by the attention of those query heads and Q blocks, so memory is a bounded
+ * number of rows of N floats, never the whole B*H*ceil(N/128)*N table.
+ * Results do not depend on the chunking (each row's arithmetic is the same).
  *   k: the original K in k_dtype; k_mean, q_mean: from sage_quant_qk.
  *   lse: float [B][H][N] or NULL (then lse_corr must be NULL, else
  *     SAGE_ERR_ARG); meaning as in sage_attn_fwd_lse.
- *   workspace: device memory of ws_bytes >= B*H*N*4 (one Q block per
- *     chunk), else SAGE_ERR_WORKSPACE; the chunk is the largest number of
- *     Q blocks that fits (a multiple of 16 above 16).  sizes.ws_smooth_q is
- *     the default: R = min(ceil(N/128), max(32, 16 * ceil(ceil(2048 / (B*H))
- *     / 16))) blocks, enough for 2048 workgroups per attention launch, at
- *     least 32 blocks per Delta S pass.  Its contents on entry do not
- *     matter.
+ *   workspace: device memory of ws_bytes, holding R = ws_bytes / (4*N) Delta S
+ *     rows; R >= H/H_kv, else SAGE_ERR_WORKSPACE.  Its contents on entry do
+ *     not matter.  With G = H/H_kv query heads per (b, kv head) group and
+ *     M = ceil(N/128) Q blocks, a chunk is
+ *       1. whole groups with all their Q blocks, g of them, when the largest
+ *          multiple of 8 with g*G*M <= R is >= 8 and g*G*M is no less than
+ *          the rows of a case-2 chunk (each (b, kv head) then stays on one
+ *          XCD, and each Delta S pass reads the K of its groups once); g is
+ *          evened out over the chunks;
+ *       2. else, when R >= B*H, all B*H_kv groups with r = R / (B*H) Q
+ *          blocks each;
+ *       3. else one group with r = R / G Q blocks;
+ *     r evened out over the chunks and rounded up to a multiple of 16 where
+ *     that still fits.
+ *   sizes.ws_smooth_q is the default: every head's rows of
+ *     min(M, max(32, 16*ceil(ceil(2048/(B*H))/16))) Q blocks, which grows
+ *     linearly with N.
  */
 sage_status sage_attn_fwd_smooth_q(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                    const float* k_scale, const uint8_t* v_f8,

@@ -485,8 +485,8 @@ def sage_attn_fwd_lse(qk: dict, vq: dict, *, causal: bool, sm_scale: float,
 
 def smooth_q_workspace(B: int, H: int, N: int, d: int, rows: int | None = None,
                        device="cuda") -> torch.Tensor:
-    """Workspace of sage_attn_fwd_smooth_q: the library's default (sizes.ws_smooth_q), or
-    room for the Delta S rows of `rows` Q blocks per chunk."""
+    """Workspace of sage_attn_fwd_smooth_q: the library's default (sizes.ws_smooth_q, which
+    depends on B*H and N only), or room for `rows` Q blocks of every head's Delta S rows."""
     nbytes = (sage_buffer_sizes(B, H, H, N, d)["ws_smooth_q"] if rows is None
               else B * H * rows * N * 4)
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)

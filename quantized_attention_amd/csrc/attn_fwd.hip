@@ -25,9 +25,11 @@
 
 namespace sage {
 
-// The grid covers q tiles qt0 .. qt0 + nqt - 1 of every (b, h).
+// The grid covers q tiles qt0 .. qt0 + nqt - 1 of the query heads of the
+// (b, kv head) groups bk0 .. bk0 + total / (nqt * H/H_kv) - 1 (bk = b*H_kv + hk).
 // SQ: Q was smoothed by its 128-block means; delta_s holds the Delta S rows
-// of those q tiles, [B][H][nqt][N] (log2 units), added to every score.
+// of those heads and q tiles, [heads][nqt][N] (log2 units), added to every
+// score.
 // PV4: P V on the FP4 matrix cores in MXFP4 (v_f8 holds E2M1 codes, v_e8 the
 // E8M0 scale bytes, see quant_v_mxfp4); P~ is quantized per 32 keys of a row.
 template <int D, bool CAUSAL, bool BF16, bool SQ, bool PV4>
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     const uint8_t* __restrict__ v_e8, const float* __restrict__ delta_s,
     void* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ lse_corr, int H, int H_kv, int N, float lam, int qg_shift,
-    int qt0, int nqt, int total) {
+    int bk0, int qt0, int nqt, int total) {
   // Every float32 step of the softmax below is the one the oracle takes (each
   // named quantity rounded once); no multiply may be fused into a following add.
 #pragma clang fp contract(off)
@@ -66,9 +68,9 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
   const int group = H / H_kv;
   int gm, qt, hk, b;
   if (CAUSAL) {
-    const int nbk = total / (nqt * group);   // B * H_kv
+    const int nbk = total / (nqt * group);   // (b, kv head) groups in this launch
     int rest = blockIdx.x;
-    const int bk = rest % nbk; rest /= nbk;
+    const int bk = bk0 + rest % nbk; rest /= nbk;
     gm = rest % group;
     qt = qt0 + nqt - 1 - rest / group;
     b = bk / H_kv;
@@ -77,8 +79,9 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
     int rest = xcd_remap(blockIdx.x, total);
     gm = rest % group; rest /= group;
     qt = qt0 + rest % nqt; rest /= nqt;
-    hk = rest % H_kv;
-    b = rest / H_kv;
+    const int bk = bk0 + rest;
+    hk = bk % H_kv;
+    b = bk / H_kv;
   }
   const int h = hk * group + gm;
 
@@ -153,7 +156,9 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
   for (int i = 0; i < KNB; ++i) koff[i] = k_tile_offset<D>(i * kWaves + wave, lane);
   // Delta S row of this workgroup's Q block; waves 0 and 1 stage a tile's
   // 128 values (one float per lane; keys past N read zeros)
-  const rsrc_t rds = make_rsrc(SQ ? delta_s + ((size_t)(b * H + h) * nqt + qt - qt0) * N : delta_s,
+  // (the launch's heads are consecutive: local head b * H + h - bk0 * group)
+  const rsrc_t rds = make_rsrc(SQ ? delta_s + ((size_t)(b * H + h - bk0 * group) * nqt + qt - qt0) * N
+                                  : delta_s,
                                SQ ? (uint32_t)N * 4 : 0u);
   const rsrc_t rvs = make_rsrc(vsh, PV4 ? (uint32_t)ntk * VSBYTES : 0u);
   // K and V codes (and, for MXFP4, the tile's 512 scale bytes; with Delta S
@@ -563,14 +568,15 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                                 const uint8_t* v_e8, const float* delta_s, void* o, int bf16_out,
                                 float* lse, const float* lse_corr, int B, int H, int H_kv, int N,
-                                int d, int q_group, int causal, float sm_scale, int qt0, int nqt,
-                                hipStream_t stream) {
+                                int d, int q_group, int causal, float sm_scale, int bk0, int nbk,
+                                int qt0, int nqt, hipStream_t stream) {
   using namespace sage;
   const int qg_shift = q_group == kBlkQ ? 7 : q_group == kWaveQ ? 5 : q_group == 1 ? 0 : -1;
   if (qg_shift < 0) return hipErrorInvalidValue;
   const int ntq = (N + kBlockQ - 1) / kBlockQ;
   if (qt0 < 0 || nqt <= 0 || qt0 + nqt > ntq) return hipErrorInvalidValue;
-  const long long total = (long long)B * H * nqt;
+  if (bk0 < 0 || nbk <= 0 || bk0 + nbk > B * H_kv) return hipErrorInvalidValue;
+  const long long total = (long long)nbk * (H / H_kv) * nqt;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const float lam = sm_scale * kLog2e;   // the softmax constant in log2 units
   dim3 grid((unsigned)total), block(kWaves * 64);
@@ -580,7 +586,7 @@ hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const 
   if (d == DD && (causal != 0) == CC && (bf16_out != 0) == BB && sq == SS && pv4 == PP) {          \
     hipLaunchKernelGGL((attn_fwd_kernel<DD, CC, BB, SS, PP>), grid, block, 0, stream, q_i8,       \
                        q_scale, k_i8, k_scale, v_f8, v_scale, v_e8, delta_s, o, lse, lse_corr, H, \
-                       H_kv, N, lam, qg_shift, qt0, nqt, (int)total);                         \
+                       H_kv, N, lam, qg_shift, bk0, qt0, nqt, (int)total);                    \
     return hipGetLastError();                                                                     \
   }
 #define SAGE_ATTN_CASES(SS, PP)              \

@@ -3,9 +3,10 @@
 // Algorithm 1 of the SageAttention2 detail page subtracts each Q block's mean
 // q_bar_i before quantizing Q and adds GEMV(q_bar_i, K_j^T) back to every
 // score of the block; its pipeline figure computes that GEMV before
-// quantization, on the smoothed K.  Here, for every (b, h), 128-token Q
-// block i and key j:
-//   out[b][h][i][j] = fp32(sum_c q_mean[b][h][i][c] * Ks[j][c] * sm_log2),
+// quantization, on the smoothed K.  Here, for the flattened heads
+// bh = bh0 + u (u < nbh, bh = b*H + h), the 128-token Q blocks i = i0 + r
+// (r < nrows) and every key j:
+//   out[u][r][j] = fp32(sum_c q_mean[b][h][i][c] * Ks[j][c] * sm_log2),
 //   Ks[j][c] = float32(K[b][h_kv][j][c]) - k_mean[b][h_kv][c]
 // (the values the K quantizer sees), already in the attention kernel's
 // log2 score units.  The products of the float32 operands are exact in
@@ -15,8 +16,9 @@
 // entry decides scores that the FP8 rounding of P~ turns into codes, so its
 // value must not move with the order of an FP32 sum.
 //
-// A range of Q blocks at a time: the attention of smoothed Q consumes the
-// table in chunks of Q blocks, so its memory is rows x N, never N^2/128.
+// A range of heads and Q blocks at a time: the attention of smoothed Q
+// consumes the rows in chunks, so its memory is heads x rows x N for a
+// bounded number of heads x rows, never N^2/128 per head.
 //
 // Work split: a workgroup of 4 waves owns 64 keys of one (b, h).  Each wave
 // keeps its 16 keys' smoothed K rows in registers as FP64 (the B operand,
@@ -38,10 +40,10 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
                                                       const float* __restrict__ k_mean,
                                                       const float* __restrict__ q_mean,
                                                       float* __restrict__ out, int H, int H_kv,
-                                                      int N, int nmb, int i0, int nrows,
-                                                      float sm_log2) {
+                                                      int N, int nmb, int bh0, int i0,
+                                                      int nrows, float sm_log2) {
   constexpr int QD = D / 4;   // channels per lane group
-  const int bh = blockIdx.y, b = bh / H, h = bh % H, hk = h / (H / H_kv);
+  const int bh = bh0 + blockIdx.y, b = bh / H, h = bh % H, hk = h / (H / H_kv);
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int col = lane % 16, g = lane / 16;
   const int key = blockIdx.x * 64 + wave * 16 + col;
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
     }
   }
   const float* qm = q_mean + ((size_t)bh * nmb + i0) * D;
-  float* ob = out + (size_t)bh * nrows * N;
+  float* ob = out + (size_t)blockIdx.y * nrows * N;
   const double scale = (double)sm_log2;
   for (int r0 = 0; r0 < nrows; r0 += 16) {
     // A operand: mean row i0 + r0 + col (rows past the range read its last
@@ -101,17 +103,18 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
 }  // namespace sage
 
 hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
-                               int B, int H, int H_kv, int N, int d, float sm_scale, int i0,
-                               int nrows, float* out, hipStream_t st) {
+                               int B, int H, int H_kv, int N, int d, float sm_scale, int bh0,
+                               int nbh, int i0, int nrows, float* out, hipStream_t st) {
   using namespace sage;
   const int nmb = (N + kBlkQ - 1) / kBlkQ;
   if (i0 < 0 || nrows <= 0 || i0 + nrows > nmb) return hipErrorInvalidValue;
-  const dim3 grid((N + 63) / 64, B * H), block(256);
+  if (bh0 < 0 || nbh <= 0 || bh0 + nbh > B * H || nbh > 65535) return hipErrorInvalidValue;
+  const dim3 grid((N + 63) / 64, nbh), block(256);
   const float sm_log2 = sm_scale * kLog2e;
 #define SAGE_DS(DD, BB)                                                                         \
   if (d == DD && (bf16 != 0) == BB) {                                                           \
     hipLaunchKernelGGL((delta_s_kernel<DD, BB>), grid, block, 0, st, k, k_mean, q_mean, out, H, \
-                       H_kv, N, nmb, i0, nrows, sm_log2);                                       \
+                       H_kv, N, nmb, bh0, i0, nrows, sm_log2);                                  \
     return hipGetLastError();                                                                   \
   }
   SAGE_DS(64, false)

@@ -18,16 +18,16 @@ hipError_t sage_launch_quant(const void* q, const void* k, const void* v, int bf
                              float* k_mean, float* q_mean, uint8_t* v_f8, float* v_scale, void* ws,
                              hipStream_t st);
 hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
-                               int B, int H, int H_kv, int N, int d, float sm_scale, int i0,
-                               int nrows, float* out, hipStream_t st);
+                               int B, int H, int H_kv, int N, int d, float sm_scale, int bh0,
+                               int nbh, int i0, int nrows, float* out, hipStream_t st);
 hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, int d,
                                uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st);
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_f8, const float* v_scale,
                                 const uint8_t* v_e8, const float* delta_s, void* o, int bf16_out,
                                 float* lse, const float* lse_corr, int B, int H, int H_kv, int N,
-                                int d, int q_group, int causal, float sm_scale, int qt0, int nqt,
-                                hipStream_t stream);
+                                int d, int q_group, int causal, float sm_scale, int bk0, int nbk,
+                                int qt0, int nqt, hipStream_t stream);
 hipError_t sage_launch_quant_v_mxfp4(const void* v, int bf16, int B, int H_kv, int N, int d,
                                      uint8_t* v_f4, uint8_t* v_e8, hipStream_t st);
 hipError_t sage_launch_lse_correction(const void* q, int bf16, const float* k_mean, int B, int H,
@@ -58,13 +58,53 @@ sage_status check_shape(int B, int H, int H_kv, int N, int d) {
 
 int64_t q_blocks(int N) { return ((int64_t)N + SAGE_BLKQ - 1) / SAGE_BLKQ; }
 
-// Q blocks per chunk of sage_attn_fwd_smooth_q's default workspace: enough
-// for 2048 attention workgroups per launch, at least 32 rows per Delta S
-// pass (each pass reads all of K once), a multiple of 16 (the pass's row
-// group), at most the number of Q blocks.
+// One chunk of sage_attn_fwd_smooth_q: `groups` (b, kv head) groups with
+// `rows` Q blocks of each of their query heads.
+struct SqChunk {
+  int64_t groups, rows;
+};
+
+// Rows an attention launch should have for its dispatch rounds to fill
+// (about 2048 workgroups, 4 rounds at d = 128).
+constexpr int64_t kSqTargetRows = 2048;
+
+// `rows` spread evenly over the chunks it takes at most `rmax` at a time,
+// rounded up to a multiple of 16 (the Delta S pass's row group) where that
+// still fits.
+int64_t even_rows(int64_t total, int64_t rmax) {
+  const int64_t n = (total + rmax - 1) / rmax;
+  const int64_t r = (total + n - 1) / n, r16 = (r + 15) / 16 * 16;
+  return r16 <= rmax ? r16 : r;
+}
+
+// The chunk for a workspace of `cap` Delta S rows (N floats each), cap >= group:
+//  1. whole groups with all their Q blocks, when a multiple of 8 groups (so
+//     each (b, kv head) stays on one XCD's L2) fits and its attention launch
+//     is no smaller than that of case 2: each Delta S pass then reads the K
+//     of its groups once;
+//  2. else every group with a range of Q blocks (one pass over K per range);
+//  3. else (a workspace smaller than one row per head) one group at a time.
+SqChunk smooth_q_chunk(int64_t nbk, int64_t group, int64_t nmb, int64_t cap) {
+  const int64_t per = group * nmb;   // rows of one group
+  int64_t g = cap / per;
+  if (g >= nbk) return {nbk, nmb};
+  if (cap < nbk * group) return {1, even_rows(nmb, cap / group)};
+  const SqChunk by_rows = {nbk, even_rows(nmb, cap / (nbk * group))};
+  g -= g % 8;
+  if (g >= 8 && g * per >= by_rows.groups * group * by_rows.rows) {
+    const int64_t n = (nbk + g - 1) / g;
+    int64_t ge = ((nbk + n - 1) / n + 7) / 8 * 8;
+    return {ge < g ? ge : g, nmb};
+  }
+  return by_rows;
+}
+
+// The default workspace: every head's rows for R Q blocks, R enough for
+// kSqTargetRows rows in all, at least 32 (a Delta S pass over K per 32 Q
+// blocks or fewer), a multiple of 16, at most the number of Q blocks.
 int64_t smooth_q_default_rows(int B, int H, int N) {
   const int64_t bh = (int64_t)B * H;
-  int64_t r = (2048 + bh - 1) / bh;
+  int64_t r = (kSqTargetRows + bh - 1) / bh;
   r = (r + 15) / 16 * 16;
   if (r < 32) r = 32;
   return r < q_blocks(N) ? r : q_blocks(N);
@@ -188,7 +228,8 @@ sage_status sage_delta_s(const void* k, sage_dtype dtype, const float* k_mean,
   if ((int64_t)B * H * nrows * N > kMaxElems) return SAGE_ERR_SHAPE;
   if (!aligned16(k) || !aligned16(q_mean) || !aligned16(delta_s)) return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_delta_s(k, dtype == SAGE_BF16, k_mean, q_mean, B, H, H_kv, N, d,
-                                      sm_scale, i0, nrows, delta_s, (hipStream_t)stream));
+                                      sm_scale, 0, B * H, i0, nrows, delta_s,
+                                      (hipStream_t)stream));
 }
 
 sage_status sage_quant_v(const void* v, sage_dtype dtype, int B, int H_kv, int N, int d,
@@ -220,7 +261,7 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
     return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr,
                                        nullptr, o, out_dtype == SAGE_BF16, nullptr, nullptr, B, H,
-                                       H_kv, N, d, q_group, causal, sm_scale, 0,
+                                       H_kv, N, d, q_group, causal, sm_scale, 0, B * H_kv, 0,
                                        (int)q_blocks(N), (hipStream_t)stream));
 }
 
@@ -241,7 +282,7 @@ sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const in
     return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr,
                                        nullptr, o, out_dtype == SAGE_BF16, lse, lse_corr, B, H,
-                                       H_kv, N, d, q_group, causal, sm_scale, 0,
+                                       H_kv, N, d, q_group, causal, sm_scale, 0, B * H_kv, 0,
                                        (int)q_blocks(N), (hipStream_t)stream));
 }
 
@@ -267,25 +308,27 @@ sage_status sage_attn_fwd_smooth_q(const int8_t* q_i8, const float* q_scale, con
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_f8) || !aligned16(o) ||
       !aligned16(k) || !aligned16(q_mean))
     return SAGE_ERR_ALIGN;
-  // Q blocks per chunk: as many Delta S rows as the workspace holds
-  const int64_t nmb = q_blocks(N), row_bytes = (int64_t)B * H * N * (int64_t)sizeof(float);
-  if (!workspace || (int64_t)(ws_bytes / (size_t)row_bytes) < 1) return SAGE_ERR_WORKSPACE;
+  // the chunk: as many Delta S rows (N floats each) as the workspace holds
+  const int64_t nmb = q_blocks(N), nbk = (int64_t)B * H_kv, group = H / H_kv;
+  const int64_t cap = workspace ? (int64_t)(ws_bytes / ((size_t)N * sizeof(float))) : 0;
+  if (cap < group) return SAGE_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SAGE_ERR_ALIGN;
-  int64_t rows = (int64_t)(ws_bytes / (size_t)row_bytes);
-  if (rows >= nmb) rows = nmb;
-  else if (rows > 16) rows -= rows % 16;
-  if ((int64_t)B * H * rows * N > kMaxElems) return SAGE_ERR_SHAPE;
+  const SqChunk ck = smooth_q_chunk(nbk, group, nmb, cap);
   float* ds = static_cast<float*>(workspace);
   const hipStream_t hs = (hipStream_t)stream;
-  for (int64_t i0 = 0; i0 < nmb; i0 += rows) {
-    const int n = (int)(nmb - i0 < rows ? nmb - i0 : rows);
-    hipError_t e = sage_launch_delta_s(k, k_dtype == SAGE_BF16, k_mean, q_mean, B, H, H_kv, N, d,
-                                       sm_scale, (int)i0, n, ds, hs);
-    if (e != hipSuccess) return SAGE_ERR_HIP;
-    e = sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr, ds, o,
-                             out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d, q_group,
-                             causal, sm_scale, (int)i0, n, hs);
-    if (e != hipSuccess) return SAGE_ERR_HIP;
+  for (int64_t g0 = 0; g0 < nbk; g0 += ck.groups) {
+    const int ng = (int)(nbk - g0 < ck.groups ? nbk - g0 : ck.groups);
+    for (int64_t i0 = 0; i0 < nmb; i0 += ck.rows) {
+      const int n = (int)(nmb - i0 < ck.rows ? nmb - i0 : ck.rows);
+      hipError_t e = sage_launch_delta_s(k, k_dtype == SAGE_BF16, k_mean, q_mean, B, H, H_kv, N,
+                                         d, sm_scale, (int)(g0 * group), (int)(ng * group),
+                                         (int)i0, n, ds, hs);
+      if (e != hipSuccess) return SAGE_ERR_HIP;
+      e = sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr, ds, o,
+                               out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d, q_group,
+                               causal, sm_scale, (int)g0, ng, (int)i0, n, hs);
+      if (e != hipSuccess) return SAGE_ERR_HIP;
+    }
   }
   return SAGE_OK;
 }
@@ -318,7 +361,7 @@ sage_status sage_attn_fwd_mxfp4(const int8_t* q_i8, const float* q_scale, const 
     return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f4, nullptr, v_e8, nullptr,
                                        o, out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d,
-                                       q_group, causal, sm_scale, 0, (int)q_blocks(N),
+                                       q_group, causal, sm_scale, 0, B * H_kv, 0, (int)q_blocks(N),
                                        (hipStream_t)stream));
 }
 

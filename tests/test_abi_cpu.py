@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
             "sage_attn_fwd_smooth_q"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sage_abi_version() == 8
+    assert lib.sage_abi_version() == 9
 
 
 def test_status_strings():
@@ -57,15 +57,54 @@ def test_buffer_sizes(B, H, H_kv, N, d, q_group):
     assert s["ws_quant_v"] == 4 * B * H_kv * math.ceil(N / 256) * d
     assert s["ws_quant_qkv"] == s["ws_quant_qk"] + s["ws_quant_v"]
     assert s["q_mean"] == 4 * B * H * math.ceil(N / 128) * d
-    assert s["ws_smooth_q"] == 4 * B * H * _smooth_q_rows(B * H, N) * N
+    assert s["ws_smooth_q"] == 4 * B * H * _smooth_q_default_rows(B * H, N) * N
     assert s["v_f4"] == B * H_kv * math.ceil(N / 128) * 64 * d
     assert s["v_e8"] == B * H_kv * math.ceil(N / 128) * 512
 
 
-def _smooth_q_rows(bh, N):
-    """Default Q blocks per chunk of sage_attn_fwd_smooth_q (the rule sage.h states)."""
+def _even_rows(total, rmax):
+    n = -(-total // rmax)
+    r = -(-total // n)
+    r16 = -(-r // 16) * 16
+    return r16 if r16 <= rmax else r
+
+
+def _smooth_q_chunk(nbk, G, M, R):
+    """(groups, Q blocks) of one sage_attn_fwd_smooth_q chunk for a workspace of R Delta
+    S rows, by the rule sage.h states."""
+    g = R // (G * M)
+    if g >= nbk:
+        return nbk, M
+    if R < nbk * G:
+        return 1, _even_rows(M, R // G)
+    rows = _even_rows(M, R // (nbk * G))
+    g -= g % 8
+    if g >= 8 and g * G * M >= nbk * G * rows:
+        n = -(-nbk // g)
+        return min(g, -(-(-(-nbk // n)) // 8) * 8), M
+    return nbk, rows
+
+
+def _smooth_q_default_rows(bh, N):
+    """Default Q blocks per head of sage_attn_fwd_smooth_q's workspace (sage.h's rule)."""
     r = max(32, 16 * math.ceil(math.ceil(2048 / bh) / 16))
     return min(math.ceil(N / 128), r)
+
+
+@pytest.mark.parametrize("nbk,G,M,R,want", [
+    (128, 1, 256, 4096, (16, 256)),    # sweep N=32K default: 16 whole heads per chunk
+    (48, 1, 138, 2304, (48, 48)),      # video-DiT default: 16 heads (2208 rows) < 48 x 48
+    (8, 4, 800, 2048, (8, 64)),        # GQA long default: every group, 64 Q blocks
+    (48, 1, 138, 1104, (8, 138)),      # 8 heads (1104 rows) = 48 x 23 rows: whole heads
+    (48, 1, 138, 4416, (24, 138)),     # 32 heads fit (4416 > 48 x 80): evened to 24 + 24
+    (40, 1, 256, 4096, (16, 256)),     # 16 + 16 + 8
+    (2, 2, 8, 4, (2, 1)), (2, 2, 8, 12, (2, 3)), (2, 2, 8, 64, (2, 8)),
+    (2, 2, 8, 3, (1, 1)),
+    (2, 2, 18, 40, (2, 9)), (3, 1, 1, 7, (3, 1)), (6, 2, 3, 12, (6, 1)),
+])
+def test_smooth_q_chunk_rule(nbk, G, M, R, want):
+    """The chunk rule in closed cases."""
+    assert _smooth_q_chunk(nbk, G, M, R) == want
 
 
 def test_largest_head_fits_32_bit_buffer_ranges():
@@ -86,7 +125,7 @@ def test_smooth_q_workspace_is_linear_in_n():
         per_n.add(s["ws_smooth_q"] / N)
         assert s["ws_smooth_q"] * 8 <= 4 * 32 * math.ceil(N / 128) * N
     assert len(per_n) == 1
-    # sequence sweep at N = 32K: 128 heads x 32 rows x 32768 keys (512 MiB, not 4 GiB)
+    # sequence sweep at N = 32K: 128 heads x 32 Q blocks x 32768 keys (512 MiB, not 4 GiB)
     assert qa.sage_buffer_sizes(4, 32, 32, 32768, 128)["ws_smooth_q"] == 4 * 128 * 32 * 32768
 
 
@@ -138,7 +177,7 @@ def _attn_sq(lib, **kw):
     a = dict(q_i8=FAKE, q_scale=FAKE, k_i8=FAKE, k_scale=FAKE, v_f8=FAKE, v_scale=FAKE, k=FAKE,
              k_dt=0, k_mean=FAKE, q_mean=FAKE, o=FAKE, dt=0, lse=None, corr=None, B=1, H=2,
              H_kv=2, N=256, d=64, qg=128, causal=0, sm_scale=0.125, ws=FAKE,
-             ws_bytes=2 * 256 * 4, stream=None)
+             ws_bytes=256 * 4, stream=None)
     a.update(kw)
     return lib.sage_attn_fwd_smooth_q(*a.values())
 
@@ -262,7 +301,8 @@ def test_delta_s_rejects(kw, code):
     (dict(o=None), 1), (dict(N=0), 2), (dict(d=96), 3), (dict(H=3), 4), (dict(k_dt=2), 5),
     (dict(dt=7), 5), (dict(qg=64), 6), (dict(causal=2), 6), (dict(sm_scale=0.0), 6),
     (dict(corr=FAKE), 6), (dict(k=FAKE + 2), 9), (dict(q_mean=FAKE + 4), 9),
-    (dict(ws=None), 7), (dict(ws_bytes=2 * 256 * 4 - 1), 7), (dict(ws=FAKE + 8), 9),
+    (dict(ws=None), 7), (dict(ws_bytes=256 * 4 - 1), 7), (dict(ws=FAKE + 8), 9),
+    (dict(H=4, H_kv=2, ws_bytes=2 * 256 * 4 - 1), 7),
 ])
 def test_attn_fwd_smooth_q_rejects(kw, code):
     assert _attn_sq(qa.load_library(), **kw) == code

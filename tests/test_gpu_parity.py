@@ -531,12 +531,15 @@ def test_smooth_q_lse(gpu_lib):
 @pytest.mark.parametrize("B,H,H_kv,N,d,dtype,causal", [
     (1, 4, 2, 1000, 64, torch.float16, True),
     (2, 2, 1, 2200, 128, torch.bfloat16, False),
+    (2, 6, 3, 300, 64, torch.float16, True),
+    (1, 32, 16, 300, 64, torch.bfloat16, True),
 ])
 def test_smooth_q_chunks_do_not_change_the_result(gpu_lib, B, H, H_kv, N, d, dtype, causal):
-    """sage_attn_fwd_smooth_q computes the Delta S rows a chunk of Q blocks at a time in
-    its workspace.  Every chunk size (one block, a ragged 3, 16, the default, a workspace
-    larger than the whole table) gives the same output and LSE bit for bit, and the
-    workspace's previous contents do not matter."""
+    """sage_attn_fwd_smooth_q computes the Delta S rows a chunk at a time in its
+    workspace.  Workspaces of 2 to 48 Delta S rows (one group at a time with a range of
+    Q blocks; every group with a range of Q blocks; for the 16-group shape at 48 rows,
+    8 whole groups at a time), the default and more than the whole table give the same
+    output and LSE bit for bit, and the workspace's previous contents do not matter."""
     print(f"smooth_q chunks case B{B} H{H}/{H_kv} N{N} d{d} {dtype} causal={causal}",
           flush=True)
     q, k, v = _biased_q_inputs(B, H, H_kv, N, d, dtype, seed=N + d)
@@ -546,8 +549,9 @@ def test_smooth_q_chunks_do_not_change_the_result(gpu_lib, B, H, H_kv, N, d, dty
     kd = k.to(DEV)
     nmb = -(-N // 128)
     runs = {}
-    for rows in (None, 1, 3, 16, nmb + 5):
-        ws = gpu_lib.smooth_q_workspace(B, H, N, d, rows=rows, device=DEV)
+    for rows in (None, 2, 5, 12, 24, 48, B * H * (nmb + 5)):
+        ws = (gpu_lib.smooth_q_workspace(B, H, N, d, device=DEV) if rows is None else
+              torch.empty(rows * N * 4, dtype=torch.uint8, device=DEV))
         ws.fill_(0xFF)   # NaN bit patterns: a row the kernel read before writing would show
         runs[rows] = gpu_lib.sage_attn_fwd_smooth_q(qk, vq, kd, causal=causal, sm_scale=sm,
                                                     out_dtype=dtype, return_lse=True,
@@ -773,7 +777,7 @@ def test_workload_parity_q_group(gpu_lib, name, heads, nrows, q_group):
 
 @pytest.mark.parametrize("name,heads,nrows,q_group", [
     ("llm_prefill", [(0, 3)], 128, 128),
-    ("video_dit", [(0, 11)], 64, 1),
+    ("video_dit", [(0, 11), (0, 40)], 64, 1),
     ("sweep@N4096", [(3, 2)], 96, 128),
 ])
 def test_workload_parity_smooth_q(gpu_lib, name, heads, nrows, q_group):
