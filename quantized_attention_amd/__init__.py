@@ -33,7 +33,7 @@ consecutive Q tokens per scale: 128 (per block), 32 (per wave, the per-warp
 granularity) or 1 (per query, the per-thread granularity); the attention
 entry points read it from the length of ``q_scale``.  ``smooth_q`` subtracts each
 128-token Q block's mean before quantizing and adds the Delta S term back to
-the scores (Algorithm 1's GEMV compensation), computed a chunk of Q blocks at a
+the scores (Algorithm 1's GEMV compensation), computed a chunk of heads and Q blocks at a
 time into a bounded workspace.  ``pv="mxfp4"`` runs P V in MXFP4
 (E2M1 with E8M0 scales per 32 keys, the OCP format the pages name for MI350-class
 GPUs) on the FP4 matrix cores.
@@ -496,7 +496,7 @@ def sage_attn_fwd_smooth_q(qk: dict, vq: dict, k: torch.Tensor, *, causal: bool,
                            sm_scale: float, out_dtype=torch.float16, return_lse: bool = False,
                            lse_corr=None, workspace=None, out=None, lse=None, stream=None):
     """Attention of smoothed Q (sage_quant_qk with smooth_q): the Delta S term
-    q_mean . (k - k_mean) is computed a chunk of Q blocks at a time into `workspace`
+    q_mean . (k - k_mean) is computed a chunk of heads and Q blocks at a time into `workspace`
     (default: smooth_q_workspace) and added to the scores.  k: the original K.
     Returns O, or (O, lse) with return_lse."""
     q_i8, k_i8 = qk["q_i8"], qk["k_i8"]
