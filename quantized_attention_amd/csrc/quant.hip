@@ -33,7 +33,7 @@
 namespace sage {
 
 constexpr int kQuantThreads = 256;
-constexpr int kStatChunk = 256;   // tokens per colstats_partial workgroup
+constexpr int kStatChunk = 256;   // tokens per kv_stats_partial workgroup
 
 template <bool BF16>
 __device__ __forceinline__ void unpack8(const uint4 u, float* x) {
@@ -64,62 +64,84 @@ __device__ __forceinline__ float div_rn(float v, float s, float y) {
 constexpr float kDivRnMinScale = 1e-30f;
 
 // ---------------------------------------------------------------------------
-// Per-channel statistics of one [N][D] slice over a chunk of kStatChunk
-// tokens: MODE 0 the FP64 sum (K), MODE 1 the absolute max (V, as float).
-// The RPP row groups of the workgroup are combined in a fixed order; ws is
-// [B*Hkv][nchunk][D] (double or float).
-template <int D, bool BF16, int MODE>
-__device__ __forceinline__ void colstats_chunk(const void* __restrict__ x, void* __restrict__ ws,
-                                               int N, int nchunk, int chunk, int bh,
-                                               double (*red)[D]) {
-  constexpr int TPR = D / 8;                    // threads per token row
-  constexpr int RPP = kQuantThreads / TPR;      // rows per pass
-  const int tid = threadIdx.x, cg = tid % TPR, rsub = tid / TPR;
-  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (size_t)bh * N * D;
-  const int n0 = chunk * kStatChunk, n1 = min(N, n0 + kStatChunk);
-  double acc[8];
-  float mx[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { acc[i] = 0.0; mx[i] = 0.f; }
-  for (int n = n0 + rsub; n < n1; n += RPP) {
-    const uint4 u = *reinterpret_cast<const uint4*>(xs + (size_t)n * D + cg * 8);
-    float v[8];
-    unpack8<BF16>(u, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (MODE == 0) acc[i] += (double)v[i];
-      else mx[i] = fmaxf(mx[i], fabsf(v[i]));
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) red[rsub][cg * 8 + i] = MODE == 0 ? acc[i] : (double)mx[i];
-  __syncthreads();
-  if (tid < D) {
-    if (MODE == 0) {
-      double s = 0.0;
-      for (int r = 0; r < RPP; ++r) s += red[r][tid];
-      reinterpret_cast<double*>(ws)[((size_t)bh * nchunk + chunk) * D + tid] = s;
-    } else {
-      float m = 0.f;
-      for (int r = 0; r < RPP; ++r) m = fmaxf(m, (float)red[r][tid]);
-      reinterpret_cast<float*>(ws)[((size_t)bh * nchunk + chunk) * D + tid] = m;
-    }
-  }
-}
-
-// One pass over a chunk of tokens of K and/or V: the FP64 column sums of K
-// (for its mean) and the column amax of V (for its scales).  grid (nchunk,
-// B*Hkv).
+// One pass over a chunk of kStatChunk tokens of K and/or V of one (b, kv
+// head): the FP64 column sums of K (for its mean) and the column amax of V
+// (for its scales).  Each thread reads every RPP-th token row of its
+// 8-channel group, kStatUnroll rows of each tensor in flight at a time; the
+// RPP row groups are then combined in a fixed order.  The K sums are exact,
+// so no order matters for them; amax is order-free.  grid (nchunk, B*Hkv);
+// kws and vws are [B*Hkv][nchunk][D] (double, float).
+constexpr int kStatUnroll = 4;
 template <int D, bool BF16>
 __global__ __launch_bounds__(kQuantThreads) void kv_stats_partial(const void* __restrict__ k,
                                                                   const void* __restrict__ v,
                                                                   double* __restrict__ kws,
                                                                   float* __restrict__ vws, int N,
                                                                   int nchunk, int do_k, int do_v) {
-  __shared__ double red[kQuantThreads / (D / 8)][D];
-  if (do_k) colstats_chunk<D, BF16, 0>(k, kws, N, nchunk, blockIdx.x, blockIdx.y, red);
-  if (do_k && do_v) __syncthreads();
-  if (do_v) colstats_chunk<D, BF16, 1>(v, vws, N, nchunk, blockIdx.x, blockIdx.y, red);
+  constexpr int TPR = D / 8;                    // threads per token row
+  constexpr int RPP = kQuantThreads / TPR;      // rows per pass
+  constexpr int U = kStatUnroll;
+  static_assert(2 * D <= kQuantThreads, "one thread per channel for each statistic");
+  __shared__ double red_k[RPP][D];
+  __shared__ float red_v[RPP][D];
+  const int tid = threadIdx.x, cg = tid % TPR, rsub = tid / TPR;
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const size_t base = (size_t)bh * N * D + cg * 8;
+  const uint16_t* ks = reinterpret_cast<const uint16_t*>(k) + base;
+  const uint16_t* vs = reinterpret_cast<const uint16_t*>(v) + base;
+  const int n0 = chunk * kStatChunk, n1 = min(N, n0 + kStatChunk);
+  double acc[8];
+  float mx[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { acc[i] = 0.0; mx[i] = 0.f; }
+  for (int n = n0 + rsub; n < n1; n += U * RPP) {
+    uint4 uk[U], uv[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int r = n + j * RPP;
+      if (r < n1) {
+        if (do_k) uk[j] = *reinterpret_cast<const uint4*>(ks + (size_t)r * D);
+        if (do_v) uv[j] = *reinterpret_cast<const uint4*>(vs + (size_t)r * D);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (n + j * RPP < n1) {
+        float x[8];
+        if (do_k) {
+          unpack8<BF16>(uk[j], x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += (double)x[i];
+        }
+        if (do_v) {
+          unpack8<BF16>(uv[j], x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(x[i]));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    red_k[rsub][cg * 8 + i] = acc[i];
+    red_v[rsub][cg * 8 + i] = mx[i];
+  }
+  __syncthreads();
+  // threads 0 .. D-1 combine the K sums, D .. 2D-1 the V maxima
+  if (tid < D) {
+    if (do_k) {
+      double t = 0.0;
+      for (int r = 0; r < RPP; ++r) t += red_k[r][tid];
+      kws[((size_t)bh * nchunk + chunk) * D + tid] = t;
+    }
+  } else if (tid < 2 * D) {
+    if (do_v) {
+      const int c = tid - D;
+      float m = 0.f;
+      for (int r = 0; r < RPP; ++r) m = fmaxf(m, red_v[r][c]);
+      vws[((size_t)bh * nchunk + chunk) * D + c] = m;
+    }
+  }
 }
 
 // The chunks combined: k_mean[bh][c] = float32(sum / N) (0 when !smooth_k)
