@@ -212,8 +212,10 @@ def run_lse(w, steps: int, warmup: int) -> dict:
 
 
 def delta_s_alone(plan, k, steps: int) -> float:
-    """Milliseconds of the Delta S passes sage_attn_fwd_smooth_q runs per call (the same
-    chunks of Q blocks, into the plan's workspace), without the attention between them."""
+    """Milliseconds of the Delta S work sage_attn_fwd_smooth_q does per call, without the
+    attention between its passes: every head and Q block, in chunks of Q-block rows that
+    fill the plan's workspace. The entry point may instead split the same work into groups
+    of whole heads (its chunk rule); the launches then cover the same rows in another order."""
     import torch
     import quantized_attention_amd as qa
     B, H, _, N, _ = plan.shape
