@@ -267,6 +267,9 @@ sage_status sage_attn_fwd_lse(const int8_t* q_i8, const float* q_scale, const in
  * by the attention of those query heads and Q blocks, so memory is a bounded
  * number of rows of N floats, never the whole B*H*ceil(N/128)*N table.
  * Results do not depend on the chunking (each row's arithmetic is the same).
+ * With causal = 1 the pass may skip keys a Q block cannot attend (those at or
+ * past (i + 1) * 128 for block i), about half the work of whole rows; the
+ * skipped entries of the workspace keep whatever they held.
  *   k: the original K in k_dtype; k_mean, q_mean: from sage_quant_qk.
  *   lse: float [B][H][N] or NULL (then lse_corr must be NULL, else
  *     SAGE_ERR_ARG); meaning as in sage_attn_fwd_lse.

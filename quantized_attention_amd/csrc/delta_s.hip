@@ -20,6 +20,12 @@
 // consumes the rows in chunks, so its memory is heads x rows x N for a
 // bounded number of heads x rows, never N^2/128 per head.
 //
+// Causal: Q block i attends keys below (i + 1) * 128 only, so a key past that
+// bound never meets row i.  With `causal` set, a workgroup's 64 keys are
+// computed for the rows from the first block whose range reaches them (in
+// steps of 16 rows) and the entries above each block's diagonal are left
+// unwritten: half the FP64 work of a causal table.
+//
 // Work split: a workgroup of 4 waves owns 64 keys of one (b, h).  Each wave
 // keeps its 16 keys' smoothed K rows in registers as FP64 (the B operand,
 // d/4 doubles per lane) and walks the range's mean rows 16 at a time (the
@@ -41,8 +47,15 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
                                                       const float* __restrict__ q_mean,
                                                       float* __restrict__ out, int H, int H_kv,
                                                       int N, int nmb, int bh0, int i0,
-                                                      int nrows, float sm_log2) {
+                                                      int nrows, int causal, float sm_log2) {
   constexpr int QD = D / 4;   // channels per lane group
+  // first row of the range that reads this workgroup's keys (all of them
+  // unless causal), rounded down to the 16-row MFMA group
+  int rbeg = 0;
+  if (causal) {
+    rbeg = max(0, (int)(blockIdx.x * 64) / kBlkQ - i0) & ~15;
+    if (rbeg >= nrows) return;
+  }
   const int bh = bh0 + blockIdx.y, b = bh / H, h = bh % H, hk = h / (H / H_kv);
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int col = lane % 16, g = lane / 16;
@@ -76,7 +89,7 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
   const float* qm = q_mean + ((size_t)bh * nmb + i0) * D;
   float* ob = out + (size_t)blockIdx.y * nrows * N;
   const double scale = (double)sm_log2;
-  for (int r0 = 0; r0 < nrows; r0 += 16) {
+  for (int r0 = rbeg; r0 < nrows; r0 += 16) {
     // A operand: mean row i0 + r0 + col (rows past the range read its last
     // row and are not stored)
     const float* qr = qm + (size_t)min(r0 + col, nrows - 1) * D + g * QD;
@@ -104,17 +117,20 @@ __global__ __launch_bounds__(256) void delta_s_kernel(const void* __restrict__ k
 
 hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
                                int B, int H, int H_kv, int N, int d, float sm_scale, int bh0,
-                               int nbh, int i0, int nrows, float* out, hipStream_t st) {
+                               int nbh, int i0, int nrows, int causal, float* out,
+                               hipStream_t st) {
   using namespace sage;
   const int nmb = (N + kBlkQ - 1) / kBlkQ;
   if (i0 < 0 || nrows <= 0 || i0 + nrows > nmb) return hipErrorInvalidValue;
   if (bh0 < 0 || nbh <= 0 || bh0 + nbh > B * H || nbh > 65535) return hipErrorInvalidValue;
-  const dim3 grid((N + 63) / 64, nbh), block(256);
+  // causal: keys from (i0 + nrows) * 128 on meet none of the range's rows
+  const int nkeys = causal && (int64_t)(i0 + nrows) * kBlkQ < N ? (i0 + nrows) * kBlkQ : N;
+  const dim3 grid((nkeys + 63) / 64, nbh), block(256);
   const float sm_log2 = sm_scale * kLog2e;
 #define SAGE_DS(DD, BB)                                                                         \
   if (d == DD && (bf16 != 0) == BB) {                                                           \
     hipLaunchKernelGGL((delta_s_kernel<DD, BB>), grid, block, 0, st, k, k_mean, q_mean, out, H, \
-                       H_kv, N, nmb, bh0, i0, nrows, sm_log2);                                  \
+                       H_kv, N, nmb, bh0, i0, nrows, causal, sm_log2);                          \
     return hipGetLastError();                                                                   \
   }
   SAGE_DS(64, false)

@@ -19,7 +19,8 @@ hipError_t sage_launch_quant(const void* q, const void* k, const void* v, int bf
                              hipStream_t st);
 hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
                                int B, int H, int H_kv, int N, int d, float sm_scale, int bh0,
-                               int nbh, int i0, int nrows, float* out, hipStream_t st);
+                               int nbh, int i0, int nrows, int causal, float* out,
+                               hipStream_t st);
 hipError_t sage_launch_quant_v(const void* v, int bf16, int B, int H_kv, int N, int d,
                                uint8_t* v_f8, float* v_scale, void* ws, hipStream_t st);
 hipError_t sage_launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
@@ -228,7 +229,7 @@ sage_status sage_delta_s(const void* k, sage_dtype dtype, const float* k_mean,
   if ((int64_t)B * H * nrows * N > kMaxElems) return SAGE_ERR_SHAPE;
   if (!aligned16(k) || !aligned16(q_mean) || !aligned16(delta_s)) return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_delta_s(k, dtype == SAGE_BF16, k_mean, q_mean, B, H, H_kv, N, d,
-                                      sm_scale, 0, B * H, i0, nrows, delta_s,
+                                      sm_scale, 0, B * H, i0, nrows, 0, delta_s,
                                       (hipStream_t)stream));
 }
 
@@ -322,7 +323,7 @@ sage_status sage_attn_fwd_smooth_q(const int8_t* q_i8, const float* q_scale, con
       const int n = (int)(nmb - i0 < ck.rows ? nmb - i0 : ck.rows);
       hipError_t e = sage_launch_delta_s(k, k_dtype == SAGE_BF16, k_mean, q_mean, B, H, H_kv, N,
                                          d, sm_scale, (int)(g0 * group), (int)(ng * group),
-                                         (int)i0, n, ds, hs);
+                                         (int)i0, n, causal, ds, hs);
       if (e != hipSuccess) return SAGE_ERR_HIP;
       e = sage_launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_f8, v_scale, nullptr, ds, o,
                                out_dtype == SAGE_BF16, lse, lse_corr, B, H, H_kv, N, d, q_group,
