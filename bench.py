@@ -7,9 +7,11 @@ Default workload: the sequence-sweep configuration at N = 32768
 (B=4, H=32, d=128, fp16, non-causal), the one the headline TOPS is quoted on.
 
 Prints ONE JSON line.  ``value`` is whole-step TOPS, 4*B*H*N^2*d / t_step
-(halved when causal); ``attn_tops`` is the attention kernel alone (the pages'
-convention: quantization time excluded), from the mean of the per-step
-launch times; ``attn_tops_median`` takes their median (20 steps by default).
+(halved when causal), t_step from replays of the step captured as a HIP graph
+(``--eager``: from eager launches; ``ms_per_step_eager`` is always reported);
+``attn_tops`` is the attention kernel alone (the pages' convention:
+quantization time excluded), from the mean of the per-step HIP-event times of
+the eager steps; ``attn_tops_median`` takes their median (20 steps by default).
 ``roofline`` is the attention
 kernel's algorithmic TOPS against the dense INT8/FP8 MFMA peak, with the
 kernel time measured by HIP events on the launch stream.  ``cpu_baseline``
@@ -119,6 +121,9 @@ def main():
                          "blocks; the Delta S passes are also timed alone)")
     ap.add_argument("--pv", default="fp8", choices=("fp8", "mxfp4"),
                     help="P V format: FP8 E4M3 (the method's) or MXFP4 on the FP4 matrix cores")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the whole step as eager launches (default: replays of the step "
+                         "captured as a HIP graph; the kernel split is always timed eagerly)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device-to-device copy of this many MiB (3 times), "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -155,11 +160,12 @@ def main():
         names.append("gqa_long")
         for name in names:
             r = run_config(W.get(name), max(args.steps, 20), args.warmup, q_group=args.q_group,
-                           smooth_q=args.smooth_q, pv=args.pv)
+                           smooth_q=args.smooth_q, pv=args.pv, graph=not args.eager)
             print(json.dumps(r), flush=True)
         return
     res = run_config(W.get(args.config), args.steps, args.warmup, full=True,
-                     q_group=args.q_group, smooth_q=args.smooth_q, pv=args.pv)
+                     q_group=args.q_group, smooth_q=args.smooth_q, pv=args.pv,
+                     graph=not args.eager)
     if args.lse:
         res["lse"] = run_lse(W.get(args.config), args.steps, args.warmup)
     if not args.no_cpu:
@@ -238,8 +244,11 @@ def delta_s_alone(plan, k, steps: int) -> float:
 
 
 def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 128,
-               smooth_q: bool = False, pv: str = "fp8") -> dict:
-    """Time `steps` whole steps of workload `w` (inputs resident on the GPU)."""
+               smooth_q: bool = False, pv: str = "fp8", graph: bool = True) -> dict:
+    """Time `steps` whole steps of workload `w` (inputs resident on the GPU): first as
+    eager launches with HIP events between the quantization and the attention (the
+    kernel split), then, with `graph`, as replays of the step captured as a HIP graph
+    (the whole-step rate; the same launches without the host's per-launch cost)."""
     import torch
     import quantized_attention_amd as qa
     import workloads as W
@@ -273,7 +282,19 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
         plan.attn()
         e[3].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_eager = time.perf_counter() - t0
+    wall = wall_eager
+    if graph:
+        g = plan.capture(q, k, v)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del g
     # smooth Q: the attention phase includes the Delta S passes; time them alone too
     t_ds = delta_s_alone(plan, k, steps) if smooth_q else 0.0
 
@@ -297,6 +318,8 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_launch": "hip graph replay" if graph else "eager",
+        "ms_per_step_eager": round(wall_eager * 1e3 / steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -326,7 +349,8 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
         },
     }
     if not full:
-        keep = ("value", "ms_per_step", "config", "attn_tops", "attn_ms", "attn_ms_median",
+        keep = ("value", "ms_per_step", "ms_per_step_eager", "config", "attn_tops", "attn_ms",
+                "attn_ms_median",
                 "attn_tops_median", "quant_ms", "quant_share", "quant_gbs", "delta_s_ms",
                 "delta_s_ws_bytes")
         res = {k: res[k] for k in keep}

@@ -654,3 +654,20 @@ class SagePlan:
     def __call__(self, q, k, v, stream=None):
         self.quant(q, k, v, stream)
         return self.attn(stream)
+
+    def capture(self, q, k, v):
+        """Record one quant() + attn() step on q, k, v as a HIP graph and return it
+        (a torch.cuda.CUDAGraph).  graph.replay() reruns the step's launches on the
+        same buffers: it reads what q, k and v hold at replay time and writes self.o
+        (and the plan's code buffers), so copy new inputs into q, k, v first.  The
+        step's launches are this library's kernels only (no memset or copy nodes).
+        One eager step on a side stream comes first, as graph capture requires."""
+        side = torch.cuda.Stream(device=self.o.device)
+        side.wait_stream(torch.cuda.current_stream(self.o.device))
+        with torch.cuda.stream(side):
+            self(q, k, v)
+        torch.cuda.current_stream(self.o.device).wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self(q, k, v)
+        return graph

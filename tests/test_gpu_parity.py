@@ -572,6 +572,39 @@ def test_smooth_q_chunks_do_not_change_the_result(gpu_lib, B, H, H_kv, N, d, dty
     compare_output(o0[:, :, torch.from_numpy(rws).to(DEV)], o_ref)
 
 
+@pytest.mark.parametrize("smooth_q,pv,causal", [(False, "fp8", False), (True, "fp8", True),
+                                                 (False, "mxfp4", True)])
+def test_plan_graph_replays_match_eager(gpu_lib, smooth_q, pv, causal):
+    """SagePlan.capture records quant() + attn() as a HIP graph.  Every replay, with eager
+    steps on other inputs and synchronizations between the replays, gives the eager
+    step's output bit for bit, and a replay reads the inputs' contents at replay time."""
+    B, H, H_kv, N, d, dtype = 1, 4, 2, 700, 128, torch.float16
+    print(f"graph replay case smooth_q={smooth_q} pv={pv} causal={causal}", flush=True)
+    plan = gpu_lib.SagePlan(B, H, H_kv, N, d, dtype, causal, device=DEV, smooth_q=smooth_q,
+                            pv=pv)
+    q, k, v = (t.to(DEV) for t in _biased_q_inputs(B, H, H_kv, N, d, dtype, seed=5))
+    q2, k2, v2 = (t.to(DEV) for t in _biased_q_inputs(B, H, H_kv, N, d, dtype, seed=6))
+    o1 = plan(q, k, v).clone()
+    o2 = plan(q2, k2, v2).clone()
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all() and not torch.equal(o1, o2)
+    graph = plan.capture(q, k, v)
+    torch.cuda.synchronize()
+    for i in range(3):
+        plan(q2, k2, v2)
+        torch.cuda.synchronize()
+        assert torch.equal(plan.o, o2), i
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.o, o1), i
+    q.copy_(q2)
+    k.copy_(k2)
+    v.copy_(v2)
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(plan.o, o2)
+
+
 def test_delta_s_row_ranges(gpu_lib):
     """sage_delta_s over a range of Q blocks writes exactly those rows of the whole table."""
     q, k, v = _biased_q_inputs(1, 3, 1, 1100, 64, torch.float16, seed=77)
