@@ -166,11 +166,44 @@ def main():
     res = run_config(W.get(args.config), args.steps, args.warmup, full=True,
                      q_group=args.q_group, smooth_q=args.smooth_q, pv=args.pv,
                      graph=not args.eager)
+    res["roofline"]["mfma_loop"] = mfma_loop(res["attn_tops"])
     if args.lse:
         res["lse"] = run_lse(W.get(args.config), args.steps, args.warmup)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(W.get(args.config), args.cpu_budget)
     print(json.dumps(res), flush=True)
+
+
+def mfma_loop(attn_tops: float) -> dict:
+    """The dense MFMA rate a register-only loop sustains (sage_mfma_peak: 512 workgroups of
+    4 waves, two waves per SIMD, INT8 32x32x32 and FP8 32x32x64), the shader clock during
+    the INT8 loop, and
+    the attention kernel's fraction of the INT8 loop's rate and of the published peak
+    scaled to that clock."""
+    import numpy as np
+    import torch
+    import quantized_attention_amd as qa
+    stream = torch.cuda.current_stream()
+    out = {}
+    for kind, name, iters in ((0, "i8", 24000), (1, "f8", 12000)):
+        qa.sage_mfma_peak(kind, 200)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ops, clocks, sink, khz = qa.sage_mfma_peak(kind, iters)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if not torch.all(sink == 64 * (32 if kind == 0 else 64) * iters):
+            raise RuntimeError("sage_mfma_peak: accumulator sums are not the expected ones")
+        c = clocks.cpu().numpy().astype(np.float64)
+        out[name + "_tops"] = round(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        # waves that shared a SIMD with more waves than the rest take longer
+        out[name + "_wave_clock_spread"] = round(float(c[:, 0].max() / c[:, 0].min()), 3)
+        if kind == 0:
+            out["clock_ghz"] = round(float(np.median(c[:, 0] / c[:, 1])) * khz / 1e6, 3)
+    out["attn_frac_of_i8_loop"] = round(attn_tops / out["i8_tops"], 4)
+    out["peak_at_loop_clock"] = round(PEAK_TOPS * out["clock_ghz"] / 2.4, 1)
+    out["attn_frac_at_loop_clock"] = round(attn_tops / out["peak_at_loop_clock"], 4)
+    return out
 
 
 def run_lse(w, steps: int, warmup: int) -> dict:

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 9
+#define SAGE_ABI_VERSION 10
 
 /* Q tokens per INT8 scale (default), K tokens per INT8 scale. */
 #define SAGE_BLKQ 128
@@ -353,6 +353,31 @@ sage_status sage_attn_fwd_mxfp4(const int8_t* q_i8, const float* q_scale, const 
  */
 sage_status sage_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int H_kv,
                           int N, int d, int b, int h, int32_t* s_out, void* stream);
+
+/*
+ * Diagnostic for the roofline (not a step of the method): the dense MFMA rate
+ * the device sustains and its shader clock meanwhile, against which the
+ * attention kernel's fraction of peak can be stated besides the published
+ * 2.4 GHz figure (the SageAttention2 detail page rates its kernels as a
+ * fraction of the matrix cores' peak).  Each of nwg workgroups of 4 waves
+ * issues, per wave, 4 * iters independent MFMAs back to back on register
+ * operands whose bytes are all 1 (kind 0: v_mfma_i32_32x32x32_i8, the
+ * instruction of S = Q K^T, 65536 ops each; kind 1: the scaled FP8 32x32x64
+ * MFMA of P V with unit scales, operands E4M3 1.0, 131072 flops each).
+ *   clocks: int64 [nwg*4][2], caller-owned device memory: per wave, the
+ *     shader clocks (clock64) and the constant-rate clocks (wall_clock64) its
+ *     loop took.
+ *   sink: uint32 [nwg*256], caller-owned device memory: per lane, the sum of
+ *     its 64 accumulator elements, 64 * 32 * iters (kind 0) or 64 * 64 * iters
+ *     (kind 1), so a caller can check that every MFMA ran.
+ *   wall_khz: host int, receives the constant-rate clock's frequency (kHz) of
+ *     the current device.
+ *   kind not 0 or 1, iters outside [1, 2^18] or nwg outside [1, 65536]:
+ *   SAGE_ERR_ARG; clocks or sink not 16-byte aligned: SAGE_ERR_ALIGN; nothing
+ *   launched either way.
+ */
+sage_status sage_mfma_peak(int kind, int iters, int nwg, int64_t* clocks, uint32_t* sink,
+                           int* wall_khz, void* stream);
 
 /*
  * sage_quant_qk without a workspace, for callers that cannot allocate device

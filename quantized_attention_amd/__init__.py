@@ -27,6 +27,8 @@ Entry points (same names as the C ABI):
     sage_qk_int32(q_i8, k_i8, b, h) -> int32 [N, N] (diagnostic)
     sage_quant_qk_noalloc(q, k, smooth_k=True, q_group=128, smooth_q=False, out=...)
         -> as sage_quant_qk, with the library's fixed scratch array (allocates nothing)
+    sage_mfma_peak(kind=0, iters=24000, nwg=512) -> (ops, clocks, sink, wall_khz)
+        (roofline diagnostic: a dense MFMA loop and the clock it runs at)
 and the composition ``sageattn(q, k, v, is_causal=False, sm_scale=None,
 smooth_k=True, return_lse=False, q_group=128, smooth_q=False)``.  ``q_group`` is the number of
 consecutive Q tokens per scale: 128 (per block), 32 (per wave, the per-warp
@@ -50,7 +52,8 @@ __all__ = ["SageError", "library_path", "load_library", "sage_buffer_sizes", "sa
            "sage_quant_v", "sage_quant_v_mxfp4", "sage_delta_s", "sage_attn_fwd",
            "sage_attn_fwd_lse", "sage_attn_fwd_smooth_q", "sage_attn_fwd_mxfp4",
            "sage_lse_correction",
-           "sage_qk_int32", "sage_quant_qk_noalloc", "sage_quant_qkv", "sageattn", "SagePlan",
+           "sage_qk_int32", "sage_quant_qk_noalloc", "sage_quant_qkv", "sage_mfma_peak",
+           "sageattn", "SagePlan",
            "smooth_q_workspace", "BLKQ", "BLKK",
            "KV_TILE", "Q_GROUPS", "SCRATCH_BYTES"]
 
@@ -112,10 +115,11 @@ def load_library():
                                           vp, vp]
     lib.sage_quant_qkv.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp,
                                    vp, vp, vp, sz, vp]
+    lib.sage_mfma_peak.argtypes = [i, i, i, vp, vp, ctypes.POINTER(i), vp]
     for f in ("sage_buffer_sizes", "sage_quant_qk", "sage_delta_s", "sage_quant_v", "sage_attn_fwd",
               "sage_attn_fwd_lse", "sage_lse_correction", "sage_qk_int32", "sage_quant_v_mxfp4",
               "sage_attn_fwd_mxfp4", "sage_quant_qk_noalloc", "sage_quant_qkv",
-              "sage_attn_fwd_smooth_q"):
+              "sage_attn_fwd_smooth_q", "sage_mfma_peak"):
         getattr(lib, f).restype = i
     _lib = lib
     return lib
@@ -599,6 +603,28 @@ def sageattn(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
         return sage_attn_fwd(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype)
     return sage_attn_fwd_lse(qk, vq, causal=is_causal, sm_scale=sm_scale, out_dtype=q.dtype,
                              lse_corr=corr)
+
+
+MFMA_PEAK_OPS = {0: 32 * 32 * 32 * 2, 1: 32 * 32 * 64 * 2}   # ops per MFMA of each kind
+
+
+def sage_mfma_peak(kind: int = 0, iters: int = 24000, nwg: int = 512, device="cuda",
+                   stream=None):
+    """Roofline diagnostic: nwg workgroups of 4 waves, each wave issuing 4 * iters
+    back-to-back MFMAs (kind 0: INT8 32x32x32, kind 1: scaled FP8 32x32x64) on
+    register operands.  Returns (ops, clocks, sink, wall_khz): the launch's
+    algorithmic ops, int64 [nwg*4, 2] per-wave (shader clocks, constant-rate
+    clocks), int32 [nwg*256] per-lane accumulator sums (64*32*iters or
+    64*64*iters) and the constant-rate clock's kHz.  The caller times the launch."""
+    clocks = torch.empty((nwg * 4, 2), dtype=torch.int64, device=device)
+    sink = torch.empty(nwg * 256, dtype=torch.int32, device=device)
+    khz = ctypes.c_int(0)
+    _check(load_library().sage_mfma_peak(int(kind), int(iters), int(nwg), _ptr(clocks),
+                                         _ptr(sink), ctypes.byref(khz),
+                                         _stream(stream, clocks.device)),
+           "sage_mfma_peak")
+    ops = nwg * 4 * 4 * iters * MFMA_PEAK_OPS[kind]
+    return ops, clocks, sink, khz.value
 
 
 class SagePlan:

@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsage_amd.so")
-SOURCES = ["sage_abi.hip", "quant.hip", "attn_fwd.hip", "delta_s.hip", "sage_noalloc.hip"]
+SOURCES = ["sage_abi.hip", "quant.hip", "attn_fwd.hip", "delta_s.hip", "sage_noalloc.hip",
+           "mfma_peak.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

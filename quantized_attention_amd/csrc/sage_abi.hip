@@ -17,6 +17,8 @@ hipError_t sage_launch_quant(const void* q, const void* k, const void* v, int bf
                              int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
                              float* k_mean, float* q_mean, uint8_t* v_f8, float* v_scale, void* ws,
                              hipStream_t st);
+hipError_t sage_launch_mfma_peak(int kind, int iters, int nwg, long long* clocks, uint32_t* sink,
+                                 hipStream_t st);
 hipError_t sage_launch_delta_s(const void* k, int bf16, const float* k_mean, const float* q_mean,
                                int B, int H, int H_kv, int N, int d, float sm_scale, int bh0,
                                int nbh, int i0, int nrows, int causal, float* out,
@@ -389,6 +391,20 @@ sage_status sage_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, 
   if (!aligned16(q_i8) || !aligned16(k_i8)) return SAGE_ERR_ALIGN;
   return from_hip(sage_launch_qk_int32(q_i8, k_i8, B, H, H_kv, N, d, b, h, s_out,
                                        (hipStream_t)stream));
+}
+
+sage_status sage_mfma_peak(int kind, int iters, int nwg, int64_t* clocks, uint32_t* sink,
+                           int* wall_khz, void* stream) {
+  if (!clocks || !sink || !wall_khz) return SAGE_ERR_NULL;
+  if ((kind != 0 && kind != 1) || iters < 1 || iters > (1 << 18) || nwg < 1 || nwg > 65536)
+    return SAGE_ERR_ARG;
+  if (!aligned16(clocks) || !aligned16(sink)) return SAGE_ERR_ALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return SAGE_ERR_HIP;
+  return from_hip(sage_launch_mfma_peak(kind, iters, nwg, reinterpret_cast<long long*>(clocks),
+                                        sink, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -28,10 +28,10 @@ def test_library_exports_every_declared_symbol():
             "sage_lse_correction", "sage_buffer_sizes", "sage_qk_int32", "sage_status_str",
             "sage_delta_s", "sage_quant_v_mxfp4", "sage_attn_fwd_mxfp4",
             "sage_abi_version", "sage_quant_qk_noalloc", "sage_quant_qkv",
-            "sage_attn_fwd_smooth_q"} <= set(names)
+            "sage_attn_fwd_smooth_q", "sage_mfma_peak"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sage_abi_version() == 9
+    assert lib.sage_abi_version() == 10
 
 
 def test_status_strings():
@@ -445,3 +445,18 @@ def test_smooth_q_entry_points_refuse_the_wrong_codes():
     plan = qa.SagePlan(1, 2, 2, 256, 64, torch.float16, False, device="cpu", smooth_q=True)
     with pytest.raises(RuntimeError, match="quant"):
         plan.attn()
+
+
+def _mfma_peak(lib, kind=0, iters=100, nwg=4, clocks=FAKE, sink=FAKE):
+    khz = ctypes.c_int(0)
+    return lib.sage_mfma_peak(kind, iters, nwg, clocks, sink, ctypes.byref(khz), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(clocks=None), 1), (dict(sink=None), 1), (dict(kind=2), 6), (dict(kind=-1), 6),
+    (dict(iters=0), 6), (dict(iters=(1 << 18) + 1), 6), (dict(nwg=0), 6), (dict(nwg=65537), 6),
+    (dict(clocks=FAKE + 8), 9), (dict(sink=FAKE + 4), 9),
+])
+def test_mfma_peak_rejects(kw, code):
+    """The roofline probe checks its arguments before touching a device."""
+    assert _mfma_peak(qa.load_library(), **kw) == code

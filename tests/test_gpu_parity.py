@@ -605,6 +605,24 @@ def test_plan_graph_replays_match_eager(gpu_lib, smooth_q, pv, causal):
     assert torch.equal(plan.o, o2)
 
 
+@pytest.mark.parametrize("kind", [0, 1])
+def test_mfma_peak_loop_runs_every_mfma(gpu_lib, kind):
+    """The roofline probe: every lane's accumulator sum is 64 elements x (32 or 64) x iters
+    (all operands 1), every wave's clocks are positive, and the shader clock they imply is
+    a plausible one."""
+    print(f"mfma peak probe kind={kind}", flush=True)
+    iters, nwg = 2000, 512
+    ops, clocks, sink, khz = gpu_lib.sage_mfma_peak(kind, iters, nwg, device=DEV)
+    torch.cuda.synchronize()
+    assert ops == nwg * 16 * iters * (65536 if kind == 0 else 131072)
+    per = 32 if kind == 0 else 64
+    assert torch.all(sink == 64 * per * iters)
+    c = clocks.cpu().numpy().astype(np.float64)
+    assert (c > 0).all() and khz > 0
+    ghz = float(np.median(c[:, 0] / c[:, 1])) * khz / 1e6
+    assert 0.5 < ghz < 3.0, ghz
+
+
 def test_delta_s_row_ranges(gpu_lib):
     """sage_delta_s over a range of Q blocks writes exactly those rows of the whole table."""
     q, k, v = _biased_q_inputs(1, 3, 1, 1100, 64, torch.float16, seed=77)
