@@ -175,17 +175,18 @@ def main():
 
 
 def mfma_loop(attn_tops: float) -> dict:
-    """The dense MFMA rate a register-only loop sustains (sage_mfma_peak: 512 workgroups of
-    4 waves, two waves per SIMD, INT8 32x32x32 and FP8 32x32x64), the shader clock during
-    the INT8 loop, and
-    the attention kernel's fraction of the INT8 loop's rate and of the published peak
-    scaled to that clock."""
+    """The dense MFMA rate a register-only loop sustains (sage_mfma_peak: 256 workgroups of
+    4 waves, one wave per SIMD when each CU takes one workgroup; INT8 32x32x32 and FP8
+    32x32x64), the clocks each MFMA took in a wave, the shader clock during the INT8 loop,
+    and the attention kernel's fraction of the INT8 loop's rate and of the published peak
+    scaled to that clock.  (The clock under the attention kernel itself comes from the
+    GRBM_GUI_ACTIVE counter of a profiled run; the loop's may differ.)"""
     import numpy as np
     import torch
     import quantized_attention_amd as qa
     stream = torch.cuda.current_stream()
     out = {}
-    for kind, name, iters in ((0, "i8", 24000), (1, "f8", 12000)):
+    for kind, name, iters in ((0, "i8", 48000), (1, "f8", 24000)):
         qa.sage_mfma_peak(kind, 200)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -196,7 +197,9 @@ def mfma_loop(attn_tops: float) -> dict:
             raise RuntimeError("sage_mfma_peak: accumulator sums are not the expected ones")
         c = clocks.cpu().numpy().astype(np.float64)
         out[name + "_tops"] = round(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
-        # waves that shared a SIMD with more waves than the rest take longer
+        # shader clocks per MFMA in a wave (32 and 64 at the full rate of a SIMD); waves
+        # that shared a SIMD take longer, which the spread shows
+        out[name + "_clocks_per_mfma"] = round(float(np.median(c[:, 0])) / (4 * iters), 2)
         out[name + "_wave_clock_spread"] = round(float(c[:, 0].max() / c[:, 0].min()), 3)
         if kind == 0:
             out["clock_ghz"] = round(float(np.median(c[:, 0] / c[:, 1])) * khz / 1e6, 3)

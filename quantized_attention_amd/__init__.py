@@ -27,7 +27,7 @@ Entry points (same names as the C ABI):
     sage_qk_int32(q_i8, k_i8, b, h) -> int32 [N, N] (diagnostic)
     sage_quant_qk_noalloc(q, k, smooth_k=True, q_group=128, smooth_q=False, out=...)
         -> as sage_quant_qk, with the library's fixed scratch array (allocates nothing)
-    sage_mfma_peak(kind=0, iters=24000, nwg=512) -> (ops, clocks, sink, wall_khz)
+    sage_mfma_peak(kind=0, iters=48000, nwg=256) -> (ops, clocks, sink, wall_khz)
         (roofline diagnostic: a dense MFMA loop and the clock it runs at)
 and the composition ``sageattn(q, k, v, is_causal=False, sm_scale=None,
 smooth_k=True, return_lse=False, q_group=128, smooth_q=False)``.  ``q_group`` is the number of
@@ -608,7 +608,7 @@ def sageattn(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
 MFMA_PEAK_OPS = {0: 32 * 32 * 32 * 2, 1: 32 * 32 * 64 * 2}   # ops per MFMA of each kind
 
 
-def sage_mfma_peak(kind: int = 0, iters: int = 24000, nwg: int = 512, device="cuda",
+def sage_mfma_peak(kind: int = 0, iters: int = 48000, nwg: int = 256, device="cuda",
                    stream=None):
     """Roofline diagnostic: nwg workgroups of 4 waves, each wave issuing 4 * iters
     back-to-back MFMAs (kind 0: INT8 32x32x32, kind 1: scaled FP8 32x32x64) on
