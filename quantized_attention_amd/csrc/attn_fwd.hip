@@ -54,6 +54,9 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
   // K (with Delta S) and V tiles are double-buffered.
   __shared__ __attribute__((aligned(16))) char lds_k[2][KBYTES + DSBYTES];
   __shared__ __attribute__((aligned(16))) char lds_v[2][VBYTES + VSBYTES];
+  // the kv head's V channel scales for the epilogue (FP8 P V), staged once at
+  // the start so the epilogue does not wait on a global load
+  __shared__ __attribute__((aligned(16))) float lds_vs[PV4 ? 4 : D];
 
   // ---- which (b, kv head, q tile, group member) this workgroup computes.
   // Non-causal (equal work per workgroup): each XCD takes a contiguous range
@@ -180,6 +183,15 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
   };
   load_k(0);
   load_v(0);
+  if constexpr (!PV4) {
+    // waves 0 .. D/64-1: one scale per lane, straight into LDS (visible after
+    // the first tile's wait and barrier)
+    if (wave < D / 64) {
+      const rsrc_t rvsc = make_rsrc(v_scale + (size_t)(b * H_kv + hk) * D, (uint32_t)D * 4);
+      buffer_to_lds<4>(rvsc, reinterpret_cast<char*>(lds_vs) + wave * 256,
+                       (uint32_t)((wave * 64 + lane) * 4), 0u);
+    }
+  }
 
   // One 128-key step of the online softmax.  MASK: the tile holds keys past
   // the diagonal (causal) or past N; only the last tile can.
@@ -489,15 +501,17 @@ __global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
   }
   if (qi < N) {
     char* orow = reinterpret_cast<char*>(out) + ((size_t)(b * H + h) * N + qi) * D * 2;
-    const float* vs = v_scale + (size_t)(b * H_kv + hk) * D;
 #pragma unroll
     for (int c = 0; c < NKC; ++c)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int ch = c * 32 + 8 * r4 + 4 * half;
+        const float4 s4 = PV4 ? float4{1.f, 1.f, 1.f, 1.f}
+                              : *reinterpret_cast<const float4*>(lds_vs + (PV4 ? 0 : ch));
+        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
         float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = acc_o[c][r4 * 4 + j] * inv * (PV4 ? 1.0f : vs[ch + j]);
+        for (int j = 0; j < 4; ++j) v[j] = acc_o[c][r4 * 4 + j] * inv * sv[j];
         uint2 pk;
         if (BF16) {
           __hip_bfloat16 x0 = __float2bfloat16(v[0]), x1 = __float2bfloat16(v[1]);
