@@ -33,8 +33,10 @@ namespace sage {
 // PV4: P V on the FP4 matrix cores in MXFP4 (v_f8 holds E2M1 codes, v_e8 the
 // E8M0 scale bytes, see quant_v_mxfp4); P~ is quantized per 32 keys of a row.
 template <int D, bool CAUSAL, bool BF16, bool SQ, bool PV4>
-// d = 64 fits three workgroups per CU (168 registers); d = 128 two.
-__global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void attn_fwd_kernel(
+// d = 64 fits three workgroups per CU (168 registers), four with MXFP4 P V
+// (128: no product by 448 and a smaller P, +3 % on a d = 64 video workload
+// against three); d = 128 two.
+__global__ __launch_bounds__(kWaves * 64, D == 64 ? (PV4 ? 4 : 3) : 2) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_f8, const float* __restrict__ v_scale,
