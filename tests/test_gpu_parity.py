@@ -533,6 +533,7 @@ def test_smooth_q_lse(gpu_lib):
     (2, 2, 1, 2200, 128, torch.bfloat16, False),
     (2, 6, 3, 300, 64, torch.float16, True),
     (1, 32, 16, 300, 64, torch.bfloat16, True),
+    (4, 16, 8, 1100, 128, torch.float16, True),
 ])
 def test_smooth_q_chunks_do_not_change_the_result(gpu_lib, B, H, H_kv, N, d, dtype, causal):
     """sage_attn_fwd_smooth_q computes the Delta S rows a chunk at a time in its
