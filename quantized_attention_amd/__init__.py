@@ -685,9 +685,10 @@ class SagePlan:
         """Record one quant() + attn() step on q, k, v as a HIP graph and return it
         (a torch.cuda.CUDAGraph).  graph.replay() reruns the step's launches on the
         same buffers: it reads what q, k and v hold at replay time and writes self.o
-        (and the plan's code buffers), so copy new inputs into q, k, v first.  The
-        step's launches are this library's kernels only (no memset or copy nodes).
-        One eager step on a side stream comes first, as graph capture requires."""
+        (and the plan's code buffers), so copy new inputs into q, k, v first; q, k, v
+        and the plan must stay alive as long as the graph is replayed.  The step's
+        launches are this library's kernels only (no memset or copy nodes).  One
+        eager step on a side stream comes first, as graph capture requires."""
         side = torch.cuda.Stream(device=self.o.device)
         side.wait_stream(torch.cuda.current_stream(self.o.device))
         with torch.cuda.stream(side):
