@@ -320,17 +320,24 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
     torch.cuda.synchronize()
     wall_eager = time.perf_counter() - t0
     wall = wall_eager
+    launch = "eager"
     if graph:
-        g = plan.capture(q, k, v)
-        for _ in range(warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            g.replay()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        del g
+        try:
+            g = plan.capture(q, k, v)
+        except RuntimeError as e:   # capture unsupported here: report the eager steps
+            torch.cuda.synchronize()
+            g, launch = None, f"eager (HIP graph capture failed: {str(e)[:120]})"
+        if g is not None:
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                g.replay()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            launch = "hip graph replay"
+            del g
     # smooth Q: the attention phase includes the Delta S passes; time them alone too
     t_ds = delta_s_alone(plan, k, steps) if smooth_q else 0.0
 
@@ -354,7 +361,7 @@ def run_config(w, steps: int, warmup: int, full: bool = False, q_group: int = 12
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
-        "step_launch": "hip graph replay" if graph else "eager",
+        "step_launch": launch,
         "ms_per_step_eager": round(wall_eager * 1e3 / steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
